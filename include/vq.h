@@ -1,0 +1,193 @@
+/*
+ * vq.h - C ABI of the MI355X (gfx950) product-VQ KV-cache hot path.
+ *
+ * Method: VecInfer-style product vector quantization of attention keys and
+ * values, as described on the "veloxquant_mlx.cache.vecinfer_cache module"
+ * page (module description: per-(head, channel) smoothing and a
+ * Walsh-Hadamard rotation of the keys, product-VQ encoding against a
+ * codebook, dequantization; per-token storage (D / d_k) * b_k / 8 bytes) and
+ * on the "Metal Kernels API" page (sections "VecInfer kernels" and
+ * "Fused SDPA").
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major (last index fastest), device
+ *     pointers, unless stated otherwise.  fp16 means IEEE binary16.
+ *   - Codes are uint8 (n_centroids <= 256).  A code buffer has shape
+ *     [B, H, S_cap, D / sub_dim]: token slot t of (b, h) starts at byte
+ *     ((b * H + h) * S_cap + t) * (D / sub_dim).
+ *   - Sub-vector j of a D-vector covers dims [j * sub_dim, (j+1) * sub_dim).
+ *     One codebook [n_centroids, sub_dim] (fp32) serves every sub-vector,
+ *     head and batch row.
+ *   - smooth is NULL (no smoothing) or fp32 [smooth_rows, D] with
+ *     smooth_rows = 1 (one row shared by all heads) or H (one row per head;
+ *     for attention, per kv head).  Encode divides by it, decode multiplies.
+ *     Its entries must be finite and nonzero; they are not inspected.
+ *   - transform = 1 applies the normalized Sylvester Walsh-Hadamard matrix
+ *     H[i][k] = (-1)^popcount(i & k) / sqrt(D) (symmetric, its own inverse);
+ *     transform = 0 applies none (the value path).
+ *   - Every call is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns without synchronizing.  The caller owns every
+ *     buffer; the library allocates no device memory and keeps no state
+ *     between calls other than cached device attributes.
+ *   - Errors: arguments are validated on the host before any HIP call; on
+ *     failure nothing is enqueued and a nonzero status is returned, with a
+ *     message available from vq_last_error().  Device data (codes, lengths)
+ *     is not validated: kv lengths are clamped to [0, S_cap].  A failed
+ *     kernel launch returns VQ_ERR_HIP; faults during execution surface at
+ *     the caller's next synchronization.  The library never aborts.
+ */
+#ifndef VQ_H
+#define VQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  VQ_OK = 0,
+  VQ_ERR_INVALID_ARGUMENT = 1, /* inconsistent shapes, null pointers, ranges */
+  VQ_ERR_UNSUPPORTED = 2,      /* outside the compiled caps (see vq_supports_shape) */
+  VQ_ERR_NO_DEVICE = 3,        /* no HIP device is visible */
+  VQ_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
+  VQ_ERR_WORKSPACE = 5         /* attention workspace missing or too small */
+};
+
+/* Upper bound on B for the per-row write offsets of vq_encode. */
+#define VQ_MAX_ROW_OFFSETS 256
+
+/* Static description of a status code. */
+const char* vq_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* vq_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int vq_version(void);
+
+/*
+ * 1 if (n_centroids, n_sub, head_dim) fits the compiled kernels, else 0.
+ * Mirrors supports_shape of the fused attention ("Metal Kernels API", "Fused
+ * SDPA": a check of the codebook size, the number of sub-vectors and the
+ * head dimension, not of batch or sequence sizes; head_dim a multiple of 32).
+ * Caps: 1 <= n_centroids <= 256; head_dim in {32, 64, 128, 256};
+ * n_sub divides head_dim, head_dim / n_sub in {1, 2, 4, 8, 16}, n_sub <= 64.
+ * vq_attend additionally needs n_sub to be a multiple of 4 for both codes.
+ */
+int vq_supports_shape(int n_centroids, int n_sub, int head_dim);
+
+/*
+ * Key (or value) encode: smooth -> rotate -> nearest centroid, written into
+ * a code buffer ("Metal Kernels API", "VecInfer kernels",
+ * vecinfer_quantize_metal and the first three steps of
+ * vecinfer_encode_decode_metal; the cache appends codes into index buffers,
+ * "veloxquant_mlx.cache.vecinfer_cache module", update_and_fetch).
+ *
+ *   keys_f16    [B, H, S, D] fp16
+ *   codebook    [n_centroids, sub_dim] fp32
+ *   smooth      NULL or [smooth_rows, D] fp32 (see conventions)
+ *   transform   0 or 1
+ *   codes       [B, H, S_cap, D / sub_dim] uint8; token t of row b is
+ *               written to slot off_b + t, off_b = row_offsets[b] if
+ *               row_offsets != NULL else S_off.  Other slots are untouched.
+ *   row_offsets NULL or HOST array of B int32 (B <= VQ_MAX_ROW_OFFSETS),
+ *               each with 0 <= off_b and off_b + S <= S_cap.
+ * The centroid index minimizes the fp32 squared distance summed over the
+ * sub-vector; exact ties resolve to the lowest index.
+ * Errors: INVALID_ARGUMENT for null pointers, nonpositive sizes, S_off or
+ * offsets out of range, D % sub_dim != 0, smooth_rows not in {1, H};
+ * UNSUPPORTED outside the caps.  S = 0 or B = 0 is a no-op returning VQ_OK.
+ */
+int vq_encode(const void* keys_f16, int B, int H, int S, int D,
+              const float* codebook, int n_centroids, int sub_dim,
+              const float* smooth, int smooth_rows, int transform,
+              uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets,
+              void* stream);
+
+/*
+ * Decode: codebook gather -> inverse rotation -> inverse smoothing ("Metal
+ * Kernels API", "VecInfer kernels", vecinfer_dequant_metal and the last three
+ * steps of vecinfer_encode_decode_metal).
+ *
+ *   codes       [B, H, S_cap, D / sub_dim] uint8; slots [S_off, S_off + S)
+ *               are read.  Codes >= n_centroids are undefined behaviour.
+ *   out         [B, H, S, D]; out_dtype 0 = fp32, 1 = fp16 (round to
+ *               nearest even).
+ * Errors as vq_encode.
+ */
+int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
+              const float* codebook, int n_centroids, int sub_dim,
+              const float* smooth, int smooth_rows, int transform, int D,
+              void* out, int out_dtype, void* stream);
+
+/*
+ * Fused round trip in one kernel: the codes of vq_encode and the
+ * reconstruction of vq_decode of those codes ("Metal Kernels API",
+ * "VecInfer kernels", vecinfer_encode_decode_metal: smooth -> WHT -> VQ
+ * encode -> dequant -> inverse WHT -> inverse smooth in one dispatch).
+ *
+ *   recon       [B, H, S, D]; out_dtype 0 = fp32, 1 = fp16.
+ * Other arguments and errors as vq_encode.
+ */
+int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D,
+                     const float* codebook, int n_centroids, int sub_dim,
+                     const float* smooth, int smooth_rows, int transform,
+                     uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets,
+                     void* recon, int out_dtype, void* stream);
+
+/*
+ * Bytes of device workspace vq_attend needs for this shape (0 on invalid
+ * sizes).  Depends only on its arguments, not on the device.
+ */
+size_t vq_attend_workspace_bytes(int B, int H_q, int S_q, int D, int H_kv,
+                                 int S_cap, int sliding_window);
+
+/*
+ * Fused attention read directly from key and value codes ("Metal Kernels
+ * API", "Fused SDPA", metal_fused_sdpa; with the raw query and the dual
+ * transform applied inside as in "veloxquant_mlx.cache.vecinfer_cache
+ * module", fused_sdpa).  The result equals softmax attention over the
+ * decoded keys K_hat = ((C_k[k_codes]) . H) * s and values C_v[v_codes]:
+ *
+ *   out[b, h, i] = sum_t p_t V_hat[b, g, t],
+ *   p = softmax_t(scale * q[b, h, i] . K_hat[b, g, t]) over the valid t,
+ *   g = h / (H_q / H_kv),
+ *   q_abs = len_b - S_q + i (queries align to the tail of the key axis),
+ *   t valid iff t < len_b, and (causal => t <= q_abs), and
+ *              (sliding_window > 0 => t > q_abs - sliding_window).
+ * A query row with no valid key gets zeros.
+ *
+ *   q_f16       [B, H_q, S_q, D] fp16 raw queries
+ *   k_codes     [B, H_kv, S_cap, D / k_sub_dim] uint8
+ *   k_codebook  [n_centroids, k_sub_dim] fp32
+ *   smooth      NULL or [smooth_rows, D] fp32 smooth factors of the keys
+ *               (smooth_rows 1 or H_kv); transform as for vq_encode
+ *   v_codes     [B, H_kv, S_cap, D / v_sub_dim] uint8 (no smooth, no rotation)
+ *   v_codebook  [n_centroids, v_sub_dim] fp32
+ *   kv_lens     NULL (every row holds S_cap keys) or DEVICE int32 [B];
+ *               values are clamped to [0, S_cap]
+ *   out_f16     [B, H_q, S_q, D] fp16
+ *   workspace   DEVICE buffer of >= vq_attend_workspace_bytes(...) bytes,
+ *               zero-filled before its first use; every call leaves it
+ *               ready for the next.  Calls that may run concurrently need
+ *               distinct workspaces.
+ * Errors: INVALID_ARGUMENT for null pointers, nonpositive sizes,
+ * H_q % H_kv != 0, D % sub_dim != 0, smooth_rows not in {1, H_kv},
+ * sliding_window < 0; UNSUPPORTED outside the caps; WORKSPACE when the
+ * workspace is NULL or smaller than required.
+ */
+int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D,
+              const uint8_t* k_codes, const float* k_codebook, int k_sub_dim,
+              const float* smooth, int smooth_rows, int transform,
+              const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
+              int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens,
+              float scale, int causal, int sliding_window,
+              void* out_f16, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQ_H */

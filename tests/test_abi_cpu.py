@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol declared in include/vq.h, and rejects invalid arguments before any
+HIP call.  Valid calls on a host without a device return VQ_ERR_NO_DEVICE."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from vector_quantized_kv_amd import _lib, api
+from vector_quantized_kv_amd.build import build_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vq.h")
+OK, INVALID, UNSUPPORTED, NO_DEVICE, HIPERR, WORKSPACE = range(6)
+P = ctypes.c_void_p(0x10000)          # a non-null pointer that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        build_library(verbose=False)
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = header_functions()
+    for n in ["vq_encode", "vq_decode", "vq_encode_decode", "vq_attend",
+              "vq_attend_workspace_bytes", "vq_supports_shape", "vq_status_string", "vq_last_error"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (vq_\w+)", out))
+    for n in header_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(header_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings(lib):
+    assert lib.vq_status_string(OK) == b"ok"
+    assert b"invalid" in lib.vq_status_string(INVALID)
+    assert lib.vq_status_string(99) == b"unknown status"
+    assert lib.vq_version() >= 100
+
+
+@pytest.mark.parametrize("n_c,n_sub,D,ok", [
+    (256, 16, 128, 1), (256, 16, 64, 1), (256, 32, 128, 1), (1, 64, 256, 1), (16, 32, 32, 1),
+    (257, 16, 128, 0), (0, 16, 128, 0), (256, 16, 96, 0), (256, 128, 128, 0), (256, 5, 128, 0),
+    (256, 4, 128, 0), (256, 16, 512, 0)])
+def test_supports_shape(lib, n_c, n_sub, D, ok):
+    assert lib.vq_supports_shape(n_c, n_sub, D) == ok
+
+
+def enc(lib, B=1, H=2, S=8, D=64, n_c=256, dsub=4, smooth=P, srows=2, transform=1, S_cap=8,
+        S_off=0, offs=None, keys=P, cb=P, codes=P):
+    return lib.vq_encode(keys, B, H, S, D, cb, n_c, dsub, smooth, srows, transform, codes, S_cap,
+                         S_off, offs, None)
+
+
+def test_encode_validation(lib):
+    assert enc(lib, keys=None) == INVALID
+    assert enc(lib, codes=None) == INVALID
+    assert enc(lib, D=64, dsub=3) == INVALID            # D % sub_dim
+    assert enc(lib, n_c=300) == INVALID                 # does not fit uint8
+    assert enc(lib, n_c=0) == INVALID
+    assert enc(lib, srows=3) == INVALID                 # smooth rows not 1 or H
+    assert enc(lib, transform=2) == INVALID
+    assert enc(lib, S_off=4) == INVALID                 # 4 + 8 > 8
+    assert enc(lib, S_off=-1) == INVALID
+    assert enc(lib, H=0) == INVALID
+    assert enc(lib, D=96, dsub=4) == UNSUPPORTED        # head dim cap
+    assert enc(lib, D=128, dsub=1) == UNSUPPORTED       # 128 sub-vectors > 64
+    offs = (ctypes.c_int32 * 2)(0, 5)
+    assert enc(lib, B=2, S=4, offs=offs) == INVALID     # row 1 writes [5, 9)
+    assert b"row 1" in lib.vq_last_error()
+    assert enc(lib, B=257, offs=(ctypes.c_int32 * 257)()) == INVALID   # too many rows
+    assert enc(lib, B=0) in (OK,)                       # empty: no-op
+    assert enc(lib, S=0) in (OK,)
+
+
+def test_decode_and_encode_decode_validation(lib):
+    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, P, 2, 1, P, 8, 0, None, None, 1, None)
+    assert st == INVALID                                # recon NULL
+    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, P, 2, 1, P, 8, 0, None, P, 7, None)
+    assert st == INVALID                                # out_dtype
+    st = lib.vq_decode(P, 1, 2, 8, 8, 1, P, 256, 4, None, 1, 1, 64, P, 0, None)
+    assert st == INVALID                                # slots [1, 9) outside [0, 8)
+    st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 256, 4, None, 1, 1, 48, P, 0, None)
+    assert st == UNSUPPORTED                            # D = 48
+    st = lib.vq_decode(None, 1, 2, 8, 8, 0, P, 256, 4, None, 1, 1, 64, P, 0, None)
+    assert st == INVALID
+
+
+def att(lib, B=2, Hq=8, Sq=1, D=128, dk=8, dv=4, n_c=256, Hkv=2, S_cap=64, W=0, causal=1,
+        ws=P, ws_bytes=1 << 30, smooth=P, srows=2, scale=0.1, q=P):
+    return lib.vq_attend(q, B, Hq, Sq, D, P, P, dk, smooth, srows, 1, P, P, dv, n_c, Hkv, S_cap,
+                         None, scale, causal, W, P, ws, ws_bytes, None)
+
+
+def test_attend_validation(lib):
+    assert att(lib, q=None) == INVALID
+    assert att(lib, Hq=6, Hkv=4) == INVALID              # H_q % H_kv
+    assert att(lib, dk=3) == INVALID                     # D % sub_dim
+    assert att(lib, W=-1) == INVALID
+    assert att(lib, causal=2) == INVALID
+    assert att(lib, srows=3) == INVALID
+    assert att(lib, scale=float("inf")) == INVALID
+    assert att(lib, D=96) == UNSUPPORTED
+    assert att(lib, D=32, dk=16) == UNSUPPORTED          # 2 key sub-vectors: not a multiple of 4
+    assert att(lib, ws=None) == WORKSPACE
+    assert att(lib, ws_bytes=16) == WORKSPACE
+    assert b"workspace needs" in lib.vq_last_error()
+    assert att(lib, B=0) == OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="a device is visible")
+def test_valid_calls_report_no_device(lib):
+    assert enc(lib) == NO_DEVICE
+    assert att(lib) == NO_DEVICE
+    assert b"no HIP device" in lib.vq_last_error()
+
+
+def test_workspace_bytes(lib):
+    f = lib.vq_attend_workspace_bytes
+    assert f(0, 8, 1, 128, 8, 1024, 0) == 0
+    assert f(1, 6, 1, 128, 4, 1024, 0) == 0              # H_q % H_kv
+    a = f(16, 32, 1, 128, 8, 32768, 0)
+    b = f(16, 32, 1, 128, 8, 32768, 4096)
+    assert a > 0 and b > 0
+    # (D + 2) floats per split partial, rows rounded up to 8
+    assert a % ((128 + 2) * 4 * 16 * 8 * 8) == 0
+
+
+def test_binding_rejects_host_tensors(lib):
+    k = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
+    cb = torch.zeros(256, 4)
+    with pytest.raises(ValueError, match="device tensor"):
+        api.vq_encode(k, cb, 4)
+    with pytest.raises(ValueError, match="fp16|float16"):
+        api.vq_encode(k.float(), cb, 4)

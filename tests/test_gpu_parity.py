@@ -1,0 +1,331 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (float tolerances follow the stated targets of the method's hot path):
+  codes           bit-exact, except at near-ties where the oracle's top-2
+                  distance gap is below 1e-5 relative; there the GPU's
+                  choice must itself be a near-optimal centroid (its oracle
+                  distance within 1e-5 * d2 of the minimum); mismatches are
+                  counted and printed.
+  reconstruction  fp32 output within 1e-3 absolute of the fp64 oracle;
+                  fp16 output within 1e-3 + half an fp16 ulp of it.
+  attention       fp16 output within 2e-3 absolute + 1e-2 relative of the
+                  fp64 oracle (allclose form), fed the same codes.
+Full-size workloads run on the GPU in the launch configuration the
+benchmark times; the oracle checks sampled outputs computed one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.vq_oracle as O
+from vector_quantized_kv_amd import synth
+from vector_quantized_kv_amd import (vq_attend, vq_decode, vq_encode, vq_encode_decode)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NEAR_TIE = 1e-5
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def oracle_transform(keys, smooth):
+    return O.forward_transform(keys, smooth, True)
+
+
+# ----------------------------------------------------------------------------
+# comparison helpers
+# ----------------------------------------------------------------------------
+def check_codes(keys, codebook, sub_dim, smooth, transform, gpu_codes, tag=""):
+    """Compare GPU codes [B, H, S, n_sub] with the oracle under the near-tie rule."""
+    ref, gap = O.encode(keys, codebook, sub_dim, smooth, transform)
+    gpu = np.asarray(gpu_codes).astype(np.int64)
+    mism = gpu != ref
+    n = int(mism.sum())
+    if n:
+        assert np.all(gap[mism] < NEAR_TIE), f"{tag}: {n} code mismatches, some not near-ties"
+        xt = O.forward_transform(keys, smooth, transform)
+        dist = O.pvq_distances(xt, codebook, sub_dim)             # [..., n_sub, n_c]
+        d_gpu = np.take_along_axis(dist, gpu[..., None], -1)[..., 0]
+        srt = np.sort(dist, -1)
+        d1, d2 = srt[..., 0], srt[..., 1]
+        assert np.all(d_gpu[mism] - d1[mism] <= NEAR_TIE * d2[mism]), f"{tag}: GPU code not near-optimal"
+    print(f"[codes] {tag}: {gpu.size} codes, {n} near-tie mismatches")
+    return n
+
+
+def check_recon(gpu, ref64, dtype, tag=""):
+    gpu = np.asarray(gpu).astype(np.float64)
+    if dtype == "fp32":
+        tol = 1e-3
+    else:
+        r16 = ref64.astype(np.float16)
+        ulp = np.abs(np.spacing(r16).astype(np.float64))
+        tol = 1e-3 + 0.5 * ulp
+    err = np.abs(gpu - ref64)
+    assert np.all(err <= tol), f"{tag}: recon error {err.max():.3g}"
+    print(f"[recon] {tag}: max abs err {err.max():.3g}")
+
+
+def check_attn(gpu, ref, tag=""):
+    gpu = np.asarray(gpu).astype(np.float64)
+    err = np.abs(gpu - ref)
+    bad = err > 2e-3 + 1e-2 * np.abs(ref)
+    assert not np.any(np.isnan(gpu)), f"{tag}: NaN in output"
+    assert not bad.any(), f"{tag}: {int(bad.sum())} elements out of tolerance, max err {err.max():.3g}"
+    print(f"[attn] {tag}: max abs err {err.max():.3g}")
+
+
+def run_attend(cfg, k_codes=None, v_codes=None, **over):
+    p = dict(cfg, **over)
+    kc = dev(p["k_codes"] if k_codes is None else k_codes)
+    vc = dev(p["v_codes"] if v_codes is None else v_codes)
+    lens = None if p.get("kv_lens") is None else dev(np.asarray(p["kv_lens"], np.int32))
+    out = vq_attend(dev(p["q"]), kc, dev(p["k_codebook"]), vc, dev(p["v_codebook"]),
+                    scale=p["scale"], smooth=None if p.get("smooth") is None else dev(p["smooth"]),
+                    transform=p.get("transform", True), kv_lens=lens, causal=p["causal"],
+                    sliding_window=p["window"])
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def oracle_attend(p, k_codes, v_codes, rows=None):
+    return O.attend(p["q"], k_codes, p["k_codebook"], v_codes, p["v_codebook"], scale=p["scale"],
+                    causal=p["causal"], sliding_window=p["window"], smooth=p.get("smooth"),
+                    transform=p.get("transform", True), kv_lens=p.get("kv_lens"), rows=rows)
+
+
+# ----------------------------------------------------------------------------
+# tiny workload: encode keys and values, then attend from the GPU's codes
+# ----------------------------------------------------------------------------
+def test_tiny_end_to_end():
+    c = synth.tiny(oracle_transform)
+    k, v, s = c["keys"], c["values"], c["smooth"]
+    rk, kc = vq_encode_decode(dev(k), dev(c["k_codebook"]), c["dk"], smooth=dev(s),
+                              out_dtype=torch.float32)
+    rv, vc = vq_encode_decode(dev(v), dev(c["v_codebook"]), c["dv"], transform=False,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kc, vc = kc.cpu().numpy(), vc.cpu().numpy()
+    check_codes(k, c["k_codebook"], c["dk"], s, True, kc, "tiny keys")
+    check_codes(v, c["v_codebook"], c["dv"], None, False, vc, "tiny values")
+    check_recon(rk.cpu().numpy(), O.decode(kc, c["k_codebook"], s, True), "fp32", "tiny keys")
+    check_recon(rv.cpu().numpy(), O.decode(vc, c["v_codebook"]), "fp32", "tiny values")
+    # fp16 reconstruction and the encode-only entry point give the same codes
+    r16, kc16 = vq_encode_decode(dev(k), dev(c["k_codebook"]), c["dk"], smooth=dev(s))
+    kc_only = vq_encode(dev(k), dev(c["k_codebook"]), c["dk"], smooth=dev(s))
+    torch.cuda.synchronize()
+    assert np.array_equal(kc16.cpu().numpy(), kc) and np.array_equal(kc_only.cpu().numpy(), kc)
+    check_recon(r16.cpu().numpy(), O.decode(kc, c["k_codebook"], s, True), "fp16", "tiny keys fp16")
+    # attention from the GPU's codes
+    p = dict(c, k_codes=kc, v_codes=vc, kv_lens=None)
+    out = run_attend(p)
+    check_attn(out, oracle_attend(p, kc, vc), "tiny attend")
+
+
+def test_identity_codebook_round_trip():
+    """Codebook rows = transformed sub-vectors of 16 tokens: each sub-vector
+    encodes to its own row and the fp16 reconstruction returns the keys."""
+    c = synth.tiny()
+    keys = np.ascontiguousarray(c["keys"][:, :1, :16])
+    s = c["smooth"][:1]
+    C = O.forward_transform(keys, s, True).reshape(-1, c["dk"]).astype(np.float32)
+    rec, codes = vq_encode_decode(dev(keys), dev(C), c["dk"], smooth=dev(s))
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy().reshape(-1), np.arange(256))
+    rec = rec.cpu().numpy()
+    same = np.mean(rec.view(np.uint16) == keys.view(np.uint16))
+    check_recon(rec, keys.astype(np.float64), "fp16", "identity codebook")
+    print(f"[identity] bit-identical fp16 elements: {same:.4f}")
+    assert same > 0.98
+
+
+# ----------------------------------------------------------------------------
+# key encode throughput workload at full size (sampled oracle)
+# ----------------------------------------------------------------------------
+def test_encode_full_size_sampled():
+    c = synth.encode(oracle_transform)
+    k, s, C = c["keys"], c["smooth"], c["k_codebook"]
+    rec, codes = vq_encode_decode(dev(k), dev(C), c["dk"], smooth=dev(s))
+    codes_only = vq_encode(dev(k), dev(C), c["dk"], smooth=dev(s))
+    torch.cuda.synchronize()
+    codes, rec = codes.cpu().numpy(), rec.cpu().numpy()
+    assert np.array_equal(codes_only.cpu().numpy(), codes)
+    rng = np.random.default_rng(0)
+    total = 0
+    for h in range(c["H"]):
+        ts = np.sort(rng.choice(c["S"], 256, replace=False))
+        kk = np.ascontiguousarray(k[:, h:h + 1, ts])
+        total += check_codes(kk, C, c["dk"], s[h:h + 1], True, codes[:, h:h + 1, ts], f"encode h{h}")
+        check_recon(rec[:, h:h + 1, ts], O.decode(codes[:, h:h + 1, ts], C, s[h:h + 1], True), "fp16",
+                    f"encode h{h}")
+    assert total <= 5
+
+
+def test_decode_entry_point():
+    rng = np.random.default_rng(1)
+    B, H, S_cap, D, d = 2, 3, 40, 128, 8
+    C = rng.standard_normal((256, d)).astype(np.float32)
+    s = rng.uniform(0.5, 4, size=(H, D)).astype(np.float32)
+    codes = rng.integers(0, 256, size=(B, H, S_cap, D // d), dtype=np.uint8)
+    out = vq_decode(dev(codes), dev(C), smooth=dev(s), S=25, S_off=7)
+    out16 = vq_decode(dev(codes), dev(C), smooth=dev(s), S=25, S_off=7, out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    ref = O.decode(codes[:, :, 7:32], C, s, True)
+    check_recon(out.cpu().numpy(), ref, "fp32", "decode")
+    check_recon(out16.cpu().numpy(), ref, "fp16", "decode fp16")
+    out = vq_decode(dev(codes), dev(C), transform=False, S=10, S_off=0)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), O.pvq_decode(codes[:, :, :10], C).astype(np.float32))
+
+
+@pytest.mark.parametrize("D,d,n_c", [(32, 1, 256), (32, 4, 7), (64, 16, 256), (128, 2, 256),
+                                     (128, 16, 64), (256, 4, 256), (256, 8, 1)])
+def test_encode_shapes(D, d, n_c):
+    rng = np.random.default_rng(D * 100 + d)
+    B, H, S = 2, 3, 37                       # ragged tail of token-heads
+    k = synth.outlier_normal(rng, (B, H, S, D), 2)
+    s = synth.smooth_factors(k)
+    xt = O.forward_transform(k, s, True).reshape(-1, d)
+    C = synth.sample_rows(rng, xt, n_c)
+    rec, codes = vq_encode_decode(dev(k), dev(C), d, smooth=dev(s[0]), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy()
+    check_codes(k, C, d, s[0], True, codes, f"D{D} d{d}")
+    check_recon(rec.cpu().numpy(), O.decode(codes, C, s[0], True), "fp32", f"D{D} d{d}")
+
+
+def test_encode_append_and_row_offsets():
+    rng = np.random.default_rng(2)
+    B, H, S, D, d, S_cap = 3, 2, 5, 64, 4, 20
+    k = synth.outlier_normal(rng, (B, H, S, D), 2)
+    C = rng.standard_normal((256, d)).astype(np.float32)
+    buf = torch.full((B, H, S_cap, D // d), 0xAB, dtype=torch.uint8, device=DEV)
+    vq_encode(dev(k), dev(C), d, transform=False, codes=buf, S_off=9)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    ref, _ = O.encode(k, C, d)
+    assert np.array_equal(got[:, :, 9:14], ref)
+    assert np.all(got[:, :, :9] == 0xAB) and np.all(got[:, :, 14:] == 0xAB)
+    buf.fill_(0xAB)
+    offs = [0, 15, 7]
+    vq_encode(dev(k), dev(C), d, transform=False, codes=buf, row_offsets=offs)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    for b, o in enumerate(offs):
+        assert np.array_equal(got[b, :, o:o + S], ref[b])
+        mask = np.ones(S_cap, bool)
+        mask[o:o + S] = False
+        assert np.all(got[b][:, mask] == 0xAB)
+
+
+# ----------------------------------------------------------------------------
+# decode attention over random codes
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("S_kv", [512, 2048, 8192])
+def test_decode_attend(S_kv):
+    c = synth.decode(S_kv)
+    out = run_attend(c)
+    check_attn(out, oracle_attend(c, c["k_codes"], c["v_codes"]), f"decode S{S_kv}")
+
+
+@pytest.mark.parametrize("window", [0, 4096])
+def test_gqa_long_sampled(window):
+    enc = synth.encode(oracle_transform)
+    c = synth.gqa_long(window, k_codebook=enc["k_codebook"], smooth=enc["smooth"])
+    out = run_attend(c)
+    rng = np.random.default_rng(window + 1)
+    rows = [(b, int(h)) for b in range(c["B"]) for h in rng.choice(c["H_q"], 2, replace=False)]
+    rows = [rows[i] for i in rng.choice(len(rows), 12, replace=False)]
+    ref = oracle_attend(c, c["k_codes"], c["v_codes"], rows=rows)
+    for b, h in rows:
+        check_attn(out[b, h], ref[b, h], f"gqa W{window} b{b} h{h}")
+
+
+def test_prefill_append_and_attend_sampled():
+    c = synth.prefill(oracle_transform)
+    kbuf, vbuf = dev(c["k_codes"]), dev(c["v_codes"])
+    vq_encode(dev(c["keys"]), dev(c["k_codebook"]), c["dk"], smooth=dev(c["smooth"]), codes=kbuf,
+              S_off=c["S_off"])
+    vq_encode(dev(c["values"]), dev(c["v_codebook"]), c["dv"], transform=False, codes=vbuf,
+              S_off=c["S_off"])
+    torch.cuda.synchronize()
+    kc, vc = kbuf.cpu().numpy(), vbuf.cpu().numpy()
+    lo, hi = c["S_off"], c["S_off"] + c["S_q"]
+    assert np.array_equal(kc[:, :, :lo], c["k_codes"][:, :, :lo])
+    assert np.all(kc[:, :, hi:] == 0) and np.all(vc[:, :, hi:] == 0)
+    rng = np.random.default_rng(5)
+    for b, h in [(0, 0), (3, 7)]:
+        check_codes(c["keys"][b:b + 1, h:h + 1], c["k_codebook"], c["dk"], c["smooth"][h:h + 1],
+                    True, kc[b:b + 1, h:h + 1, lo:hi], f"prefill keys b{b} h{h}")
+        check_codes(c["values"][b:b + 1, h:h + 1], c["v_codebook"], c["dv"], None, False,
+                    vc[b:b + 1, h:h + 1, lo:hi], f"prefill values b{b} h{h}")
+    out = run_attend(c, k_codes=kc, v_codes=vc)
+    rows = [(0, 0), (1, 3), (2, 5), (3, 7)]
+    ref = oracle_attend(c, kc, vc, rows=rows)
+    for b, h in rows:
+        check_attn(out[b, h], ref[b, h], f"prefill b{b} h{h}")
+
+
+# ----------------------------------------------------------------------------
+# edge cases and metamorphic checks
+# ----------------------------------------------------------------------------
+def small_case(seed, B=3, Hq=6, Hkv=2, Sq=3, D=64, dk=4, dv=4, n_c=256, S_cap=300):
+    rng = np.random.default_rng(seed)
+    return dict(B=B, H_q=Hq, H_kv=Hkv, S_q=Sq, D=D, dk=dk, dv=dv,
+                q=synth.outlier_normal(rng, (B, Hq, Sq, D), 2),
+                k_codes=rng.integers(0, n_c, size=(B, Hkv, S_cap, D // dk), dtype=np.uint8),
+                v_codes=rng.integers(0, n_c, size=(B, Hkv, S_cap, D // dv), dtype=np.uint8),
+                k_codebook=rng.standard_normal((n_c, dk)).astype(np.float32),
+                v_codebook=rng.standard_normal((n_c, dv)).astype(np.float32),
+                smooth=rng.uniform(0.5, 5, size=(Hkv, D)).astype(np.float32),
+                kv_lens=np.array([S_cap, 1, 150][:B], np.int32), scale=1 / math.sqrt(D),
+                causal=True, window=0)
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 1), (True, 7), (False, 0),
+                                           (False, 5), (True, 10000)])
+def test_masks_gqa_multi_query(causal, window):
+    c = small_case(10, S_cap=700)
+    c["kv_lens"] = np.array([700, 2, 333], np.int32)
+    p = dict(c, causal=causal, window=window)
+    out = run_attend(p)
+    check_attn(out, oracle_attend(p, c["k_codes"], c["v_codes"]), f"masks c{causal} W{window}")
+
+
+def test_empty_and_short_rows():
+    c = small_case(11, Sq=4)
+    c["kv_lens"] = np.array([0, 2, 300], np.int32)      # empty row; causal row shorter than S_q
+    out = run_attend(c)
+    ref = oracle_attend(c, c["k_codes"], c["v_codes"])
+    assert np.all(out[0] == 0) and np.all(out[1, :, :2] == 0)
+    check_attn(out, ref, "empty/short")
+
+
+@pytest.mark.parametrize("D,dk,dv,n_c", [(128, 8, 8, 256), (128, 4, 2, 256), (64, 16, 1, 16),
+                                         (256, 4, 16, 256), (32, 2, 4, 200), (128, 8, 4, 1)])
+def test_attend_shapes(D, dk, dv, n_c):
+    c = small_case(D + dk + dv, D=D, dk=dk, dv=dv, n_c=n_c, Sq=1, Hq=8, Hkv=8)
+    out = run_attend(c)
+    check_attn(out, oracle_attend(c, c["k_codes"], c["v_codes"]), f"D{D} dk{dk} dv{dv} nc{n_c}")
+
+
+def test_split_invariance_and_gqa_equivalence():
+    """The same keys in a larger buffer (different split plan) and the GQA
+    layout vs repeated kv heads give the same output."""
+    c = small_case(12, B=2, Hq=8, Hkv=2, Sq=1, D=128, dk=8, S_cap=3000)
+    c["kv_lens"] = np.array([2900, 1777], np.int32)
+    a = run_attend(c)
+    big = dict(c)
+    pad = lambda x: np.concatenate([x, np.zeros((2, 2, 40000 - 3000, x.shape[3]), np.uint8)], 2)
+    big["k_codes"], big["v_codes"] = pad(c["k_codes"]), pad(c["v_codes"])
+    b = run_attend(big)
+    assert np.max(np.abs(a.astype(np.float64) - b)) <= 2e-3
+    rep = dict(c, H_kv=8, k_codes=np.repeat(c["k_codes"], 4, 1), v_codes=np.repeat(c["v_codes"], 4, 1),
+               smooth=np.repeat(c["smooth"], 4, 0))
+    m = run_attend(rep)
+    assert np.max(np.abs(a.astype(np.float64) - m)) <= 2e-3
+    check_attn(a, oracle_attend(c, c["k_codes"], c["v_codes"]), "split/gqa")

@@ -1,0 +1,189 @@
+"""Python binding of libvq: same names as the C ABI, torch tensors in and out.
+
+Argument marshalling only: shapes are read off the tensors, device pointers
+and the current HIP stream are passed to the C functions, and a nonzero
+status becomes a VQError.  Every step of the computation runs in the HIP
+kernels of libvq.so; there is no other implementation behind these calls.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+VQ_OK, VQ_ERR_INVALID_ARGUMENT, VQ_ERR_UNSUPPORTED, VQ_ERR_NO_DEVICE, VQ_ERR_HIP, VQ_ERR_WORKSPACE = range(6)
+
+
+class VQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+        self.message = message
+
+
+def _call(name, *args, prepare=False, result=None):
+    """Call the C function now, or (prepare=True) return a zero-argument
+    callable that makes the same call with the already-marshalled arguments
+    (for launch loops: the tensors must stay alive and unchanged in shape)."""
+    lib = _lib.load()
+    fn = getattr(lib, name)
+
+    def run():
+        st = fn(*args)
+        if st != VQ_OK:
+            raise VQError(st, lib.vq_last_error().decode() or lib.vq_status_string(st).decode())
+        return result
+
+    return run if prepare else run()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _need(t, name, dtype, ndim):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _smooth(smooth):
+    if smooth is None:
+        return None, 1
+    if smooth.dtype != torch.float32 or not smooth.is_cuda or not smooth.is_contiguous():
+        raise ValueError("smooth must be a contiguous fp32 device tensor")
+    if smooth.dim() == 1:
+        return smooth, 1
+    if smooth.dim() == 2:
+        return smooth, smooth.shape[0]
+    raise ValueError("smooth must be [D] or [H, D]")
+
+
+def vq_supports_shape(n_centroids: int, n_sub: int, head_dim: int) -> bool:
+    return bool(_lib.load().vq_supports_shape(n_centroids, n_sub, head_dim))
+
+
+def vq_encode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=None,
+              S_cap=None, S_off=0, row_offsets=None, stream=None, prepare=False):
+    """Encode fp16 keys [B, H, S, D] into uint8 codes [B, H, S_cap, D // sub_dim].
+
+    Codes of token t of row b land in slot off_b + t (off_b = row_offsets[b]
+    or S_off).  Returns the code tensor (allocated when `codes` is None)."""
+    _need(keys, "keys", torch.float16, 4)
+    _need(codebook, "codebook", torch.float32, 2)
+    B, H, S, D = keys.shape
+    if codes is None:
+        codes = torch.zeros((B, H, S_cap or S, D // sub_dim), dtype=torch.uint8, device=keys.device)
+    _need(codes, "codes", torch.uint8, 4)
+    sm, rows = _smooth(smooth)
+    offs = None
+    if row_offsets is not None:
+        offs = (ctypes.c_int32 * B)(*[int(x) for x in row_offsets])
+    return _call("vq_encode", _ptr(keys), B, H, S, D, _ptr(codebook), codebook.shape[0], sub_dim,
+                 _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off, offs,
+                 _stream(stream), prepare=prepare, result=codes)
+
+
+def vq_encode_decode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=None,
+                     S_cap=None, S_off=0, row_offsets=None, recon=None,
+                     out_dtype=torch.float16, stream=None, prepare=False):
+    """Fused encode + reconstruction.  Returns (recon [B, H, S, D], codes)."""
+    _need(keys, "keys", torch.float16, 4)
+    _need(codebook, "codebook", torch.float32, 2)
+    B, H, S, D = keys.shape
+    if codes is None:
+        codes = torch.zeros((B, H, S_cap or S, D // sub_dim), dtype=torch.uint8, device=keys.device)
+    _need(codes, "codes", torch.uint8, 4)
+    if recon is None:
+        recon = torch.empty((B, H, S, D), dtype=out_dtype, device=keys.device)
+    if recon.dtype not in (torch.float32, torch.float16):
+        raise ValueError("recon must be fp32 or fp16")
+    sm, rows = _smooth(smooth)
+    offs = None
+    if row_offsets is not None:
+        offs = (ctypes.c_int32 * B)(*[int(x) for x in row_offsets])
+    return _call("vq_encode_decode", _ptr(keys), B, H, S, D, _ptr(codebook), codebook.shape[0],
+                 sub_dim, _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off,
+                 offs, _ptr(recon), 1 if recon.dtype == torch.float16 else 0, _stream(stream),
+                 prepare=prepare, result=(recon, codes))
+
+
+def vq_decode(codes, codebook, *, smooth=None, transform=True, S=None, S_off=0,
+              out=None, out_dtype=torch.float32, stream=None, prepare=False):
+    """Decode slots [S_off, S_off + S) of codes [B, H, S_cap, n_sub] into
+    [B, H, S, n_sub * sub_dim] (fp32 by default)."""
+    _need(codes, "codes", torch.uint8, 4)
+    _need(codebook, "codebook", torch.float32, 2)
+    B, H, S_cap, n_sub = codes.shape
+    sub_dim = codebook.shape[1]
+    D = n_sub * sub_dim
+    S = S_cap - S_off if S is None else S
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=out_dtype, device=codes.device)
+    sm, rows = _smooth(smooth)
+    return _call("vq_decode", _ptr(codes), B, H, S, S_cap, S_off, _ptr(codebook), codebook.shape[0],
+                 sub_dim, _ptr(sm), rows, int(bool(transform)), D, _ptr(out),
+                 1 if out.dtype == torch.float16 else 0, _stream(stream), prepare=prepare,
+                 result=out)
+
+
+def vq_attend_workspace_bytes(B, H_q, S_q, D, H_kv, S_cap, sliding_window=0) -> int:
+    return int(_lib.load().vq_attend_workspace_bytes(B, H_q, S_q, D, H_kv, S_cap, sliding_window))
+
+
+def attend_workspace(q, k_codes, sliding_window=0):
+    """A zero-filled workspace sized for vq_attend on these shapes."""
+    B, Hq, Sq, D = q.shape
+    n = vq_attend_workspace_bytes(B, Hq, Sq, D, k_codes.shape[1], k_codes.shape[2], sliding_window)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None,
+              transform=True, kv_lens=None, causal=True, sliding_window=0, out=None,
+              workspace=None, stream=None, prepare=False):
+    """Attention of raw fp16 queries [B, H_q, S_q, D] over key/value codes
+    [B, H_kv, S_cap, n_sub]; returns fp16 [B, H_q, S_q, D]."""
+    _need(q, "q", torch.float16, 4)
+    _need(k_codes, "k_codes", torch.uint8, 4)
+    _need(v_codes, "v_codes", torch.uint8, 4)
+    _need(k_codebook, "k_codebook", torch.float32, 2)
+    _need(v_codebook, "v_codebook", torch.float32, 2)
+    B, Hq, Sq, D = q.shape
+    Hkv, S_cap = k_codes.shape[1], k_codes.shape[2]
+    if tuple(v_codes.shape[:3]) != (B, Hkv, S_cap) or k_codes.shape[0] != B:
+        raise ValueError("k_codes and v_codes must share [B, H_kv, S_cap]")
+    if k_codebook.shape[0] != v_codebook.shape[0]:
+        raise ValueError("key and value codebooks disagree on n_centroids")
+    if k_codes.shape[3] * k_codebook.shape[1] != D or v_codes.shape[3] * v_codebook.shape[1] != D:
+        raise ValueError("n_sub * sub_dim must equal D for keys and values")
+    if kv_lens is not None:
+        _need(kv_lens, "kv_lens", torch.int32, 1)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float16, device=q.device)
+    _need(out, "out", torch.float16, 4)
+    if workspace is None:
+        workspace = attend_workspace(q, k_codes, sliding_window)
+    sm, rows = _smooth(smooth)
+    return _call("vq_attend", _ptr(q), B, Hq, Sq, D, _ptr(k_codes), _ptr(k_codebook),
+                 k_codebook.shape[1], _ptr(sm), rows, int(bool(transform)), _ptr(v_codes),
+                 _ptr(v_codebook), v_codebook.shape[1], k_codebook.shape[0], Hkv, S_cap,
+                 _ptr(kv_lens), float(scale), int(bool(causal)), int(sliding_window), _ptr(out),
+                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
+                 prepare=prepare, result=out)

@@ -1,0 +1,283 @@
+// C ABI of libvq: host-side validation, then kernel launches on the caller's
+// stream.  Every check runs before the first HIP call, so invalid arguments
+// never reach the device and every error path is reachable without a GPU.
+#include "vq_internal.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+namespace vq {
+
+namespace {
+thread_local char g_last_error[512] = "";
+
+int device_count() {
+  // -1 = not probed yet.  Devices do not appear during a process's life.
+  static std::atomic<int> cached{-1};
+  int n = cached.load(std::memory_order_acquire);
+  if (n < 0) {
+    int c = 0;
+    if (hipGetDeviceCount(&c) != hipSuccess) {
+      (void)hipGetLastError();
+      c = 0;
+    }
+    cached.store(c, std::memory_order_release);
+    n = c;
+  }
+  return n;
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool supported_head_dim(int D) { return D == 32 || D == 64 || D == 128 || D == 256; }
+
+bool supported_sub_dim(int d) { return d == 1 || d == 2 || d == 4 || d == 8 || d == 16; }
+
+int check_quantizer(const char* what, int D, int n_c, int sub_dim) {
+  if (D <= 0) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: D must be positive (got %d)", what, D);
+  if (sub_dim <= 0) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: sub_dim must be positive (got %d)", what, sub_dim);
+  if (D % sub_dim != 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: D (%d) is not divisible by sub_dim (%d)", what, D, sub_dim);
+  if (n_c <= 0) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: n_centroids must be positive (got %d)", what, n_c);
+  if (n_c > 256)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: n_centroids %d does not fit uint8 codes (max 256)", what, n_c);
+  if (!vq_supports_shape(n_c, D / sub_dim, D))
+    return fail(VQ_ERR_UNSUPPORTED, "%s: (n_centroids=%d, n_sub=%d, head_dim=%d) is outside the compiled caps",
+                what, n_c, D / sub_dim, D);
+  return VQ_OK;
+}
+
+int check_smooth(const char* what, const float* smooth, int smooth_rows, int H) {
+  if (smooth && smooth_rows != 1 && smooth_rows != H)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: smooth_rows must be 1 or %d (got %d)", what, H, smooth_rows);
+  return VQ_OK;
+}
+
+int check_transform(const char* what, int transform, int D) {
+  if (transform != 0 && transform != 1)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: transform must be 0 or 1 (got %d)", what, transform);
+  if (transform == 1 && !is_pow2(D))
+    return fail(VQ_ERR_UNSUPPORTED, "%s: the Walsh-Hadamard transform needs a power-of-two D (got %d)", what, D);
+  return VQ_OK;
+}
+
+int check_device(const char* what) {
+  if (device_count() <= 0) return fail(VQ_ERR_NO_DEVICE, "%s: no HIP device is visible", what);
+  return VQ_OK;
+}
+
+int hip_status(const char* what, hipError_t e) {
+  if (e == hipSuccess) return VQ_OK;
+  return fail(VQ_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+// Shared validation of vq_encode / vq_encode_decode.
+int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
+                 const float* codebook, int n_c, int sub_dim, const float* smooth,
+                 int smooth_rows, int transform, const uint8_t* codes, int S_cap, int S_off,
+                 const int32_t* row_offsets) {
+  if (B < 0 || H <= 0 || S < 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0, H > 0, S >= 0 (got %d, %d, %d)", what, B, H, S);
+  if (!keys || !codebook || !codes)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: keys, codebook and codes must be non-null", what);
+  int st = check_quantizer(what, D, n_c, sub_dim);
+  if (st) return st;
+  if ((st = check_smooth(what, smooth, smooth_rows, H))) return st;
+  if ((st = check_transform(what, transform, D))) return st;
+  if (S_cap <= 0) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: S_cap must be positive (got %d)", what, S_cap);
+  if (row_offsets) {
+    if (B > VQ_MAX_ROW_OFFSETS)
+      return fail(VQ_ERR_INVALID_ARGUMENT, "%s: per-row offsets support B <= %d (got %d)", what,
+                  VQ_MAX_ROW_OFFSETS, B);
+    for (int b = 0; b < B; ++b) {
+      const long long o = row_offsets[b];
+      if (o < 0 || o + S > S_cap)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "%s: row %d writes slots [%lld, %lld) outside [0, %d)", what, b, o,
+                    o + S, S_cap);
+    }
+  } else if (S_off < 0 || (long long)S_off + S > S_cap) {
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: slots [%d, %lld) fall outside [0, %d)", what, S_off,
+                (long long)S_off + S, S_cap);
+  }
+  return VQ_OK;
+}
+
+int run_encode(const char* what, const void* keys, const uint8_t* codes_in, int B, int H, int S,
+               int D, const float* codebook, int n_c, int sub_dim, const float* smooth,
+               int smooth_rows, int transform, uint8_t* codes, int S_cap, int S_off,
+               const int32_t* row_offsets, void* recon, int out_dtype, int mode, void* stream) {
+  if (B == 0 || S == 0) return VQ_OK;
+  int st = check_device(what);
+  if (st) return st;
+  EncodeArgs a{};
+  a.keys = reinterpret_cast<const __half*>(keys);
+  a.codes_in = codes_in;
+  a.codebook = codebook;
+  a.smooth = smooth;
+  a.codes = codes;
+  a.recon = recon;
+  a.B = B; a.H = H; a.S = S; a.D = D; a.n_c = n_c; a.sub_dim = sub_dim;
+  a.smooth_rows = smooth_rows; a.transform = transform;
+  a.S_cap = S_cap; a.S_off = S_off; a.use_row_offsets = row_offsets != nullptr;
+  a.recon_dtype = out_dtype;
+  RowOffsets offs{};
+  if (row_offsets)
+    for (int b = 0; b < B; ++b) offs.v[b] = row_offsets[b];
+  return hip_status(what, launch_encode(a, row_offsets ? &offs : nullptr, mode,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+}  // namespace vq
+
+using namespace vq;
+
+extern "C" {
+
+const char* vq_status_string(int status) {
+  switch (status) {
+    case VQ_OK: return "ok";
+    case VQ_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case VQ_ERR_UNSUPPORTED: return "unsupported shape";
+    case VQ_ERR_NO_DEVICE: return "no HIP device";
+    case VQ_ERR_HIP: return "HIP runtime error";
+    case VQ_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+const char* vq_last_error(void) { return g_last_error; }
+
+int vq_version(void) { return 100; }
+
+int vq_supports_shape(int n_centroids, int n_sub, int head_dim) {
+  if (n_centroids < 1 || n_centroids > 256) return 0;
+  if (!supported_head_dim(head_dim)) return 0;
+  if (n_sub < 1 || n_sub > 64 || head_dim % n_sub != 0) return 0;
+  return supported_sub_dim(head_dim / n_sub) ? 1 : 0;
+}
+
+int vq_encode(const void* keys_f16, int B, int H, int S, int D, const float* codebook,
+              int n_centroids, int sub_dim, const float* smooth, int smooth_rows, int transform,
+              uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_encode("vq_encode", keys_f16, B, H, S, D, codebook, n_centroids, sub_dim, smooth,
+                        smooth_rows, transform, codes, S_cap, S_off, row_offsets);
+  if (st) return st;
+  return run_encode("vq_encode", keys_f16, nullptr, B, H, S, D, codebook, n_centroids, sub_dim,
+                    smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets, nullptr, 0,
+                    0, stream);
+}
+
+int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D, const float* codebook,
+                     int n_centroids, int sub_dim, const float* smooth, int smooth_rows,
+                     int transform, uint8_t* codes, int S_cap, int S_off,
+                     const int32_t* row_offsets, void* recon, int out_dtype, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_encode("vq_encode_decode", keys_f16, B, H, S, D, codebook, n_centroids, sub_dim,
+                        smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets);
+  if (st) return st;
+  if (!recon) return fail(VQ_ERR_INVALID_ARGUMENT, "vq_encode_decode: recon must be non-null");
+  if (out_dtype != 0 && out_dtype != 1)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "vq_encode_decode: out_dtype must be 0 (fp32) or 1 (fp16)");
+  return run_encode("vq_encode_decode", keys_f16, nullptr, B, H, S, D, codebook, n_centroids,
+                    sub_dim, smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets,
+                    recon, out_dtype, 1, stream);
+}
+
+int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
+              const float* codebook, int n_centroids, int sub_dim, const float* smooth,
+              int smooth_rows, int transform, int D, void* out, int out_dtype, void* stream) {
+  g_last_error[0] = 0;
+  const char* what = "vq_decode";
+  if (B < 0 || H <= 0 || S < 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0, H > 0, S >= 0 (got %d, %d, %d)", what, B, H, S);
+  if (!codes || !codebook || !out)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: codes, codebook and out must be non-null", what);
+  int st = check_quantizer(what, D, n_centroids, sub_dim);
+  if (st) return st;
+  if ((st = check_smooth(what, smooth, smooth_rows, H))) return st;
+  if ((st = check_transform(what, transform, D))) return st;
+  if (out_dtype != 0 && out_dtype != 1)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: out_dtype must be 0 (fp32) or 1 (fp16)", what);
+  if (S_cap <= 0 || S_off < 0 || (long long)S_off + S > S_cap)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: slots [%d, %lld) fall outside [0, %d)", what, S_off,
+                (long long)S_off + S, S_cap);
+  return run_encode(what, nullptr, codes, B, H, S, D, codebook, n_centroids, sub_dim, smooth,
+                    smooth_rows, transform, nullptr, S_cap, S_off, nullptr, out, out_dtype, 2,
+                    stream);
+}
+
+size_t vq_attend_workspace_bytes(int B, int H_q, int S_q, int D, int H_kv, int S_cap,
+                                 int sliding_window) {
+  AttendPlan p;
+  if (!plan_attend(B, H_q, S_q, D, H_kv, S_cap, sliding_window, &p)) return 0;
+  return p.workspace_bytes;
+}
+
+int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* k_codes,
+              const float* k_codebook, int k_sub_dim, const float* smooth, int smooth_rows,
+              int transform, const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
+              int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens, float scale,
+              int causal, int sliding_window, void* out_f16, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  const char* what = "vq_attend";
+  if (B < 0 || S_q < 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0 and S_q >= 0 (got %d, %d)", what, B, S_q);
+  if (H_q <= 0 || H_kv <= 0 || S_cap <= 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need H_q, H_kv, S_cap > 0 (got %d, %d, %d)", what, H_q, H_kv,
+                S_cap);
+  if (!q_f16 || !k_codes || !k_codebook || !v_codes || !v_codebook || !out_f16)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: q, codes, codebooks and out must be non-null", what);
+  if (H_q % H_kv != 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: H_q (%d) is not a multiple of H_kv (%d)", what, H_q, H_kv);
+  int st = check_quantizer("vq_attend (keys)", D, n_centroids, k_sub_dim);
+  if (st) return st;
+  if ((st = check_quantizer("vq_attend (values)", D, n_centroids, v_sub_dim))) return st;
+  if ((D / k_sub_dim) % 4 != 0 || (D / v_sub_dim) % 4 != 0)
+    return fail(VQ_ERR_UNSUPPORTED, "%s: the number of key and value sub-vectors must be multiples of 4", what);
+  if ((st = check_smooth(what, smooth, smooth_rows, H_kv))) return st;
+  if ((st = check_transform(what, transform, D))) return st;
+  if (causal != 0 && causal != 1)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1 (got %d)", what, causal);
+  if (sliding_window < 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: sliding_window must be >= 0 (got %d)", what, sliding_window);
+  if (!std::isfinite(scale)) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: scale must be finite", what);
+  if (B == 0 || S_q == 0) return VQ_OK;
+  AttendPlan plan;
+  if (!plan_attend(B, H_q, S_q, D, H_kv, S_cap, sliding_window, &plan))
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: no launch plan for this shape", what);
+  size_t lds = 0;
+  if (!attend_pick_rows(plan.rows, D / k_sub_dim, n_centroids, v_sub_dim, D / v_sub_dim, D, &lds))
+    return fail(VQ_ERR_UNSUPPORTED, "%s: the query LUT does not fit in LDS for this shape", what);
+  if (!workspace || workspace_bytes < plan.workspace_bytes)
+    return fail(VQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", what, plan.workspace_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((st = check_device(what))) return st;
+  AttendArgs a{};
+  a.q = reinterpret_cast<const __half*>(q_f16);
+  a.k_codes = k_codes; a.k_codebook = k_codebook; a.smooth = smooth;
+  a.v_codes = v_codes; a.v_codebook = v_codebook; a.kv_lens = kv_lens;
+  a.out = reinterpret_cast<__half*>(out_f16);
+  a.partials = reinterpret_cast<float*>(workspace);
+  a.B = B; a.Hq = H_q; a.Sq = S_q; a.D = D; a.Hkv = H_kv; a.S_cap = S_cap;
+  a.dk = k_sub_dim; a.dv = v_sub_dim; a.n_c = n_centroids;
+  a.smooth_rows = smooth_rows; a.transform = transform;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.causal = causal; a.window = sliding_window;
+  return hip_status(what, launch_attend(a, plan, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,445 @@
+// Split-K attention read directly from product-VQ key and value codes.
+//
+// Method ("Metal Kernels API" page, "Fused SDPA", metal_fused_sdpa;
+// "veloxquant_mlx.cache.vecinfer_cache module" page, fused_sdpa): the raw
+// query gets the dual transform q~ = (q * s) . H, so that
+// q~ . K~_t = q . K_hat_t; scores are sums of per-sub-vector query LUT
+// entries LUT[j][c] = <q~_j, C_k[c]> gathered by the key codes; softmax runs
+// online (base 2, scale and log2(e) folded into the LUT); values are
+// gathered from the value codebook by the value codes.
+//
+// Work decomposition (MI355X): one workgroup per (batch row, kv head,
+// row group of up to R query rows, split of the key axis).  The R rows of a
+// GQA group share one LUT in LDS laid out [j][code][row], so one code byte
+// fetches the score terms of every row with a single LDS read.  Each wave
+// owns a stream of 64-key chunks: lane = key for the score, mask and online
+// softmax; then lanes re-map to (4-dim slice of the head, key parity) to
+// accumulate values.  The four waves and the splits are merged with the
+// log-sum-exp rule (flash-decoding); splits are combined by a second kernel.
+#include "vq_internal.h"
+
+#include <algorithm>
+
+namespace vq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr size_t kLdsBudget = 160 * 1024;
+
+struct AttParams {
+  int B, Hq, Sq, Hkv, S_cap, dk, dv, n_c, nsk, nsv, smooth_rows, transform;
+  float fold;  // WHT normalization (if any) * scale * log2(e)
+  int causal, window;
+  int G, rows, R, n_rgroups, split_tokens, n_split;
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Reads R consecutive floats (R-aligned in the LDS) with vector loads.
+template <int R>
+__device__ __forceinline__ void lds_read_row(const float* e, float (&v)[R]) {
+  if constexpr (R == 1) {
+    v[0] = e[0];
+  } else if constexpr (R == 2) {
+    const float2 a = *reinterpret_cast<const float2*>(e);
+    v[0] = a.x; v[1] = a.y;
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; r += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(e + r);
+      v[r] = a.x; v[r + 1] = a.y; v[r + 2] = a.z; v[r + 3] = a.w;
+    }
+  }
+}
+
+// LDS carve-up, in floats (the code staging area is counted in bytes / 4).
+struct LdsLayout {
+  size_t lut, cv, qt, pst, vst, total_floats;
+};
+
+__host__ __device__ inline LdsLayout lds_layout(int nsk, int n_c, int dv, int nsv, int R, int D) {
+  // every region starts on a 16-byte boundary (vector LDS reads)
+  auto up4 = [](size_t v) { return (v + 3) / 4 * 4; };
+  LdsLayout L;
+  size_t o = 0;
+  L.lut = o; o += (size_t)nsk * n_c * R;
+  // the merge at the end reuses the LUT area: make sure it is large enough
+  const size_t merge = (size_t)kWaves * R * (D + 2);
+  if (o < merge) o = merge;
+  o = up4(o);
+  L.cv = o; o = up4(o + (size_t)n_c * dv);
+  L.qt = o; o = up4(o + (size_t)R * D);
+  L.pst = o; o = up4(o + (size_t)kWaves * 64 * R);
+  L.vst = o; o = up4(o + (size_t)kWaves * 64 * nsv / 4);
+  L.total_floats = o;
+  return L;
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(kThreads) void attend_split_kernel(
+    const __half* __restrict__ q, const uint8_t* __restrict__ kcodes,
+    const float* __restrict__ kcb, const float* __restrict__ smooth,
+    const uint8_t* __restrict__ vcodes, const float* __restrict__ vcb,
+    const int32_t* __restrict__ kv_lens, float* __restrict__ part, AttParams p) {
+  extern __shared__ float smem[];
+  const LdsLayout L = lds_layout(p.nsk, p.n_c, p.dv, p.nsv, R, D);
+  float* lut = smem + L.lut;
+  float* cv = smem + L.cv;
+  float* qt = smem + L.qt;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int unit = blockIdx.x;  // b * Hkv + g
+  const int rg = blockIdx.y;
+  const int s = blockIdx.z;
+  const int b = unit / p.Hkv, g = unit % p.Hkv;
+  int len = kv_lens ? kv_lens[b] : p.S_cap;
+  len = min(max(len, 0), p.S_cap);
+  const int lo_all = p.window > 0 ? max(0, len - p.Sq - p.window + 1) : 0;
+  const int s_lo = lo_all + s * p.split_tokens;
+  const int s_hi = min(s_lo + p.split_tokens, len);
+  float* out_part = part + (((size_t)unit * p.n_rgroups + rg) * p.n_split + s) * R * (D + 2);
+
+  if (s_lo >= s_hi) {  // nothing to attend in this split
+    if (tid < R) { out_part[tid * (D + 2)] = -INFINITY; out_part[tid * (D + 2) + 1] = 0.f; }
+    return;
+  }
+
+  // ---- rows of this workgroup ------------------------------------------
+  int qabs[R];
+  bool rvalid[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int gr = rg * R + r;
+    rvalid[r] = gr < p.rows;
+    const int i = rvalid[r] ? gr % p.Sq : 0;
+    qabs[r] = len - p.Sq + i;
+  }
+
+  // ---- dual transform of the queries: q~ = (q * s) . H ------------------
+  const float* srow = smooth ? smooth + (size_t)(p.smooth_rows == 1 ? 0 : g) * D : nullptr;
+  for (int idx = tid; idx < R * D; idx += kThreads) {
+    const int r = idx / D, c = idx % D;
+    const int gr = rg * R + r;
+    float v = 0.f;
+    if (gr < p.rows) {
+      const int hl = gr / p.Sq, i = gr % p.Sq;
+      const int h = g * p.G + hl;
+      v = __half2float(q[(((size_t)b * p.Hq + h) * p.Sq + i) * D + c]);
+      if (srow) v *= srow[c];
+    }
+    qt[idx] = v;
+  }
+  __syncthreads();
+  if (p.transform) {
+    for (int hb = 1; hb < D; hb <<= 1) {
+      for (int k = tid; k < R * D / 2; k += kThreads) {
+        const int r = k / (D / 2), m = k % (D / 2);
+        const int i0 = (m / hb) * 2 * hb + (m % hb), i1 = i0 + hb;
+        const float a = qt[r * D + i0], c = qt[r * D + i1];
+        qt[r * D + i0] = a + c;
+        qt[r * D + i1] = a - c;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- query LUT [j][code][row] and value codebook in LDS --------------
+  for (int idx = tid; idx < p.nsk * p.n_c; idx += kThreads) {
+    const int j = idx / p.n_c, c = idx % p.n_c;
+    const float* crow = kcb + (size_t)c * p.dk;
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    for (int e = 0; e < p.dk; ++e) {
+      const float ce = crow[e];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = fmaf(qt[r * D + j * p.dk + e], ce, acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] *= p.fold;
+#pragma unroll
+    for (int r = 0; r < R; ++r) lut[(size_t)idx * R + r] = acc[r];
+  }
+  for (int idx = tid; idx < p.n_c * p.dv; idx += kThreads) cv[idx] = vcb[idx];
+  __syncthreads();
+
+  // ---- stream the split's keys in 64-key chunks per wave ----------------
+  constexpr int QPL = D / 4;          // 4-dim slices per head
+  constexpr int TG = 64 / QPL;        // keys handled in parallel in the value phase
+  const int dq = lane % QPL, ts = lane / QPL;
+  float* pst = smem + L.pst + (size_t)wave * 64 * R;
+  uint32_t* vst = reinterpret_cast<uint32_t*>(smem + L.vst) + (size_t)wave * 64 * (p.nsv / 4);
+  const uint8_t* vst_b = reinterpret_cast<const uint8_t*>(vst);
+
+  float m[R], l[R], acc[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    m[r] = -INFINITY; l[r] = 0.f;
+    acc[r][0] = acc[r][1] = acc[r][2] = acc[r][3] = 0.f;
+  }
+
+  const int n_tok = s_hi - s_lo;
+  const int n_chunks = (n_tok + 63) / 64;
+  const int n_iter = (n_chunks + kWaves - 1) / kWaves;
+  const size_t row0 = (size_t)unit * p.S_cap;
+  const int nskw = p.nsk / 4, nsvw = p.nsv / 4;
+  const int cmax = p.n_c - 1;  // codes beyond the codebook are clamped, never read out of bounds
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int chunk = it * kWaves + wave;
+    const int t = s_lo + chunk * 64 + lane;
+    const bool tv = chunk < n_chunks && t < s_hi;
+
+    float sc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) sc[r] = 0.f;
+    if (tv) {
+      const uint32_t* kr = reinterpret_cast<const uint32_t*>(kcodes + (row0 + t) * p.nsk);
+      for (int jw = 0; jw < nskw; ++jw) {
+        const uint32_t w = kr[jw];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int code = min((int)((w >> (8 * k)) & 0xff), cmax);
+          const float* e = lut + ((size_t)(jw * 4 + k) * p.n_c + code) * R;
+          float v[R];
+          lds_read_row<R>(e, v);
+#pragma unroll
+          for (int r = 0; r < R; ++r) sc[r] += v[r];
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      bool ok = tv && rvalid[r];
+      if (p.causal) ok = ok && t <= qabs[r];
+      if (p.window > 0) ok = ok && t > qabs[r] - p.window;
+      if (!ok) sc[r] = -INFINITY;
+      const float cm = wave_max(sc[r]);
+      const float mn = fmaxf(m[r], cm);
+      const float alpha = (mn == -INFINITY) ? 1.f : exp2f(m[r] - mn);
+      const float pr = (sc[r] == -INFINITY) ? 0.f : exp2f(sc[r] - mn);
+      l[r] = l[r] * alpha + pr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[r][e] *= alpha;
+      m[r] = mn;
+      pst[lane * R + r] = pr;
+    }
+    {
+      const uint32_t* vr = reinterpret_cast<const uint32_t*>(vcodes + (row0 + (tv ? t : 0)) * p.nsv);
+      for (int jw = 0; jw < nsvw; ++jw) vst[lane * nsvw + jw] = tv ? vr[jw] : 0u;
+    }
+    __syncthreads();
+
+    for (int tt = 0; tt < 64 / TG; ++tt) {
+      const int tk = tt * TG + ts;
+      float pr[R];
+      lds_read_row<R>(pst + tk * R, pr);
+      const uint8_t* cr = vst_b + (size_t)tk * p.nsv;
+      float c4[4];
+      if (p.dv >= 4) {
+        const int dim0 = 4 * dq;
+        const int code = min((int)cr[dim0 / p.dv], cmax);
+        const float4 v = *reinterpret_cast<const float4*>(cv + code * p.dv + dim0 % p.dv);
+        c4[0] = v.x; c4[1] = v.y; c4[2] = v.z; c4[3] = v.w;
+      } else if (p.dv == 2) {
+        const int c0 = min((int)cr[2 * dq], cmax), c1 = min((int)cr[2 * dq + 1], cmax);
+        c4[0] = cv[c0 * 2]; c4[1] = cv[c0 * 2 + 1];
+        c4[2] = cv[c1 * 2]; c4[3] = cv[c1 * 2 + 1];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c4[e] = cv[min((int)cr[4 * dq + e], cmax)];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(pr[r], c4[e], acc[r][e]);
+    }
+    __syncthreads();
+  }
+
+  // ---- merge lanes, then waves ------------------------------------------
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    l[r] = wave_sum(l[r]);
+#pragma unroll
+    for (int o = QPL; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[r][e] += __shfl_xor(acc[r][e], o);
+  }
+  float* wm = smem;                    // [kWaves][R]
+  float* wl = wm + kWaves * R;         // [kWaves][R]
+  float* wacc = wl + kWaves * R;       // [kWaves][R][D]
+  // the LUT area is free once every wave has left the loop
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) { wm[wave * R + r] = m[r]; wl[wave * R + r] = l[r]; }
+  }
+  if (ts == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wacc[((size_t)wave * R + r) * D + 4 * dq + e] = acc[r][e];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < R * (D + 2); idx += kThreads) {
+    const int r = idx / (D + 2), c = idx % (D + 2);
+    if (rg * R + r >= p.rows) continue;
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * R + r]);
+    float v;
+    if (c == 0) {
+      v = M;
+    } else {
+      v = 0.f;
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = wm[w * R + r];
+        const float om = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        v += om * (c == 1 ? wl[w * R + r] : wacc[((size_t)w * R + r) * D + (c - 2)]);
+      }
+    }
+    out_part[idx] = v;
+  }
+}
+
+// One block per output row: combine the splits with the log-sum-exp rule.
+template <int D>
+__global__ __launch_bounds__(D) void attend_merge_kernel(const float* __restrict__ part,
+                                                          __half* __restrict__ out, AttParams p) {
+  const int row = blockIdx.x;  // ((b * Hq + h) * Sq + i)
+  const int i = row % p.Sq;
+  const int bh = row / p.Sq;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  const int g = h / p.G, hl = h % p.G;
+  const int unit = b * p.Hkv + g;
+  const int gr = hl * p.Sq + i;
+  const int rg = gr / p.R, r = gr % p.R;
+  const float* base = part + ((size_t)unit * p.n_rgroups + rg) * p.n_split * p.R * (D + 2) +
+                      (size_t)r * (D + 2);
+  const size_t stride = (size_t)p.R * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, base[s * stride]);
+  float lsum = 0.f, a = 0.f;
+  for (int s = 0; s < p.n_split; ++s) {
+    const float ms = base[s * stride];
+    if (ms == -INFINITY) continue;
+    const float om = exp2f(ms - M);
+    lsum += om * base[s * stride + 1];
+    a += om * base[s * stride + 2 + threadIdx.x];
+  }
+  out[(size_t)row * D + threadIdx.x] = __float2half_rn(lsum > 0.f ? a / lsum : 0.f);
+}
+
+template <int D, int R>
+hipError_t launch_dr(const AttendArgs& a, const AttParams& p, size_t lds_bytes, hipStream_t st) {
+  auto k = attend_split_kernel<D, R>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+  if (e != hipSuccess) return e;
+  dim3 grid(a.B * a.Hkv, p.n_rgroups, p.n_split);
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), lds_bytes, st, a.q, a.k_codes, a.k_codebook,
+                     a.smooth, a.v_codes, a.v_codebook, a.kv_lens, a.partials, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(a.B * a.Hq * a.Sq), dim3(D), 0, st,
+                     a.partials, a.out, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttendArgs& a, const AttParams& p, size_t lds_bytes, hipStream_t st) {
+  switch (p.R) {
+    case 1: return launch_dr<D, 1>(a, p, lds_bytes, st);
+    case 2: return launch_dr<D, 2>(a, p, lds_bytes, st);
+    case 4: return launch_dr<D, 4>(a, p, lds_bytes, st);
+    case 8: return launch_dr<D, 8>(a, p, lds_bytes, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, AttendPlan* pl) {
+  if (B <= 0 || Hq <= 0 || Sq <= 0 || D <= 0 || Hkv <= 0 || S_cap <= 0 || window < 0) return false;
+  if (Hq % Hkv != 0) return false;
+  pl->G = Hq / Hkv;
+  pl->rows = pl->G * Sq;
+  const long long max_range =
+      window > 0 ? std::min<long long>(S_cap, (long long)Sq + window - 1) : S_cap;
+  // Aim for about 1024 workgroups (4 per CU on 256 CUs) across the
+  // independent (batch row, kv head, 8-row group) units, with at least 256
+  // keys per split so the per-workgroup LUT build stays amortized.
+  const long long units = (long long)B * Hkv * ((pl->rows + 7) / 8);
+  const long long target = std::max<long long>(1, (1024 + units - 1) / units);
+  long long T = (max_range + target - 1) / target;
+  T = (T + 63) / 64 * 64;
+  T = std::max<long long>(T, 256);
+  pl->split_tokens = (int)T;
+  pl->n_split = (int)std::max<long long>(1, (max_range + T - 1) / T);
+  const long long rows8 = (pl->rows + 7) / 8 * 8;
+  pl->workspace_bytes = (size_t)B * Hkv * rows8 * pl->n_split * (D + 2) * sizeof(float);
+  pl->R = 0;
+  pl->n_rgroups = 0;
+  return true;
+}
+
+// LDS bytes of one workgroup for R rows; 0 if it does not fit.
+static size_t attend_lds_bytes(int nsk, int n_c, int dv, int nsv, int R, int D) {
+  const LdsLayout L = lds_layout(nsk, n_c, dv, nsv, R, D);
+  const size_t bytes = L.total_floats * sizeof(float);
+  return bytes <= kLdsBudget ? bytes : 0;
+}
+
+int attend_pick_rows(int rows, int nsk, int n_c, int dv, int nsv, int D, size_t* lds) {
+  int want = 1;
+  while (want < rows && want < 8) want <<= 1;
+  for (int R = want; R >= 1; R >>= 1) {
+    const size_t b = attend_lds_bytes(nsk, n_c, dv, nsv, R, D);
+    if (b) { *lds = b; return R; }
+  }
+  return 0;
+}
+
+hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_t st) {
+  AttParams p;
+  p.B = a.B; p.Hq = a.Hq; p.Sq = a.Sq; p.Hkv = a.Hkv; p.S_cap = a.S_cap;
+  p.dk = a.dk; p.dv = a.dv; p.n_c = a.n_c; p.nsk = a.D / a.dk; p.nsv = a.D / a.dv;
+  p.smooth_rows = a.smooth_rows; p.transform = a.transform;
+  p.causal = a.causal; p.window = a.window;
+  p.G = plan.G; p.rows = plan.rows; p.split_tokens = plan.split_tokens; p.n_split = plan.n_split;
+  size_t lds = 0;
+  p.R = attend_pick_rows(p.rows, p.nsk, p.n_c, p.dv, p.nsv, a.D, &lds);
+  if (p.R == 0) return hipErrorInvalidValue;
+  p.n_rgroups = (p.rows + p.R - 1) / p.R;
+  if (p.n_rgroups > 65535 || p.n_split > 65535) return hipErrorInvalidValue;
+  float norm = 1.f;
+  if (a.transform) {
+    switch (a.D) {
+      case 32: norm = WhtNorm<32>::value; break;
+      case 64: norm = WhtNorm<64>::value; break;
+      case 128: norm = WhtNorm<128>::value; break;
+      case 256: norm = WhtNorm<256>::value; break;
+    }
+  }
+  p.fold = norm * a.scale_log2e;
+  switch (a.D) {
+    case 32: return launch_d<32>(a, p, lds, st);
+    case 64: return launch_d<64>(a, p, lds, st);
+    case 128: return launch_d<128>(a, p, lds, st);
+    case 256: return launch_d<256>(a, p, lds, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vq

@@ -1,0 +1,263 @@
+// Product-VQ encode / decode kernels for gfx950.
+//
+// Method ("Metal Kernels API" page, "VecInfer kernels",
+// vecinfer_encode_decode_metal; "veloxquant_mlx.cache.vecinfer_cache module"
+// page, module description): smooth (x / s) -> normalized Walsh-Hadamard
+// rotation -> nearest centroid per sub-vector (squared L2, ties to the lowest
+// index) -> [codebook gather -> inverse rotation -> x s].
+//
+// Layout on the wave: one lane per (token-head, sub-vector j).  The lane
+// keeps its sub_dim values in registers; the rotation runs as an in-register
+// butterfly over the low log2(sub_dim) index bits and as cross-lane
+// butterflies (shuffles) over the high log2(D / sub_dim) bits, so a
+// token-head's D values never leave the register file.  The nearest-centroid
+// search walks the codebook with a wave-uniform centroid index, so every
+// centroid read is a scalar (SGPR) load shared by the 64 lanes; distances
+// and the running argmin stay in registers.
+#include "vq_internal.h"
+
+namespace vq {
+namespace {
+
+constexpr int kThreads = 256;  // 4 waves of 64
+
+template <int DS>
+__device__ __forceinline__ void load_f16(const __half* __restrict__ p, float (&x)[DS]) {
+  if constexpr (DS == 1) {
+    x[0] = __half2float(p[0]);
+  } else if constexpr (DS == 2) {
+    float2 f = __half22float2(*reinterpret_cast<const __half2*>(p));
+    x[0] = f.x; x[1] = f.y;
+  } else if constexpr (DS == 4) {
+    uint2 u = *reinterpret_cast<const uint2*>(p);
+    float2 f0 = __half22float2(*reinterpret_cast<const __half2*>(&u.x));
+    float2 f1 = __half22float2(*reinterpret_cast<const __half2*>(&u.y));
+    x[0] = f0.x; x[1] = f0.y; x[2] = f1.x; x[3] = f1.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < DS; i += 8) {
+      uint4 u = *reinterpret_cast<const uint4*>(p + i);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float2 f = __half22float2(*reinterpret_cast<const __half2*>(&w[k]));
+        x[i + 2 * k] = f.x; x[i + 2 * k + 1] = f.y;
+      }
+    }
+  }
+}
+
+template <int DS>
+__device__ __forceinline__ void store_f16(__half* __restrict__ p, const float (&x)[DS]) {
+  if constexpr (DS == 1) {
+    p[0] = __float2half_rn(x[0]);
+  } else if constexpr (DS == 2) {
+    *reinterpret_cast<__half2*>(p) = __floats2half2_rn(x[0], x[1]);
+  } else if constexpr (DS == 4) {
+    __half2 a = __floats2half2_rn(x[0], x[1]), b = __floats2half2_rn(x[2], x[3]);
+    uint2 u;
+    u.x = *reinterpret_cast<uint32_t*>(&a);
+    u.y = *reinterpret_cast<uint32_t*>(&b);
+    *reinterpret_cast<uint2*>(p) = u;
+  } else {
+#pragma unroll
+    for (int i = 0; i < DS; i += 8) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        __half2 h = __floats2half2_rn(x[i + 2 * k], x[i + 2 * k + 1]);
+        w[k] = *reinterpret_cast<uint32_t*>(&h);
+      }
+      *reinterpret_cast<uint4*>(p + i) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int DS>
+__device__ __forceinline__ void store_f32(float* __restrict__ p, const float (&x)[DS]) {
+  if constexpr (DS == 1) {
+    p[0] = x[0];
+  } else if constexpr (DS == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < DS; i += 4)
+      *reinterpret_cast<float4*>(p + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+  }
+}
+
+// Unnormalized Walsh-Hadamard butterflies over the index bits held inside the
+// lane (element e of sub-vector j is index j * DS + e).
+template <int DS>
+__device__ __forceinline__ void wht_in_lane(float (&x)[DS]) {
+#pragma unroll
+  for (int h = 1; h < DS; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < DS; ++i) {
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// Butterflies over the index bits that select the lane (sub-vector j): the
+// partner of lane j for bit m is lane j ^ m in the same token-head group.
+template <int NSUB, int DS>
+__device__ __forceinline__ void wht_cross_lane(float (&x)[DS], int j) {
+#pragma unroll
+  for (int m = 1; m < NSUB; m <<= 1) {
+    const bool upper = (j & m) != 0;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) {
+      const float y = __shfl_xor(x[e], m);
+      x[e] = upper ? (y - x[e]) : (x[e] + y);
+    }
+  }
+}
+
+template <int D, int DS>
+__device__ __forceinline__ void wht(float (&x)[DS], int j) {
+  wht_in_lane<DS>(x);
+  wht_cross_lane<D / DS, DS>(x, j);
+  const float nrm = WhtNorm<D>::value;
+#pragma unroll
+  for (int e = 0; e < DS; ++e) x[e] *= nrm;
+}
+
+struct Dims {
+  int B, H, S, n_c, smooth_rows, transform, S_cap, S_off, use_row_offsets, recon_dtype;
+};
+
+// MODE 0: encode; 1: encode + reconstruct; 2: decode (codes_in -> recon).
+template <int D, int DS, int MODE>
+__global__ __launch_bounds__(kThreads) void pvq_kernel(
+    const __half* __restrict__ keys, const uint8_t* __restrict__ codes_in,
+    const float* __restrict__ cb, const float* __restrict__ smooth,
+    uint8_t* __restrict__ codes, void* __restrict__ recon, Dims d, RowOffsets offs) {
+  constexpr int NSUB = D / DS;   // lanes per token-head (<= 64)
+  constexpr int TPW = 64 / NSUB; // token-heads per wave
+  constexpr int TPB = (kThreads / 64) * TPW;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane % NSUB;
+  const long long n_th = (long long)d.B * d.H * d.S;
+  const long long th = (long long)blockIdx.x * TPB + wave * TPW + lane / NSUB;
+  const bool valid = th < n_th;
+  const long long thc = valid ? th : 0;
+  const int t = (int)(thc % d.S);
+  const long long bh = thc / d.S;
+  const int h = (int)(bh % d.H);
+  const int b = (int)(bh / d.H);
+  const float* srow = smooth ? smooth + (long long)(d.smooth_rows == 1 ? 0 : h) * D + j * DS : nullptr;
+
+  float x[DS];
+  int idx = 0;
+  if constexpr (MODE != 2) {
+    if (valid) {
+      load_f16<DS>(keys + thc * D + j * DS, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < DS; ++e) x[e] = 0.f;
+    }
+    if (srow) {
+#pragma unroll
+      for (int e = 0; e < DS; ++e) x[e] = x[e] / srow[e];
+    }
+    if (d.transform) wht<D, DS>(x, j);
+
+    // Nearest centroid: fp32 squared distance summed over e in order,
+    // strict '<' keeps the lowest index on exact ties.
+    float best = INFINITY;
+    for (int c = 0; c < d.n_c; ++c) {
+      const float* cc = cb + c * DS;
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) {
+        const float df = x[e] - cc[e];
+        acc = fmaf(df, df, acc);
+      }
+      if (acc < best) { best = acc; idx = c; }
+    }
+    if (valid) {
+      const int off = d.use_row_offsets ? offs.v[b] : d.S_off;
+      codes[(bh * d.S_cap + off + t) * NSUB + j] = (uint8_t)idx;
+    }
+  } else {
+    if (valid) idx = min((int)codes_in[(bh * d.S_cap + d.S_off + t) * NSUB + j], d.n_c - 1);
+  }
+
+  if constexpr (MODE != 0) {
+    const float* cc = cb + idx * DS;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) x[e] = cc[e];
+    if (d.transform) wht<D, DS>(x, j);  // H is its own inverse
+    if (srow) {
+#pragma unroll
+      for (int e = 0; e < DS; ++e) x[e] = x[e] * srow[e];
+    }
+    if (valid) {
+      if (d.recon_dtype == 1)
+        store_f16<DS>(reinterpret_cast<__half*>(recon) + thc * D + j * DS, x);
+      else
+        store_f32<DS>(reinterpret_cast<float*>(recon) + thc * D + j * DS, x);
+    }
+  }
+}
+
+template <int D, int DS>
+hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipStream_t st) {
+  constexpr int NSUB = D / DS;
+  constexpr int TPB = (kThreads / 64) * (64 / NSUB);
+  const long long n_th = (long long)a.B * a.H * a.S;
+  const long long blocks = (n_th + TPB - 1) / TPB;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  Dims d{a.B, a.H, a.S, a.n_c, a.smooth_rows, a.transform, a.S_cap, a.S_off,
+         a.use_row_offsets, a.recon_dtype};
+  RowOffsets o{};
+  if (offs) o = *offs;
+  dim3 grid((unsigned)blocks), block(kThreads);
+  switch (mode) {
+    case 0:
+      hipLaunchKernelGGL((pvq_kernel<D, DS, 0>), grid, block, 0, st, a.keys, a.codes_in,
+                         a.codebook, a.smooth, a.codes, a.recon, d, o);
+      break;
+    case 1:
+      hipLaunchKernelGGL((pvq_kernel<D, DS, 1>), grid, block, 0, st, a.keys, a.codes_in,
+                         a.codebook, a.smooth, a.codes, a.recon, d, o);
+      break;
+    default:
+      hipLaunchKernelGGL((pvq_kernel<D, DS, 2>), grid, block, 0, st, a.keys, a.codes_in,
+                         a.codebook, a.smooth, a.codes, a.recon, d, o);
+      break;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const EncodeArgs& a, const RowOffsets* offs, int mode, hipStream_t st) {
+  switch (a.sub_dim) {
+    case 1: if constexpr (D / 1 <= 64) return launch_ds<D, 1>(a, offs, mode, st); break;
+    case 2: if constexpr (D / 2 <= 64) return launch_ds<D, 2>(a, offs, mode, st); break;
+    case 4: return launch_ds<D, 4>(a, offs, mode, st);
+    case 8: return launch_ds<D, 8>(a, offs, mode, st);
+    case 16: return launch_ds<D, 16>(a, offs, mode, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_encode(const EncodeArgs& a, const RowOffsets* offs, int mode, hipStream_t st) {
+  switch (a.D) {
+    case 32: return launch_d<32>(a, offs, mode, st);
+    case 64: return launch_d<64>(a, offs, mode, st);
+    case 128: return launch_d<128>(a, offs, mode, st);
+    case 256: return launch_d<256>(a, offs, mode, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace vq

@@ -1,0 +1,73 @@
+// Internal declarations shared by the HIP translation units of libvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/vq.h"
+
+namespace vq {
+
+// Records a failure message for vq_last_error() and returns `status`.
+int fail(int status, const char* fmt, ...);
+
+// 1/sqrt(D) for the supported power-of-two head dims, rounded to fp32.
+template <int D> struct WhtNorm;
+template <> struct WhtNorm<32>  { static constexpr float value = 0.17677669529663688f; };
+template <> struct WhtNorm<64>  { static constexpr float value = 0.125f; };
+template <> struct WhtNorm<128> { static constexpr float value = 0.08838834764831845f; };
+template <> struct WhtNorm<256> { static constexpr float value = 0.0625f; };
+
+// Per-row write offsets passed by value in the kernel arguments.
+struct RowOffsets { int32_t v[VQ_MAX_ROW_OFFSETS]; };
+
+struct EncodeArgs {
+  const __half* keys;      // [B, H, S, D]
+  const uint8_t* codes_in; // decode: [B, H, S_cap, n_sub]
+  const float* codebook;   // [n_c, sub_dim]
+  const float* smooth;     // NULL or [smooth_rows, D]
+  uint8_t* codes;          // encode: [B, H, S_cap, n_sub]
+  void* recon;             // NULL or [B, H, S, D]
+  int B, H, S, D, n_c, sub_dim, smooth_rows, transform;
+  int S_cap, S_off, use_row_offsets, recon_dtype;  // recon_dtype 0 fp32, 1 fp16
+};
+
+// mode 0 = encode, 1 = encode + reconstruct, 2 = decode only.
+hipError_t launch_encode(const EncodeArgs& a, const RowOffsets* offs, int mode, hipStream_t st);
+
+struct AttendArgs {
+  const __half* q;          // [B, H_q, S_q, D]
+  const uint8_t* k_codes;   // [B, H_kv, S_cap, n_sub_k]
+  const float* k_codebook;  // [n_c, dk]
+  const float* smooth;      // NULL or [smooth_rows, D]
+  const uint8_t* v_codes;   // [B, H_kv, S_cap, n_sub_v]
+  const float* v_codebook;  // [n_c, dv]
+  const int32_t* kv_lens;   // NULL or [B]
+  __half* out;              // [B, H_q, S_q, D]
+  float* partials;          // workspace
+  int B, Hq, Sq, D, Hkv, S_cap, dk, dv, n_c, smooth_rows, transform;
+  float scale_log2e;
+  int causal, window;
+};
+
+struct AttendPlan {
+  int G;            // query heads per kv head
+  int rows;         // G * S_q query rows per kv head
+  int R;            // rows handled by one workgroup (1, 2, 4 or 8)
+  int n_rgroups;    // ceil(rows / R)
+  int split_tokens; // keys per split
+  int n_split;      // splits per (b, kv head, row group)
+  size_t workspace_bytes;
+};
+
+// Pure function of the shape: split count, row grouping, workspace size.
+bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, AttendPlan* p);
+
+// Rows per workgroup (1, 2, 4 or 8) whose LDS footprint fits; 0 if none does.
+int attend_pick_rows(int rows, int nsk, int n_c, int dv, int nsv, int D, size_t* lds_bytes);
+
+hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t st);
+
+}  // namespace vq
