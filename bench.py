@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--mode", choices=["full", "attend", "encode"], default="full",
+                    help="attend/encode: only launch that kernel of the main workload "
+                         "--steps times (for profiler runs); prints no JSON line")
     return ap.parse_args()
 
 
@@ -124,6 +127,17 @@ def main():
     def step(i):
         ek, ev, at = steps[i % n_sets]
         ek(); ev(); at()
+
+    if args.mode != "full":
+        for i in range(args.warmup + args.steps):
+            if args.mode == "attend":
+                steps[i % n_sets][2]()
+            else:
+                steps[i % n_sets][0]()
+                steps[i % n_sets][1]()
+        torch.cuda.synchronize()
+        log(f"[bench] mode={args.mode}: {args.warmup + args.steps} launches done")
+        return
 
     for i in range(args.warmup):
         step(i)

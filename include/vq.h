@@ -25,6 +25,9 @@
  *   - transform = 1 applies the normalized Sylvester Walsh-Hadamard matrix
  *     H[i][k] = (-1)^popcount(i & k) / sqrt(D) (symmetric, its own inverse);
  *     transform = 0 applies none (the value path).
+ *   - Device pointers must be 16-byte aligned (the kernels use 16-byte
+ *     vector accesses); a misaligned pointer is rejected as an invalid
+ *     argument.
  *   - Every call is enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and returns without synchronizing.  The caller owns every
  *     buffer; the library allocates no device memory and keeps no state
@@ -169,10 +172,9 @@ size_t vq_attend_workspace_bytes(int B, int H_q, int S_q, int D, int H_kv,
  *   kv_lens     NULL (every row holds S_cap keys) or DEVICE int32 [B];
  *               values are clamped to [0, S_cap]
  *   out_f16     [B, H_q, S_q, D] fp16
- *   workspace   DEVICE buffer of >= vq_attend_workspace_bytes(...) bytes,
- *               zero-filled before its first use; every call leaves it
- *               ready for the next.  Calls that may run concurrently need
- *               distinct workspaces.
+ *   workspace   DEVICE buffer of >= vq_attend_workspace_bytes(...) bytes
+ *               for the split partials; its contents on entry are ignored.
+ *               Calls that may run concurrently need distinct workspaces.
  * Errors: INVALID_ARGUMENT for null pointers, nonpositive sizes,
  * H_q % H_kv != 0, D % sub_dim != 0, smooth_rows not in {1, H_kv},
  * sliding_window < 0; UNSUPPORTED outside the caps; WORKSPACE when the

@@ -15,7 +15,7 @@ from vector_quantized_kv_amd.build import build_library
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vq.h")
 OK, INVALID, UNSUPPORTED, NO_DEVICE, HIPERR, WORKSPACE = range(6)
-P = ctypes.c_void_p(0x10000)          # a non-null pointer that is never dereferenced
+P = ctypes.c_void_p(0x10000)          # a non-null, aligned pointer that is never dereferenced
 
 
 @pytest.fixture(scope="module")
@@ -139,6 +139,7 @@ def test_workspace_bytes(lib):
     a = f(16, 32, 1, 128, 8, 32768, 0)
     b = f(16, 32, 1, 128, 8, 32768, 4096)
     assert a > 0 and b > 0
+    # (D + 2) floats per split partial, rows rounded up to 8
     # (D + 2) floats per split partial, rows rounded up to 8
     assert a % ((128 + 2) * 4 * 16 * 8 * 8) == 0
 

@@ -4,6 +4,7 @@
 #include "vq_internal.h"
 
 #include <atomic>
+#include <initializer_list>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -63,6 +64,14 @@ int check_transform(const char* what, int transform, int D) {
   return VQ_OK;
 }
 
+// Device buffers are read and written with 16-byte vector accesses.
+int check_aligned(const char* what, std::initializer_list<const void*> ptrs) {
+  for (const void* ptr : ptrs)
+    if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0)
+      return fail(VQ_ERR_INVALID_ARGUMENT, "%s: device pointers must be 16-byte aligned", what);
+  return VQ_OK;
+}
+
 int check_device(const char* what) {
   if (device_count() <= 0) return fail(VQ_ERR_NO_DEVICE, "%s: no HIP device is visible", what);
   return VQ_OK;
@@ -86,6 +95,7 @@ int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
   if (st) return st;
   if ((st = check_smooth(what, smooth, smooth_rows, H))) return st;
   if ((st = check_transform(what, transform, D))) return st;
+  if ((st = check_aligned(what, {keys, codebook, smooth}))) return st;
   if (S_cap <= 0) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: S_cap must be positive (got %d)", what, S_cap);
   if (row_offsets) {
     if (B > VQ_MAX_ROW_OFFSETS)
@@ -189,6 +199,7 @@ int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D, const flo
                         smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets);
   if (st) return st;
   if (!recon) return fail(VQ_ERR_INVALID_ARGUMENT, "vq_encode_decode: recon must be non-null");
+  if ((st = check_aligned("vq_encode_decode", {recon}))) return st;
   if (out_dtype != 0 && out_dtype != 1)
     return fail(VQ_ERR_INVALID_ARGUMENT, "vq_encode_decode: out_dtype must be 0 (fp32) or 1 (fp16)");
   return run_encode("vq_encode_decode", keys_f16, nullptr, B, H, S, D, codebook, n_centroids,
@@ -211,6 +222,7 @@ int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
   if ((st = check_transform(what, transform, D))) return st;
   if (out_dtype != 0 && out_dtype != 1)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: out_dtype must be 0 (fp32) or 1 (fp16)", what);
+  if ((st = check_aligned(what, {codebook, smooth, out}))) return st;
   if (S_cap <= 0 || S_off < 0 || (long long)S_off + S > S_cap)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: slots [%d, %lld) fall outside [0, %d)", what, S_off,
                 (long long)S_off + S, S_cap);
@@ -255,6 +267,9 @@ int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* 
   if (sliding_window < 0)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: sliding_window must be >= 0 (got %d)", what, sliding_window);
   if (!std::isfinite(scale)) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: scale must be finite", what);
+  if ((st = check_aligned(what, {q_f16, k_codes, k_codebook, smooth, v_codes, v_codebook, kv_lens,
+                                 out_f16, workspace})))
+    return st;
   if (B == 0 || S_q == 0) return VQ_OK;
   AttendPlan plan;
   if (!plan_attend(B, H_q, S_q, D, H_kv, S_cap, sliding_window, &plan))

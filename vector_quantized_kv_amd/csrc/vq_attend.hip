@@ -27,13 +27,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr size_t kLdsBudget = 160 * 1024;
 
-struct AttParams {
-  int B, Hq, Sq, Hkv, S_cap, dk, dv, n_c, nsk, nsv, smooth_rows, transform;
-  float fold;  // WHT normalization (if any) * scale * log2(e)
-  int causal, window;
-  int G, rows, R, n_rgroups, split_tokens, n_split;
-};
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -352,9 +345,7 @@ hipError_t launch_dr(const AttendArgs& a, const AttParams& p, size_t lds_bytes, 
                      a.smooth, a.v_codes, a.v_codebook, a.kv_lens, a.partials, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attend_merge_kernel<D>), dim3(a.B * a.Hq * a.Sq), dim3(D), 0, st,
-                     a.partials, a.out, p);
-  return hipGetLastError();
+  return launch_attend_merge(a, p, st);
 }
 
 template <int D>
@@ -369,6 +360,18 @@ hipError_t launch_d(const AttendArgs& a, const AttParams& p, size_t lds_bytes, h
 }
 
 }  // namespace
+
+hipError_t launch_attend_merge(const AttendArgs& a, const AttParams& p, hipStream_t st) {
+  const dim3 grid(a.B * a.Hq * a.Sq);
+  switch (a.D) {
+    case 32: hipLaunchKernelGGL((attend_merge_kernel<32>), grid, dim3(32), 0, st, a.partials, a.out, p); break;
+    case 64: hipLaunchKernelGGL((attend_merge_kernel<64>), grid, dim3(64), 0, st, a.partials, a.out, p); break;
+    case 128: hipLaunchKernelGGL((attend_merge_kernel<128>), grid, dim3(128), 0, st, a.partials, a.out, p); break;
+    case 256: hipLaunchKernelGGL((attend_merge_kernel<256>), grid, dim3(256), 0, st, a.partials, a.out, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, AttendPlan* pl) {
   if (B <= 0 || Hq <= 0 || Sq <= 0 || D <= 0 || Hkv <= 0 || S_cap <= 0 || window < 0) return false;
@@ -419,7 +422,8 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_
   p.causal = a.causal; p.window = a.window;
   p.G = plan.G; p.rows = plan.rows; p.split_tokens = plan.split_tokens; p.n_split = plan.n_split;
   size_t lds = 0;
-  p.R = attend_pick_rows(p.rows, p.nsk, p.n_c, p.dv, p.nsv, a.D, &lds);
+  const bool mfma = attend_mfma_plan(a.D, a.dv, p.nsk, p.rows, &p.R, &lds);
+  if (!mfma) p.R = attend_pick_rows(p.rows, p.nsk, p.n_c, p.dv, p.nsv, a.D, &lds);
   if (p.R == 0) return hipErrorInvalidValue;
   p.n_rgroups = (p.rows + p.R - 1) / p.R;
   if (p.n_rgroups > 65535 || p.n_split > 65535) return hipErrorInvalidValue;
@@ -433,6 +437,7 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_
     }
   }
   p.fold = norm * a.scale_log2e;
+  if (mfma) return launch_attend_mfma(a, p, lds, st);
   switch (a.D) {
     case 32: return launch_d<32>(a, p, lds, st);
     case 64: return launch_d<64>(a, p, lds, st);

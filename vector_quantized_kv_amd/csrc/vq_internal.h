@@ -46,7 +46,7 @@ struct AttendArgs {
   const float* v_codebook;  // [n_c, dv]
   const int32_t* kv_lens;   // NULL or [B]
   __half* out;              // [B, H_q, S_q, D]
-  float* partials;          // workspace
+  float* partials;          // workspace: split partials
   int B, Hq, Sq, D, Hkv, S_cap, dk, dv, n_c, smooth_rows, transform;
   float scale_log2e;
   int causal, window;
@@ -59,8 +59,25 @@ struct AttendPlan {
   int n_rgroups;    // ceil(rows / R)
   int split_tokens; // keys per split
   int n_split;      // splits per (b, kv head, row group)
-  size_t workspace_bytes;
+  size_t workspace_bytes; // split partials
 };
+
+// Kernel-side parameters of one attention launch (by value).
+struct AttParams {
+  int B, Hq, Sq, Hkv, S_cap, dk, dv, n_c, nsk, nsv, smooth_rows, transform;
+  float fold;  // WHT normalization (if any) * scale * log2(e)
+  int causal, window;
+  int G, rows, R, n_rgroups, split_tokens, n_split;
+};
+
+// Split merge (log-sum-exp) of the partials into the fp16 output.
+hipError_t launch_attend_merge(const AttendArgs& a, const AttParams& p, hipStream_t st);
+
+// MFMA value-path kernel: rows per workgroup and LDS bytes if the shape fits
+// (D in {64, 128}, value sub_dim 4, 8/16/32 key sub-vectors), else false.
+bool attend_mfma_plan(int D, int dv, int nsk, int rows, int* R, size_t* lds_bytes);
+hipError_t launch_attend_mfma(const AttendArgs& a, const AttParams& p, size_t lds_bytes,
+                              hipStream_t st);
 
 // Pure function of the shape: split count, row grouping, workspace size.
 bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, AttendPlan* p);
