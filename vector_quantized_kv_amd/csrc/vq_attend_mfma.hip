@@ -112,6 +112,25 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Byte rotation of the lane's NSK code bytes by 4 * rot_dw + rot_b:
+// out byte k = in byte (k + 4 rot_dw + rot_b) mod NSK.
+template <int NSK>
+__device__ __forceinline__ void rotate_codes(const KeyCodes<NSK>& in, int rot_dw, int rot_b,
+                                             uint32_t (&out)[NSK / 4]) {
+  constexpr int NWD = NSK / 4;
+  uint32_t dw[NWD];
+#pragma unroll
+  for (int d = 0; d < NWD; ++d) {
+    uint32_t v = in.w[d];
+#pragma unroll
+    for (int s = 1; s < (NWD < 4 ? NWD : 4); ++s) v = (rot_dw == s) ? in.w[(d + s) % NWD] : v;
+    dw[d] = v;
+  }
+#pragma unroll
+  for (int d = 0; d < NWD; ++d)
+    out[d] = __builtin_amdgcn_alignbyte(dw[(d + 1) % NWD], dw[d], (uint32_t)rot_b);
+}
+
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -208,29 +227,33 @@ __device__ __forceinline__ void split_body(
   }
   __syncthreads();
 
-  // ---- query LUT [j][256][R]: thread = (centroid c, half of the j range) -
+  // ---- query LUT, layout [code][j][R] -----------------------------------
+  // Entry (j, code) lives at ((code * NSK + j) * R) floats: its LDS bank
+  // group depends on j only, so a pass of lanes that reads distinct j's is
+  // conflict-free whatever the codes (see the rotated read order below).
+  // Build: thread = (j, centroid c); its query slice stays in registers.
   {
-    const int c = tid & 255;
-    const int j0 = (tid >> 8) * (NSK / 2);
-    float ck[DK];
-    if (c < p.n_c) {
+    constexpr int CPI = kThreads / NSK;   // centroids per iteration
+    const int j = tid % NSK;
+    float qs[R][DK];
 #pragma unroll
-      for (int e = 0; e < DK; ++e) ck[e] = kcb[(size_t)c * DK + e];
-    } else {
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int e = 0; e < DK; ++e) ck[e] = 0.f;
-    }
-#pragma unroll 2
-    for (int j = j0; j < j0 + NSK / 2; ++j) {
+      for (int e = 0; e < DK; ++e) qs[r][e] = qt[r * D + j * DK + e];
+    for (int c = tid / NSK; c < 256; c += CPI) {
       float acc[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float a = 0.f;
+      for (int r = 0; r < R; ++r) acc[r] = 0.f;
+      if (c < p.n_c) {
+        const float* crow = kcb + (size_t)c * DK;
 #pragma unroll
-        for (int e = 0; e < DK; ++e) a = fmaf(qt[r * D + j * DK + e], ck[e], a);
-        acc[r] = a;
+        for (int e = 0; e < DK; ++e) {
+          const float ce = crow[e];
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r] = fmaf(qs[r][e], ce, acc[r]);
+        }
       }
-      float* dst = lut + ((size_t)j * 256 + c) * R;
+      float* dst = lut + ((size_t)c * NSK + j) * R;
       if constexpr (R == 4) {
         *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
       } else if constexpr (R == 2) {
@@ -260,6 +283,15 @@ __device__ __forceinline__ void split_body(
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[w][e] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+  // rotated visiting order of the key sub-vectors: lane rotation rot, byte
+  // offsets of each visited j inside a LUT row
+  constexpr int NROT = NSK < 16 ? NSK : 16;
+  const int rot = lane & (NROT - 1);
+  const int rot_dw = rot >> 2, rot_b = rot & 3;
+  uint32_t jterm[NSK];
+#pragma unroll
+  for (int k = 0; k < NSK; ++k) jterm[k] = (uint32_t)(((k + rot) % NSK) * R * 4);
+
   const int n_blk = (s_hi - s_lo + 63) / 64;
   KeyCodes<NSK> kr, krn;
   uint32_t vr[4][NW];
@@ -288,8 +320,11 @@ __device__ __forceinline__ void split_body(
     const bool more = blk + kWaves < n_blk;
     if (more) load_keys(blk + kWaves, krn);
 
-    // scores: sum of LUT entries over the key sub-vectors
+    // scores: sum of LUT entries over the key sub-vectors, visited in the
+    // lane's rotated order j = (k + rot) mod NSK (rotated code bytes)
     const int t = s_lo + blk * 64 + lane;
+    uint32_t rc[NSK / 4];
+    rotate_codes<NSK>(kr, rot_dw, rot_b, rc);
     float sc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) sc[r] = 0.f;
@@ -297,9 +332,11 @@ __device__ __forceinline__ void split_body(
     for (int jw = 0; jw < NSK / 4; ++jw) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int code = (kr.w[jw] >> (8 * k)) & 0xff;
+        const uint32_t code = (rc[jw] >> (8 * k)) & 0xff;
         float v[R];
-        lds_row<R>(lut + ((size_t)(jw * 4 + k) * 256 + code) * R, v);
+        lds_row<R>(reinterpret_cast<const float*>(
+                       reinterpret_cast<const unsigned char*>(lut) +
+                       (code * (uint32_t)(NSK * R * 4) + jterm[jw * 4 + k])), v);
 #pragma unroll
         for (int r = 0; r < R; ++r) sc[r] += v[r];
       }

@@ -132,19 +132,23 @@ struct Dims {
 };
 
 // MODE 0: encode; 1: encode + reconstruct; 2: decode (codes_in -> recon).
-template <int D, int DS, int MODE>
+// CSPLIT waves share one group of token-heads and split the codebook between
+// them (used when there are too few token-heads to fill the chip); their
+// partial argmins are combined through LDS, lowest index first on ties.
+template <int D, int DS, int MODE, int CSPLIT>
 __global__ __launch_bounds__(kThreads) void pvq_kernel(
     const __half* __restrict__ keys, const uint8_t* __restrict__ codes_in,
     const float* __restrict__ cb, const float* __restrict__ smooth,
     uint8_t* __restrict__ codes, void* __restrict__ recon, Dims d, RowOffsets offs) {
   constexpr int NSUB = D / DS;   // lanes per token-head (<= 64)
   constexpr int TPW = 64 / NSUB; // token-heads per wave
-  constexpr int TPB = (kThreads / 64) * TPW;
+  constexpr int TPB = (kThreads / 64 / CSPLIT) * TPW;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave / CSPLIT, part = wave % CSPLIT;
   const int j = lane % NSUB;
   const long long n_th = (long long)d.B * d.H * d.S;
-  const long long th = (long long)blockIdx.x * TPB + wave * TPW + lane / NSUB;
+  const long long th = (long long)blockIdx.x * TPB + grp * TPW + lane / NSUB;
   const bool valid = th < n_th;
   const long long thc = valid ? th : 0;
   const int t = (int)(thc % d.S);
@@ -169,9 +173,13 @@ __global__ __launch_bounds__(kThreads) void pvq_kernel(
     if (d.transform) wht<D, DS>(x, j);
 
     // Nearest centroid: fp32 squared distance summed over e in order,
-    // strict '<' keeps the lowest index on exact ties.
+    // strict '<' keeps the lowest index on exact ties.  The centroid index is
+    // wave-uniform, so each centroid is one scalar load shared by all lanes.
+    const int c_lo = d.n_c * part / CSPLIT, c_hi = d.n_c * (part + 1) / CSPLIT;
     float best = INFINITY;
-    for (int c = 0; c < d.n_c; ++c) {
+    idx = c_lo;
+#pragma unroll 8
+    for (int c = c_lo; c < c_hi; ++c) {
       const float* cc = cb + c * DS;
       float acc = 0.f;
 #pragma unroll
@@ -180,6 +188,20 @@ __global__ __launch_bounds__(kThreads) void pvq_kernel(
         acc = fmaf(df, df, acc);
       }
       if (acc < best) { best = acc; idx = c; }
+    }
+    if constexpr (CSPLIT > 1) {
+      __shared__ float s_best[kThreads];
+      __shared__ int s_idx[kThreads];
+      s_best[threadIdx.x] = best;
+      s_idx[threadIdx.x] = idx;
+      __syncthreads();
+      if (part != 0) return;  // the first wave of the group finishes the token-heads
+      // later parts hold higher indices: only a strictly smaller distance wins
+#pragma unroll
+      for (int k = 1; k < CSPLIT; ++k) {
+        const int o = threadIdx.x + k * 64;
+        if (s_best[o] < best) { best = s_best[o]; idx = s_idx[o]; }
+      }
     }
     if (valid) {
       const int off = d.use_row_offsets ? offs.v[b] : d.S_off;
@@ -207,30 +229,38 @@ __global__ __launch_bounds__(kThreads) void pvq_kernel(
   }
 }
 
+template <int D, int DS, int MODE, int CSPLIT>
+void launch_one(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStream_t st) {
+  constexpr int NSUB = D / DS;
+  constexpr int TPB = (kThreads / 64 / CSPLIT) * (64 / NSUB);
+  const long long n_th = (long long)a.B * a.H * a.S;
+  const unsigned blocks = (unsigned)((n_th + TPB - 1) / TPB);
+  hipLaunchKernelGGL((pvq_kernel<D, DS, MODE, CSPLIT>), dim3(blocks), dim3(kThreads), 0, st,
+                     a.keys, a.codes_in, a.codebook, a.smooth, a.codes, a.recon, d, o);
+}
+
 template <int D, int DS>
 hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipStream_t st) {
   constexpr int NSUB = D / DS;
-  constexpr int TPB = (kThreads / 64) * (64 / NSUB);
   const long long n_th = (long long)a.B * a.H * a.S;
-  const long long blocks = (n_th + TPB - 1) / TPB;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if ((n_th + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidValue;
   Dims d{a.B, a.H, a.S, a.n_c, a.smooth_rows, a.transform, a.S_cap, a.S_off,
          a.use_row_offsets, a.recon_dtype};
   RowOffsets o{};
   if (offs) o = *offs;
-  dim3 grid((unsigned)blocks), block(kThreads);
+  // Fewer lanes than about four waves per CU (256 CUs): split the codebook
+  // over the four waves of a workgroup instead of giving each its own
+  // token-heads, so short appends (one token per row) are not latency bound.
+  const bool split = n_th * NSUB < 256LL * 64 * 4;
   switch (mode) {
     case 0:
-      hipLaunchKernelGGL((pvq_kernel<D, DS, 0>), grid, block, 0, st, a.keys, a.codes_in,
-                         a.codebook, a.smooth, a.codes, a.recon, d, o);
+      if (split) launch_one<D, DS, 0, 4>(a, d, o, st); else launch_one<D, DS, 0, 1>(a, d, o, st);
       break;
     case 1:
-      hipLaunchKernelGGL((pvq_kernel<D, DS, 1>), grid, block, 0, st, a.keys, a.codes_in,
-                         a.codebook, a.smooth, a.codes, a.recon, d, o);
+      if (split) launch_one<D, DS, 1, 4>(a, d, o, st); else launch_one<D, DS, 1, 1>(a, d, o, st);
       break;
     default:
-      hipLaunchKernelGGL((pvq_kernel<D, DS, 2>), grid, block, 0, st, a.keys, a.codes_in,
-                         a.codebook, a.smooth, a.codes, a.recon, d, o);
+      launch_one<D, DS, 2, 1>(a, d, o, st);
       break;
   }
   return hipGetLastError();
