@@ -139,9 +139,13 @@ def test_workspace_bytes(lib):
     a = f(16, 32, 1, 128, 8, 32768, 0)
     b = f(16, 32, 1, 128, 8, 32768, 4096)
     assert a > 0 and b > 0
-    # (D + 2) floats per split partial, rows rounded up to 8
-    # (D + 2) floats per split partial, rows rounded up to 8
-    assert a % ((128 + 2) * 4 * 16 * 8 * 8) == 0
+    # head dim 128 may run on the persistent kernel: one partial of 4 rows x
+    # (128 + 2) floats per (chunk, unit) pair, 4096 chunks + 128 units here
+    assert a >= (4096 + 16 * 8) * 4 * (128 + 2) * 4
+    assert a == f(16, 32, 1, 128, 8, 32768, 0)            # a pure function of the shape
+    # other head dims: (D + 2) floats per split partial, rows rounded up to 8
+    c = f(16, 32, 1, 64, 8, 32768, 0)
+    assert c > 0 and c % ((64 + 2) * 4 * 16 * 8 * 8) == 0
 
 
 def test_binding_rejects_host_tensors(lib):

@@ -392,6 +392,9 @@ bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, A
   pl->n_split = (int)std::max<long long>(1, (max_range + T - 1) / T);
   const long long rows8 = (pl->rows + 7) / 8 * 8;
   pl->workspace_bytes = (size_t)B * Hkv * rows8 * pl->n_split * (D + 2) * sizeof(float);
+  // the streaming kernel (chosen by the code sizes, which this call does not
+  // see) may need more
+  pl->workspace_bytes = std::max(pl->workspace_bytes, stream_workspace_bytes(B, Hq, Sq, D, Hkv));
   pl->R = 0;
   pl->n_rgroups = 0;
   return true;
@@ -415,6 +418,12 @@ int attend_pick_rows(int rows, int nsk, int n_c, int dv, int nsv, int D, size_t*
 }
 
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_t st) {
+  {
+    StreamParams sp;
+    size_t lds = 0;
+    if (stream_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.dk, a.dv, a.n_c, &sp, &lds, nullptr))
+      return launch_attend_stream(a, sp, lds, st);
+  }
   AttParams p;
   p.B = a.B; p.Hq = a.Hq; p.Sq = a.Sq; p.Hkv = a.Hkv; p.S_cap = a.S_cap;
   p.dk = a.dk; p.dv = a.dv; p.n_c = a.n_c; p.nsk = a.D / a.dk; p.nsv = a.D / a.dv;

@@ -79,6 +79,21 @@ bool attend_mfma_plan(int D, int dv, int nsk, int rows, int* R, size_t* lds_byte
 hipError_t launch_attend_mfma(const AttendArgs& a, const AttParams& p, size_t lds_bytes,
                               hipStream_t st);
 
+// Persistent streaming kernel (head dim 128, key sub_dim 8, value sub_dim 4).
+struct StreamParams {
+  int B, Hq, Sq, Hkv, S_cap, n_c, smooth_rows, transform, causal, window;
+  int G, GS, n_rg, U, cmin;
+  float fold;  // WHT normalization (if any) * scale * log2(e)
+};
+// True if the shape runs on the streaming kernel; fills its parameters, LDS
+// bytes and workspace bytes.
+bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int dk, int dv, int n_c,
+                 StreamParams* sp, size_t* lds_bytes, size_t* ws_bytes);
+// Workspace of the streaming kernel for this shape (0 if D is not 128).
+size_t stream_workspace_bytes(int B, int Hq, int Sq, int D, int Hkv);
+hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds_bytes,
+                                hipStream_t st);
+
 // Pure function of the shape: split count, row grouping, workspace size.
 bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, AttendPlan* p);
 
