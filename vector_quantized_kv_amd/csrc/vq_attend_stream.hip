@@ -52,7 +52,7 @@
 namespace vq {
 namespace {
 
-constexpr int kW = 16;                 // waves per workgroup
+constexpr int kW = 8;                  // waves per workgroup (2 per SIMD)
 constexpr int kThreads = kW * 64;
 constexpr int kD = 128;
 constexpr int kRows = 4;               // query rows per unit
@@ -65,7 +65,9 @@ constexpr uint32_t kPWave = kRows * kPRow;
 constexpr uint32_t kScan = kPStage + kW * kPWave;
 constexpr uint32_t kPrefix = kScan + 64;  // int prefix[U + 1]
 constexpr float kLazyMargin = 8.f;
-constexpr int kMaxWaves = 256 * kW;    // partial slots reserved for chunks
+constexpr int kMaxUnits = 4095;        // units whose prefix fits in LDS
+constexpr int kUnitsPerThread = (kMaxUnits + kThreads) / kThreads;
+constexpr int kMaxWaves = 256 * 16;    // partial slots reserved for chunks (>= 256 CUs * kW)
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -110,24 +112,23 @@ __device__ __forceinline__ T lds_ld(uint32_t addr) {
       reinterpret_cast<const lds_byte*>((size_t)addr));
 }
 
-// Key sub-vector J of the lane's key: gather its fp16 row (address = replica
-// offset | code << 8) and contract it with dims 8J..8J+7 of the query, which
-// the A-broadcast takes from block (2J mod 16) / (2J+1 mod 16) of Aq.
+// Scores of the lane's key against the query rows: key sub-vector J (the
+// gathered fp16 row kv[J]) is contracted with dims 8J..8J+7 of the query,
+// which the A-broadcast takes from block (2J mod 16) / (2J+1 mod 16) of Aq.
+// Even and odd halves accumulate separately to halve the dependent chain.
 template <int J>
-__device__ __forceinline__ void key_step(const uint32_t (&kw)[4], uint32_t kbase,
-                                         const half4_t (&Aq)[2], float4_t& sc) {
-  const uint32_t addr = __builtin_amdgcn_perm(kw[J >> 2], kbase, 0x0c0c0000u | ((4u + (J & 3)) << 8));
-  const half8_t kv = lds_ld<half8_t>(addr);
-  const half4_t lo = {kv[0], kv[1], kv[2], kv[3]};
-  const half4_t hi = {kv[4], kv[5], kv[6], kv[7]};
-  sc = __builtin_amdgcn_mfma_f32_4x4x4f16(Aq[(2 * J) >> 4], lo, sc, 4, (2 * J) & 15, 0);
-  sc = __builtin_amdgcn_mfma_f32_4x4x4f16(Aq[(2 * J + 1) >> 4], hi, sc, 4, (2 * J + 1) & 15, 0);
+__device__ __forceinline__ void key_mfma(const half8_t (&kv)[16], const half4_t (&Aq)[2],
+                                         float4_t& s0, float4_t& s1) {
+  const half4_t lo = {kv[J][0], kv[J][1], kv[J][2], kv[J][3]};
+  const half4_t hi = {kv[J][4], kv[J][5], kv[J][6], kv[J][7]};
+  s0 = __builtin_amdgcn_mfma_f32_4x4x4f16(Aq[(2 * J) >> 4], lo, s0, 4, (2 * J) & 15, 0);
+  s1 = __builtin_amdgcn_mfma_f32_4x4x4f16(Aq[(2 * J + 1) >> 4], hi, s1, 4, (2 * J + 1) & 15, 0);
 }
 
 template <int... J>
-__device__ __forceinline__ void key_steps(std::integer_sequence<int, J...>, const uint32_t (&kw)[4],
-                                          uint32_t kbase, const half4_t (&Aq)[2], float4_t& sc) {
-  (key_step<J>(kw, kbase, Aq, sc), ...);
+__device__ __forceinline__ void key_mfmas(std::integer_sequence<int, J...>, const half8_t (&kv)[16],
+                                          const half4_t (&Aq)[2], float4_t& s0, float4_t& s1) {
+  (key_mfma<J>(kv, Aq, s0, s1), ...);
 }
 
 __device__ __forceinline__ int kv_len(const StreamParams& p, const int32_t* kv_lens, int b) {
@@ -164,7 +165,7 @@ __device__ __forceinline__ int unit_len(const StreamParams& p, const int32_t* kv
   return hi3 > lo0 ? hi3 - lo0 : 0;
 }
 
-__global__ __launch_bounds__(kThreads, 1) void attend_stream_kernel(
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_stream_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ k_codes,
     const float* __restrict__ k_codebook, const float* __restrict__ smooth,
     const uint8_t* __restrict__ v_codes, const float* __restrict__ v_codebook,
@@ -176,8 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_stream_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- codebooks into LDS as replicated fp16 rows -------------------------
-  {
-    const int code = tid >> 2;
+  // four threads per code: each writes a quarter of the code's replicas
+  for (int code = tid >> 2; code < 256; code += kThreads / 4) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
     if (code < p.n_c) {
       a = reinterpret_cast<const float4*>(k_codebook)[2 * code];
@@ -198,14 +199,14 @@ __global__ __launch_bounds__(kThreads, 1) void attend_stream_kernel(
       *reinterpret_cast<uint2*>(lds + kValTab + code * 256 + (s0 + k) * 8) = hv;
   }
 
-  // ---- unit prefix (exclusive) over the U units: 4 units per thread -------
+  // ---- unit prefix (exclusive) over the U <= kMaxUnits units --------------
   int* pre = reinterpret_cast<int*>(lds + kPrefix);
   int* scan = reinterpret_cast<int*>(lds + kScan);
   {
-    int loc[4], sum = 0;
+    int loc[kUnitsPerThread], sum = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int u = 4 * tid + k;
+    for (int k = 0; k < kUnitsPerThread; ++k) {
+      const int u = kUnitsPerThread * tid + k;
       loc[k] = sum;
       sum += u < p.U ? unit_len(p, kv_lens, u, nullptr) : 0;
     }
@@ -226,8 +227,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_stream_kernel(
     }
     const int excl = off + incl - sum;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int u = 4 * tid + k;
+    for (int k = 0; k < kUnitsPerThread; ++k) {
+      const int u = kUnitsPerThread * tid + k;
       if (u < p.U) pre[u] = excl + loc[k];
     }
     if (tid == 0) pre[p.U] = total;
@@ -394,10 +395,33 @@ __global__ __launch_bounds__(kThreads, 1) void attend_stream_kernel(
       for (int k = 0; k < 16; ++k) vr[k] = vr_n[k];
       if (tb + 64 < t1) load_codes(tb + 64, kc_n, vr_n);
 
+      // ---- all LDS gathers of the block, issued up front -----------------
+      // key rows: address = replica offset | code << 8
+      half8_t kv[16];
+      {
+        const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          kv[j] = lds_ld<half8_t>(
+              __builtin_amdgcn_perm(kw[j >> 2], kbase, 0x0c0c0000u | ((4u + (j & 3)) << 8)));
+      }
+      // value rows of key pair k: [key 0 sub 2n, key 1 sub 2n, key 0 sub 2n+1, key 1 sub 2n+1]
+      u32x2_t vg[8][4];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        // [code(key 0, 2n), code(key 0, 2n+1), code(key 1, 2n), code(key 1, 2n+1)]
+        const uint32_t w = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x05040100u);
+        vg[k][0] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020400u));
+        vg[k][1] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020600u));
+        vg[k][2] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020500u));
+        vg[k][3] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020700u));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
       // ---- scores on the matrix cores ----------------------------------
-      float4_t sc = {0.f, 0.f, 0.f, 0.f};
-      const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
-      key_steps(std::make_integer_sequence<int, 16>{}, kw, kbase + kKeyTab, Aq, sc);
+      float4_t sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
+      key_mfmas(std::make_integer_sequence<int, 16>{}, kv, Aq, sc0, sc1);
+      const float4_t sc = sc0 + sc1;
 
       // ---- masks and lazy online softmax -------------------------------
       float s[kRows] = {sc[0], sc[1], sc[2], sc[3]};
@@ -454,18 +478,8 @@ __global__ __launch_bounds__(kThreads, 1) void attend_stream_kernel(
         const uint32_t x = pp[k];
         const uint4 au = make_uint4(__builtin_amdgcn_perm(0u, x, sa0), __builtin_amdgcn_perm(0u, x, sa1),
                                     __builtin_amdgcn_perm(0u, x, sa2), __builtin_amdgcn_perm(0u, x, sa3));
-        // [code(key 0, 2n), code(key 0, 2n+1), code(key 1, 2n), code(key 1, 2n+1)]
-        const uint32_t w = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x05040100u);
-        const uint32_t a00 = __builtin_amdgcn_perm(w, vbase, 0x0c020400u);  // key 0, sub 2n
-        const uint32_t a01 = __builtin_amdgcn_perm(w, vbase, 0x0c020600u);  // key 1, sub 2n
-        const uint32_t a10 = __builtin_amdgcn_perm(w, vbase, 0x0c020500u);  // key 0, sub 2n+1
-        const uint32_t a11 = __builtin_amdgcn_perm(w, vbase, 0x0c020700u);  // key 1, sub 2n+1
-        const u32x2_t r00 = lds_ld<u32x2_t>(a00);
-        const u32x2_t r01 = lds_ld<u32x2_t>(a01);
-        const u32x2_t r10 = lds_ld<u32x2_t>(a10);
-        const u32x2_t r11 = lds_ld<u32x2_t>(a11);
-        const uint4 b0 = make_uint4(r00.x, r00.y, r01.x, r01.y);
-        const uint4 b1 = make_uint4(r10.x, r10.y, r11.x, r11.y);
+        const uint4 b0 = make_uint4(vg[k][0].x, vg[k][0].y, vg[k][1].x, vg[k][1].y);
+        const uint4 b1 = make_uint4(vg[k][2].x, vg[k][2].y, vg[k][3].x, vg[k][3].y);
         const half8_t A = *reinterpret_cast<const half8_t*>(&au);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, *reinterpret_cast<const half8_t*>(&b0), acc0,
                                                       0, 0, 0);
@@ -656,7 +670,7 @@ bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int dk, int d
   if (B <= 0 || Hq <= 0 || Sq <= 0 || Hkv <= 0 || S_cap <= 0 || Hq % Hkv) return false;
   const long long G = Hq / Hkv, GS = G * Sq, n_rg = (GS + kRows - 1) / kRows;
   const long long U = (long long)B * Hkv * n_rg;
-  if (U > 4095 || U * (long long)S_cap >= (1LL << 30)) return false;
+  if (U > kMaxUnits || U * (long long)S_cap >= (1LL << 30)) return false;
   if (sp) {
     sp->B = B; sp->Hq = Hq; sp->Sq = Sq; sp->Hkv = Hkv; sp->S_cap = S_cap; sp->n_c = n_c;
     sp->G = (int)G; sp->GS = (int)GS; sp->n_rg = (int)n_rg; sp->U = (int)U; sp->cmin = 256;

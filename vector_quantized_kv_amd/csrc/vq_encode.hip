@@ -157,6 +157,16 @@ __global__ __launch_bounds__(kThreads) void pvq_kernel(
   const int b = (int)(bh / d.H);
   const float* srow = smooth ? smooth + (long long)(d.smooth_rows == 1 ? 0 : h) * D + j * DS : nullptr;
 
+  // Short inputs (CSPLIT > 1) are latency bound: stage the codebook in LDS
+  // with one coalesced pass instead of walking it with dependent scalar loads.
+  const float* cbk = cb;
+  if constexpr (CSPLIT > 1) {
+    __shared__ float s_cb[256 * DS];
+    for (int i = threadIdx.x; i < d.n_c * DS; i += kThreads) s_cb[i] = cb[i];
+    __syncthreads();
+    cbk = s_cb;
+  }
+
   float x[DS];
   int idx = 0;
   if constexpr (MODE != 2) {
@@ -174,13 +184,14 @@ __global__ __launch_bounds__(kThreads) void pvq_kernel(
 
     // Nearest centroid: fp32 squared distance summed over e in order,
     // strict '<' keeps the lowest index on exact ties.  The centroid index is
-    // wave-uniform, so each centroid is one scalar load shared by all lanes.
+    // wave-uniform, so each centroid is one scalar load (or one LDS broadcast)
+    // shared by all lanes.
     const int c_lo = d.n_c * part / CSPLIT, c_hi = d.n_c * (part + 1) / CSPLIT;
     float best = INFINITY;
     idx = c_lo;
 #pragma unroll 8
     for (int c = c_lo; c < c_hi; ++c) {
-      const float* cc = cb + c * DS;
+      const float* cc = cbk + c * DS;
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < DS; ++e) {
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void pvq_kernel(
   }
 
   if constexpr (MODE != 0) {
-    const float* cc = cb + idx * DS;
+    const float* cc = cbk + idx * DS;
 #pragma unroll
     for (int e = 0; e < DS; ++e) x[e] = cc[e];
     if (d.transform) wht<D, DS>(x, j);  // H is its own inverse
