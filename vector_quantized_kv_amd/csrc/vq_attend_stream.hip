@@ -42,7 +42,9 @@
 //           more than 8 (log2 units), so p <= 256 is exact enough in fp16
 //           and the usual block needs no cross-lane work.
 //   values  8 x 2 v_mfma_f32_16x16x32_f16: M = (row, e), N = 16 value
-//           sub-vectors (even / odd in two tiles), K = (2 keys, e'), with
+//           sub-vectors (even / odd in two tiles), K = (2 keys, e') where
+//           K group g of instruction q takes keys 4 (2q) + g, 4 (2q + 1) + g
+//           (so each value-code load of the wave is one 128-byte span), with
 //           A[(r,e)][(t,e')] = p_r(t) [e == e'] built by 4 v_perm from the
 //           staged p, and B = two gathered value rows taken as they are.
 #include "vq_internal.h"
@@ -368,34 +370,49 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const int tmax = p.S_cap - 1;
 
     // codes of one block: the lane's key (16 bytes) and, for the value
-    // MFMA, the code pairs (2n, 2n+1) of keys 16 g + j, j = 0..15, kept as
+    // MFMA, the code pairs (2n, 2n+1) of keys 4 j + g, j = 0..15, kept as
     // loaded (one per register) so that the prefetch of the next block is
-    // not waited for until that block is processed
+    // not waited for until that block is processed.  Load j of the wave
+    // reads keys 4 j .. 4 j + 3: one contiguous 128-byte span.
     auto load_codes = [&](int tb, uint4& kc, uint32_t (&vr)[16]) {
       kc = *reinterpret_cast<const uint4*>(kc_row + (size_t)min(tb + lane, tmax) * 16);
-      const int tv = tb + 16 * grp16;
+      const int tv = tb + grp16;
       if (tb + 64 <= p.S_cap) {
         const uint16_t* vp = reinterpret_cast<const uint16_t*>(vc_row + (size_t)tv * 32);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) vr[k] = vp[16 * k];
+        for (int k = 0; k < 16; ++k) vr[k] = vp[64 * k];
       } else {
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-          vr[k] = *reinterpret_cast<const uint16_t*>(vc_row + (size_t)min(tv + k, tmax) * 32);
+          vr[k] = *reinterpret_cast<const uint16_t*>(vc_row + (size_t)min(tv + 4 * k, tmax) * 32);
       }
     };
 
-    uint4 kc_n;
-    uint32_t vr_n[16];
-    load_codes(t0, kc_n, vr_n);
-    for (int tb = t0; tb < t1; tb += 64) {
-      const uint4 kc = kc_n;
-      uint32_t vr[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) vr[k] = vr_n[k];
-      if (tb + 64 < t1) load_codes(tb + 64, kc_n, vr_n);
+    // Software pipeline over 64-key blocks.  A block's key-row gathers and
+    // score MFMAs run while the previous block's value rows (gathered at the
+    // end of its own stage) go through the value MFMAs; the code buffers of
+    // consecutive blocks alternate between two register sets, so the
+    // prefetch of the next block is only waited for when it is used.
+    u32x2_t vg[8][4];  // value rows of the block whose value MFMAs are pending
+    uint32_t pp[8];    // that block's p, staged into the A operand layout
 
-      // ---- all LDS gathers of the block, issued up front -----------------
+    auto value_mfmas = [&]() {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t x = pp[k];
+        const uint4 au = make_uint4(__builtin_amdgcn_perm(0u, x, sa0), __builtin_amdgcn_perm(0u, x, sa1),
+                                    __builtin_amdgcn_perm(0u, x, sa2), __builtin_amdgcn_perm(0u, x, sa3));
+        const uint4 b0 = make_uint4(vg[k][0].x, vg[k][0].y, vg[k][1].x, vg[k][1].y);
+        const uint4 b1 = make_uint4(vg[k][2].x, vg[k][2].y, vg[k][3].x, vg[k][3].y);
+        const half8_t A = *reinterpret_cast<const half8_t*>(&au);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, *reinterpret_cast<const half8_t*>(&b0), acc0,
+                                                      0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, *reinterpret_cast<const half8_t*>(&b1), acc1,
+                                                      0, 0, 0);
+      }
+    };
+
+    auto stage = [&](int tb, const uint4& kc, const uint32_t (&vr)[16], bool pending) {
       // key rows: address = replica offset | code << 8
       half8_t kv[16];
       {
@@ -405,18 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
           kv[j] = lds_ld<half8_t>(
               __builtin_amdgcn_perm(kw[j >> 2], kbase, 0x0c0c0000u | ((4u + (j & 3)) << 8)));
       }
-      // value rows of key pair k: [key 0 sub 2n, key 1 sub 2n, key 0 sub 2n+1, key 1 sub 2n+1]
-      u32x2_t vg[8][4];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        // [code(key 0, 2n), code(key 0, 2n+1), code(key 1, 2n), code(key 1, 2n+1)]
-        const uint32_t w = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x05040100u);
-        vg[k][0] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020400u));
-        vg[k][1] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020600u));
-        vg[k][2] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020500u));
-        vg[k][3] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020700u));
-      }
       __builtin_amdgcn_sched_barrier(0);
+      if (pending) value_mfmas();
 
       // ---- scores on the matrix cores ----------------------------------
       float4_t sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
@@ -462,31 +469,48 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       {
         const uint32_t p01 = pack_half2_rtz(pr[0], pr[1]);
         const uint32_t p23 = pack_half2_rtz(pr[2], pr[3]);
-        *reinterpret_cast<uint16_t*>(ps + 0 * kPRow + 2 * lane) = (uint16_t)p01;
-        *reinterpret_cast<uint16_t*>(ps + 1 * kPRow + 2 * lane) = (uint16_t)(p01 >> 16);
-        *reinterpret_cast<uint16_t*>(ps + 2 * kPRow + 2 * lane) = (uint16_t)p23;
-        *reinterpret_cast<uint16_t*>(ps + 3 * kPRow + 2 * lane) = (uint16_t)(p23 >> 16);
+        // key 4 q + g is staged at position 16 g + q, so that lane group g
+        // finds its keys 4 q + g (q = 0..15) contiguous
+        uint8_t* const pw = ps + 2 * (16 * (lane & 3) + (lane >> 2));
+        *reinterpret_cast<uint16_t*>(pw + 0 * kPRow) = (uint16_t)p01;
+        *reinterpret_cast<uint16_t*>(pw + 1 * kPRow) = (uint16_t)(p01 >> 16);
+        *reinterpret_cast<uint16_t*>(pw + 2 * kPRow) = (uint16_t)p23;
+        *reinterpret_cast<uint16_t*>(pw + 3 * kPRow) = (uint16_t)(p23 >> 16);
       }
       wave_sync_lds();
       const uint4 P0 = *reinterpret_cast<const uint4*>(ps + rA * kPRow + 32 * grp16);
       const uint4 P1 = *reinterpret_cast<const uint4*>(ps + rA * kPRow + 32 * grp16 + 16);
-      const uint32_t pp[8] = {P0.x, P0.y, P0.z, P0.w, P1.x, P1.y, P1.z, P1.w};
+      pp[0] = P0.x; pp[1] = P0.y; pp[2] = P0.z; pp[3] = P0.w;
+      pp[4] = P1.x; pp[5] = P1.y; pp[6] = P1.z; pp[7] = P1.w;
 
-      // ---- values on the matrix cores ----------------------------------
+
+      // ---- this block's value rows, consumed by the next stage ---------
+      // rows of key pair k: [key 0 sub 2n, key 1 sub 2n, key 0 sub 2n+1, key 1 sub 2n+1]
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const uint32_t x = pp[k];
-        const uint4 au = make_uint4(__builtin_amdgcn_perm(0u, x, sa0), __builtin_amdgcn_perm(0u, x, sa1),
-                                    __builtin_amdgcn_perm(0u, x, sa2), __builtin_amdgcn_perm(0u, x, sa3));
-        const uint4 b0 = make_uint4(vg[k][0].x, vg[k][0].y, vg[k][1].x, vg[k][1].y);
-        const uint4 b1 = make_uint4(vg[k][2].x, vg[k][2].y, vg[k][3].x, vg[k][3].y);
-        const half8_t A = *reinterpret_cast<const half8_t*>(&au);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, *reinterpret_cast<const half8_t*>(&b0), acc0,
-                                                      0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, *reinterpret_cast<const half8_t*>(&b1), acc1,
-                                                      0, 0, 0);
+        // [code(key 0, 2n), code(key 0, 2n+1), code(key 1, 2n), code(key 1, 2n+1)]
+        const uint32_t w = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x05040100u);
+        vg[k][0] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020400u));
+        vg[k][1] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020600u));
+        vg[k][2] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020500u));
+        vg[k][3] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020700u));
       }
+    };
+
+    uint4 kcA, kcB;
+    uint32_t vrA[16], vrB[16];
+    load_codes(t0, kcA, vrA);
+    for (int tb = t0;;) {
+      if (tb + 64 < t1) load_codes(tb + 64, kcB, vrB);
+      stage(tb, kcA, vrA, tb != t0);
+      tb += 64;
+      if (tb >= t1) break;
+      if (tb + 64 < t1) load_codes(tb + 64, kcA, vrA);
+      stage(tb, kcB, vrB, true);
+      tb += 64;
+      if (tb >= t1) break;
     }
+    value_mfmas();
 
     pos = seg_end;
     if (pos >= end) {
