@@ -329,3 +329,21 @@ def test_split_invariance_and_gqa_equivalence():
     m = run_attend(rep)
     assert np.max(np.abs(a.astype(np.float64) - m)) <= 2e-3
     check_attn(a, oracle_attend(c, c["k_codes"], c["v_codes"]), "split/gqa")
+
+
+@pytest.mark.parametrize("Hq,Hkv,Sq,lens,causal,window", [
+    (4, 2, 100, [400, 130, 60], True, 0),     # GQA-2: 128-row tiles span two heads; len < S_q
+    (2, 2, 64, [400, 64, 0], True, 0),        # one full row tile per kv head; an empty row
+    (8, 2, 40, [400, 300, 41], True, 33),     # GQA-4 with a sliding window
+    (2, 1, 129, [400, 200, 129], False, 0),   # non-causal, a 1-row last tile
+    (2, 1, 96, [400, 390, 250], False, 50),   # non-causal window
+])
+def test_many_query_shapes(Hq, Hkv, Sq, lens, causal, window):
+    """Shapes with at least 64 query rows per kv head (the prefill path):
+    head dim 128, key sub_dim 8, value sub_dim 4, against the oracle."""
+    c = small_case(50 + Sq, B=3, Hq=Hq, Hkv=Hkv, Sq=Sq, D=128, dk=8, dv=4, S_cap=400)
+    c["kv_lens"] = np.array(lens, np.int32)
+    c["causal"], c["window"] = causal, window
+    out = run_attend(c)
+    ref = oracle_attend(c, c["k_codes"], c["v_codes"])
+    check_attn(out, ref, f"many-query Hq{Hq} Hkv{Hkv} Sq{Sq} causal{causal} W{window}")

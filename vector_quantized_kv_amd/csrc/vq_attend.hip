@@ -395,6 +395,8 @@ bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, A
   // the streaming kernel (chosen by the code sizes, which this call does not
   // see) may need more
   pl->workspace_bytes = std::max(pl->workspace_bytes, stream_workspace_bytes(B, Hq, Sq, D, Hkv));
+  pl->workspace_bytes =
+      std::max(pl->workspace_bytes, tile_workspace_bytes(B, Hq, Sq, D, Hkv, S_cap, window));
   pl->R = 0;
   pl->n_rgroups = 0;
   return true;
@@ -418,6 +420,11 @@ int attend_pick_rows(int rows, int nsk, int n_c, int dv, int nsv, int D, size_t*
 }
 
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_t st) {
+  {
+    TileParams tp;
+    if (tile_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c, &tp))
+      return launch_attend_tile(a, tp, st);
+  }
   {
     StreamParams sp;
     size_t lds = 0;

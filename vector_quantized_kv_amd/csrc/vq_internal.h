@@ -94,6 +94,19 @@ size_t stream_workspace_bytes(int B, int Hq, int Sq, int D, int Hkv);
 hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds_bytes,
                                 hipStream_t st);
 
+// Many-query kernel (prefill: at least 64 query rows per kv head; head dim
+// 128, key sub_dim 8, value sub_dim 4).
+struct TileParams {
+  int B, Hq, Sq, Hkv, S_cap, n_c, smooth_rows, transform, causal, window;
+  int G, GS, n_rt, n_split;
+  float fold;  // WHT normalization (if any) * scale * log2(e)
+};
+bool tile_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, int dk, int dv, int n_c,
+               TileParams* tp);
+// Workspace of the many-query kernel for this shape (0 if it does not apply).
+size_t tile_workspace_bytes(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window);
+hipError_t launch_attend_tile(const AttendArgs& a, TileParams tp, hipStream_t st);
+
 // Pure function of the shape: split count, row grouping, workspace size.
 bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, AttendPlan* p);
 
