@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0
 FP32_VALU_PEAK_TFLOPS = 157.3
 MIB = 1 << 20
 COPY_BYTES = 1 << 30
-ATTEND_SOURCES = ("vq_attend.hip", "vq_attend_mfma.hip", "vq_internal.h")
+ATTEND_SOURCES = ("vq_attend.hip", "vq_attend_mfma.hip", "vq_attend_stream.hip", "vq_attend_tile.hip",
+                  "vq_internal.h")
 
 
 def parse():
@@ -223,7 +224,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "vq_attend (split-K attention + merge)",
+            "kernel": "vq_attend (attend_stream_kernel + stream_merge_kernel)",
             "bytes_per_launch": attn_bytes,
             "us_per_launch": round(attn_us, 2),
         },

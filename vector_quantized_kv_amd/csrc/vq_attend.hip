@@ -428,7 +428,8 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_
   {
     StreamParams sp;
     size_t lds = 0;
-    if (stream_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.dk, a.dv, a.n_c, &sp, &lds, nullptr))
+    if (stream_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c, &sp, &lds,
+                    nullptr))
       return launch_attend_stream(a, sp, lds, st);
   }
   AttParams p;

@@ -49,6 +49,7 @@
 //           staged p, and B = two gathered value rows taken as they are.
 #include "vq_internal.h"
 
+#include <algorithm>
 #include <utility>
 
 namespace vq {
@@ -688,13 +689,17 @@ int cached_cu_count() {
 
 }  // namespace
 
-bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int dk, int dv, int n_c,
+bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, int dk, int dv, int n_c,
                  StreamParams* sp, size_t* lds_bytes, size_t* ws_bytes) {
   if (D != kD || dk != 8 || dv != 4 || n_c < 1 || n_c > 256) return false;
   if (B <= 0 || Hq <= 0 || Sq <= 0 || Hkv <= 0 || S_cap <= 0 || Hq % Hkv) return false;
   const long long G = Hq / Hkv, GS = G * Sq, n_rg = (GS + kRows - 1) / kRows;
   const long long U = (long long)B * Hkv * n_rg;
   if (U > kMaxUnits || U * (long long)S_cap >= (1LL << 30)) return false;
+  // the persistent grid's fixed cost (table fill, unit prefix, merge) only
+  // pays off with enough keys: small problems go to the per-unit kernel
+  const long long max_range = window > 0 ? std::min<long long>(S_cap, (long long)Sq + window - 1) : S_cap;
+  if (U * max_range < (1LL << 18)) return false;
   if (sp) {
     sp->B = B; sp->Hq = Hq; sp->Sq = Sq; sp->Hkv = Hkv; sp->S_cap = S_cap; sp->n_c = n_c;
     sp->G = (int)G; sp->GS = (int)GS; sp->n_rg = (int)n_rg; sp->U = (int)U; sp->cmin = 256;

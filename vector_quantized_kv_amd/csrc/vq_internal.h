@@ -87,7 +87,7 @@ struct StreamParams {
 };
 // True if the shape runs on the streaming kernel; fills its parameters, LDS
 // bytes and workspace bytes.
-bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int dk, int dv, int n_c,
+bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, int dk, int dv, int n_c,
                  StreamParams* sp, size_t* lds_bytes, size_t* ws_bytes);
 // Workspace of the streaming kernel for this shape (0 if D is not 128).
 size_t stream_workspace_bytes(int B, int Hq, int Sq, int D, int Hkv);
