@@ -347,3 +347,21 @@ def test_many_query_shapes(Hq, Hkv, Sq, lens, causal, window):
     out = run_attend(c)
     ref = oracle_attend(c, c["k_codes"], c["v_codes"])
     check_attn(out, ref, f"many-query Hq{Hq} Hkv{Hkv} Sq{Sq} causal{causal} W{window}")
+
+
+@pytest.mark.parametrize("Hq,Sq,lens,causal,window", [
+    (32, 1, [8192, 5000, 0, 1], True, 0),       # GQA-4 decode, ragged with empty and 1-key rows
+    (24, 1, [8192, 8000, 300, 64], True, 0),    # GQA-3: a 4-row unit is partly filled
+    (16, 3, [8192, 2, 4097, 8191], True, 0),    # 2 query positions per row group; len < S_q
+    (32, 1, [8192, 7000, 6000, 100], False, 0),
+    (8, 2, [8192, 8190, 5000, 2000], True, 8190),  # windowed (the window still spans the buffer)
+])
+def test_stream_kernel_cases(Hq, Sq, lens, causal, window):
+    """Decode-shaped problems large enough for the persistent streaming path
+    (head dim 128, key sub_dim 8, value sub_dim 4), every output row checked."""
+    c = small_case(70 + Hq + Sq, B=4, Hq=Hq, Hkv=8, Sq=Sq, D=128, dk=8, dv=4, S_cap=8192)
+    c["kv_lens"] = np.array(lens, np.int32)
+    c["causal"], c["window"] = causal, window
+    out = run_attend(c)
+    ref = oracle_attend(c, c["k_codes"], c["v_codes"])
+    check_attn(out, ref, f"stream Hq{Hq} Sq{Sq} causal{causal} W{window}")

@@ -4,40 +4,35 @@
 //
 // Method ("Metal Kernels API" page, "Fused SDPA", metal_fused_sdpa;
 // "veloxquant_mlx.cache.vecinfer_cache module" page, fused_sdpa): the query
-// gets the dual transform q~ = (q * s) . H, the score of key t is
-// q~ . C_k[codes of t] (equal to q . K_hat_t), the softmax runs online in
-// base 2 over split chunks, and the output accumulates p_t C_v[codes of t].
-// Instead of a per-sub-vector lookup table of query-centroid dot products,
-// the key sub-vectors are gathered from the codebook and contracted with the
-// query on the matrix cores: on gfx950 that keeps the per-key work off the
-// vector ALUs.
+// gets the dual transform q~ = (q * s) . H, the score of key t is the sum
+// over sub-vectors j of q~[j] . C_k[code_j(t)] (equal to q . K_hat_t), read
+// from a per-unit table of query-centroid products; the softmax runs online
+// in base 2 over split chunks, and the output accumulates p_t C_v[codes of t].
 //
 // Work split.  A unit is (batch row b, kv head g, group of 4 query rows);
 // query row rho of a kv head is (position rho / G, head g * G + rho % G).
 // A unit's keys are the union of its rows' valid ranges.  Units are laid
-// end to end into one token space of T = sum of unit lengths, and the
-// 16 * gridDim waves each take one equal chunk of it (at least 256 keys), so
+// end to end into one token space of T = sum of unit lengths, and each
+// persistent workgroup takes one equal chunk of it (at least 512 keys), so
 // ragged lengths and masks cost no imbalance.  The unit prefix is computed
-// on the device from kv_lens by every workgroup.  A wave writes one partial
-// (m, l, acc) per (chunk c, unit u) it touches, into slot c + u (distinct
-// for all overlapping pairs since chunks and units are both ordered), and
-// the merge kernel combines the slots of each unit.
+// on the device from kv_lens by every workgroup.  The workgroup walks its
+// chunk one unit segment at a time: it builds the unit's score table in
+// LDS, its 8 waves take the segment's 64-key blocks in turn, and the waves'
+// partials (m, l, acc) are combined in LDS into slot c + u of (chunk c,
+// unit u) (distinct for all overlapping pairs since chunks and units are
+// both ordered).  The merge kernel combines the slots of each unit.
 //
-// LDS holds, for the whole persistent workgroup, the key codebook as fp16
-// rows replicated 16 times ([code][replica][8 halves], 64 KiB) and the value
-// codebook replicated 32 times ([code][replica][4 halves], 64 KiB).  A lane
-// always reads replica (lane mod 16) for keys and (lane mod 32) for values,
-// so the 16 (b128) or 32 (b64) lanes served together always hit distinct
-// banks, whatever the codes.  The LDS byte address of a gathered row is the
-// replica offset in byte 0 and the code in byte 1, so one v_perm per code
-// both extracts the code byte and forms the address.
+// LDS holds the score table LUT[code][j][row] (fp32, 256 B per code, 64 KiB)
+// and the value codebook as fp16 rows replicated 32 times ([code][replica][4
+// halves], 64 KiB).  For the scores a lane reads its key's 16 sub-vectors in
+// an order rotated by lane mod 16, so the 16 lanes served together read 16
+// distinct j (distinct bank quads); for the values it reads replica
+// (lane mod 32), so the 32 lanes served together hit distinct banks.  The
+// LDS byte address of a gathered row has the code in byte 1, so one v_perm
+// per code both extracts the code byte and forms the address.
 //
 // Per 64-key block and wave (lane = key for the scores):
-//   scores  16 b128 gathers and 32 v_mfma_f32_4x4x4_16b_f16: block b of the
-//           instruction covers keys 4b..4b+3, K = 4 head dims; the query
-//           operand comes from one block through the A-broadcast
-//           (cbsz = 4, abid = k mod 16), so all of q~ lives in 4 VGPRs.
-//           The scores land as lane = key, 4 registers = 4 rows.
+//   scores  16 b128 table gathers and 60 fp32 adds: 4 rows at once.
 //   softmax lazy: the running max m_r moves only when a score exceeds it by
 //           more than 8 (log2 units), so p <= 256 is exact enough in fp16
 //           and the usual block needs no cross-lane work.
@@ -46,11 +41,11 @@
 //           K group g of instruction q takes keys 4 (2q) + g, 4 (2q + 1) + g
 //           (so each value-code load of the wave is one 128-byte span), with
 //           A[(r,e)][(t,e')] = p_r(t) [e == e'] built by 4 v_perm from the
-//           staged p, and B = two gathered value rows taken as they are.
+//           staged p (rounded to nearest; the row sums add the rounded p),
+//           and B = two gathered value rows taken as they are.
 #include "vq_internal.h"
 
 #include <algorithm>
-#include <utility>
 
 namespace vq {
 namespace {
@@ -60,19 +55,21 @@ constexpr int kThreads = kW * 64;
 constexpr int kD = 128;
 constexpr int kRows = 4;               // query rows per unit
 constexpr int kSlot = kRows * kD + 2 * kRows;  // floats per partial slot
-constexpr uint32_t kKeyTab = 0;        // [256][16][8] fp16
+constexpr uint32_t kLut = 0;           // [256][16][4] fp32 score table
 constexpr uint32_t kValTab = 65536;    // [256][32][4] fp16
 constexpr uint32_t kPStage = 131072;   // [wave][row][72] fp16
 constexpr uint32_t kPRow = 144;        // bytes per staged row (64 fp16 + pad)
 constexpr uint32_t kPWave = kRows * kPRow;
-constexpr uint32_t kScan = kPStage + kW * kPWave;
+constexpr uint32_t kQs = kPStage + kW * kPWave;  // [row][128] fp32 query rows
+constexpr uint32_t kCbk = kQs + kRows * kD * 4;  // [256][8] fp32 key codebook
+constexpr uint32_t kScan = kCbk + 256 * 8 * 4;
 constexpr uint32_t kPrefix = kScan + 64;  // int prefix[U + 1]
 constexpr float kLazyMargin = 8.f;
 constexpr int kMaxUnits = 4095;        // units whose prefix fits in LDS
 constexpr int kUnitsPerThread = (kMaxUnits + kThreads) / kThreads;
-constexpr int kMaxWaves = 256 * 16;    // partial slots reserved for chunks (>= 256 CUs * kW)
+constexpr int kMaxChunks = 4096;      // partial slots reserved for chunks (>= workgroups)
+static_assert(kPrefix + 4 * (kMaxUnits + 1) <= 160 * 1024, "LDS budget");
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -100,12 +97,6 @@ __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
   return *reinterpret_cast<const uint32_t*>(&h);
 }
 
-__device__ __forceinline__ uint32_t pack_half2_rtz(float a, float b) {
-  typedef __fp16 h2 __attribute__((ext_vector_type(2)));
-  const h2 v = __builtin_amdgcn_cvt_pkrtz(a, b);
-  return *reinterpret_cast<const uint32_t*>(&v);
-}
-
 // LDS accesses by byte address.  The kernel declares no static LDS, so the
 // dynamic area it uses starts at LDS address 0.
 typedef __attribute__((address_space(3))) uint8_t lds_byte;
@@ -113,25 +104,6 @@ template <typename T>
 __device__ __forceinline__ T lds_ld(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) T*>(
       reinterpret_cast<const lds_byte*>((size_t)addr));
-}
-
-// Scores of the lane's key against the query rows: key sub-vector J (the
-// gathered fp16 row kv[J]) is contracted with dims 8J..8J+7 of the query,
-// which the A-broadcast takes from block (2J mod 16) / (2J+1 mod 16) of Aq.
-// Even and odd halves accumulate separately to halve the dependent chain.
-template <int J>
-__device__ __forceinline__ void key_mfma(const half8_t (&kv)[16], const half4_t (&Aq)[2],
-                                         float4_t& s0, float4_t& s1) {
-  const half4_t lo = {kv[J][0], kv[J][1], kv[J][2], kv[J][3]};
-  const half4_t hi = {kv[J][4], kv[J][5], kv[J][6], kv[J][7]};
-  s0 = __builtin_amdgcn_mfma_f32_4x4x4f16(Aq[(2 * J) >> 4], lo, s0, 4, (2 * J) & 15, 0);
-  s1 = __builtin_amdgcn_mfma_f32_4x4x4f16(Aq[(2 * J + 1) >> 4], hi, s1, 4, (2 * J + 1) & 15, 0);
-}
-
-template <int... J>
-__device__ __forceinline__ void key_mfmas(std::integer_sequence<int, J...>, const half8_t (&kv)[16],
-                                          const half4_t (&Aq)[2], float4_t& s0, float4_t& s1) {
-  (key_mfma<J>(kv, Aq, s0, s1), ...);
 }
 
 __device__ __forceinline__ int kv_len(const StreamParams& p, const int32_t* kv_lens, int b) {
@@ -179,27 +151,20 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- codebooks into LDS as replicated fp16 rows -------------------------
-  // four threads per code: each writes a quarter of the code's replicas
-  for (int code = tid >> 2; code < 256; code += kThreads / 4) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    if (code < p.n_c) {
-      a = reinterpret_cast<const float4*>(k_codebook)[2 * code];
-      b = reinterpret_cast<const float4*>(k_codebook)[2 * code + 1];
+  // ---- codebooks into LDS: keys as fp32 rows, values as replicated fp16 ---
+  {
+    float* cbk = reinterpret_cast<float*>(lds + kCbk);
+    for (int i = tid; i < 256 * 8; i += kThreads) cbk[i] = i < p.n_c * 8 ? k_codebook[i] : 0.f;
+    // four threads per code: each writes a quarter of the code's replicas
+    for (int code = tid >> 2; code < 256; code += kThreads / 4) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (code < p.n_c) v = reinterpret_cast<const float4*>(v_codebook)[code];
+      const uint2 hv = make_uint2(pack_half2(v.x, v.y), pack_half2(v.z, v.w));
+      const int s0 = (tid & 3) * 8;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        *reinterpret_cast<uint2*>(lds + kValTab + code * 256 + (s0 + k) * 8) = hv;
     }
-    const uint4 h = make_uint4(pack_half2(a.x, a.y), pack_half2(a.z, a.w), pack_half2(b.x, b.y),
-                               pack_half2(b.z, b.w));
-    const int r0 = (tid & 3) * 4;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<uint4*>(lds + kKeyTab + code * 256 + (r0 + k) * 16) = h;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (code < p.n_c) v = reinterpret_cast<const float4*>(v_codebook)[code];
-    const uint2 hv = make_uint2(pack_half2(v.x, v.y), pack_half2(v.z, v.w));
-    const int s0 = (tid & 3) * 8;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      *reinterpret_cast<uint2*>(lds + kValTab + code * 256 + (s0 + k) * 8) = hv;
   }
 
   // ---- unit prefix (exclusive) over the U <= kMaxUnits units --------------
@@ -238,25 +203,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     __syncthreads();
   }
   const int T = pre[p.U];
-  const int NW = gridDim.x * kW;
-  const int C = max(p.cmin, (T + NW - 1) / NW);
+  const int C = max(p.cmin, (T + (int)gridDim.x - 1) / (int)gridDim.x);
   if (blockIdx.x == 0) {
     for (int u = tid; u <= p.U; u += kThreads) header[1 + u] = pre[u];
     if (tid == 0) header[0] = C;
   }
-
-  const int c = blockIdx.x * kW + wave;
+  const int c = blockIdx.x;
   const int start = c * C;  // T <= U * S_cap < 2^30 is checked on the host
   const int end = min(T, start + C);
-  // state of the wave's current unit segment; the last one is combined
-  // across the workgroup at the end
-  int u_last = -1;
-  float m[kRows], lsum[kRows];
-  float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-#pragma unroll
-  for (int r = 0; r < kRows; ++r) { m[r] = -INFINITY; lsum[r] = 0.f; }
+  if (start >= T) return;
 
-  if (start < T) {
   // unit holding token position `start`: the largest u with pre[u] <= start
   int u = 0;
   {
@@ -268,8 +224,25 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     u = lo;
   }
 
-  // lane constants
-  const uint32_t kbase = (uint32_t)(lane & 15) * 16u;                  // key replica
+  // ---- lane constants ------------------------------------------------------
+  // Score gathers: at step k = 4 a + b the lane reads sub-vector
+  // j = 4 ((a + rdw) mod 4) + (b + rb) mod 4 with (rdw, rb) = lane mod 16, so
+  // the 16 lanes served together read 16 distinct j: 16 distinct bank
+  // quads of the [code][j][row] table, whatever the codes.  jt[a] holds the
+  // four byte offsets 16 j of steps (a, b), sel[b] the v_perm selector that
+  // places the code byte of sub-vector j above that offset.
+  const int rdw = (lane >> 2) & 3, rb = lane & 3;
+  uint32_t jt[4], sel[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      w |= (uint32_t)(16 * (4 * ((a + rdw) & 3) + ((b + rb) & 3))) << (8 * b);
+    jt[a] = w;
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) sel[b] = 0x0c0c0000u | ((4u + ((b + rb) & 3)) << 8) | (uint32_t)b;
   const uint32_t vbase = (uint32_t)(lane & 31) * 8u | (1u << 16);      // value replica + 64 KiB
   const int e_a = lane & 3;          // A operand of the value MFMA: row (rA, e_a)
   const int rA = (lane & 15) >> 2;
@@ -279,9 +252,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   const uint32_t sa2 = e_a == 0 ? 0x0c0c0302u : (e_a == 1 ? 0x03020c0cu : 0x0c0c0c0cu);
   const uint32_t sa3 = e_a == 2 ? 0x0c0c0302u : (e_a == 3 ? 0x03020c0cu : 0x0c0c0c0cu);
   uint8_t* const ps = lds + kPStage + wave * kPWave;
+  float* const qs = reinterpret_cast<float*>(lds + kQs);
+  float* const red = reinterpret_cast<float*>(lds + kLut);  // [kW][kSlot], over the table
+  const int tmax = p.S_cap - 1;
 
   int pos = start;
   while (true) {
+    // ---- segment: unit u, token positions [pos, seg_end) ----------------
     const int Pu = pre[u], Pn = pre[u + 1];
     const int seg_end = min(end, Pn);
     const int rg = u % p.n_rg;
@@ -303,11 +280,41 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       full_hi = min(full_hi, khi[r]);
     }
 
-    // ---- query: dual transform into the broadcast A layout -------------
-    // lane (bq = lane / 4, row ir = lane % 4) holds dims 4 bq + e and
-    // 64 + 4 bq + e (e = 0..3) of row ir: Aq[k] serves dim chunk 16 k + bq.
-    half4_t Aq[2];
-    {
+    const size_t row_tok = (size_t)bg * p.S_cap;
+    const uint8_t* const kc_row = k_codes + row_tok * 16;
+    const uint8_t* const vc_row = v_codes + row_tok * 32 + 2 * (lane & 15);
+
+    // codes of one block: the lane's key (16 bytes) and, for the value
+    // MFMA, the code pairs (2n, 2n+1) of keys 4 j + g, j = 0..15, kept as
+    // loaded (one per register) so that the prefetch of the next block is
+    // not waited for until that block is processed.  Load j of the wave
+    // reads keys 4 j .. 4 j + 3: one contiguous 128-byte span.
+    auto load_codes = [&](int tb, uint4& kc, uint32_t (&vr)[16]) {
+      kc = *reinterpret_cast<const uint4*>(kc_row + (size_t)min(tb + lane, tmax) * 16);
+      const int tv = tb + grp16;
+      if (tb + 64 <= p.S_cap) {
+        const uint16_t* vp = reinterpret_cast<const uint16_t*>(vc_row + (size_t)tv * 32);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) vr[k] = vp[64 * k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          vr[k] = *reinterpret_cast<const uint16_t*>(vc_row + (size_t)min(tv + 4 * k, tmax) * 32);
+      }
+    };
+
+    // the wave's blocks of the segment: t0 + 64 (wave + kW i); the first
+    // one's codes load while the table is built
+    const int tb_first = t0 + 64 * wave;
+    uint4 kcA, kcB;
+    uint32_t vrA[16], vrB[16];
+    if (tb_first < t1) load_codes(tb_first, kcA, vrA);
+
+    __syncthreads();  // the previous segment's combine has read the table area
+    // ---- query rows of the unit: dual transform, scaled, into LDS ---------
+    if (wave == 0) {
+      // lane (bq = lane / 4, row ir = lane % 4) holds dims 4 bq + e and
+      // 64 + 4 bq + e (e = 0..3) of row ir
       const int bq = lane >> 2, ir = lane & 3;
       const int rho = 4 * rg + ir;
       const int rc = rho < p.GS ? rho : p.GS - 1;
@@ -351,46 +358,54 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       }
       const float f = rho < p.GS ? p.fold : 0.f;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        Aq[k] = half4_t{(_Float16)(x[4 * k] * f), (_Float16)(x[4 * k + 1] * f),
-                        (_Float16)(x[4 * k + 2] * f), (_Float16)(x[4 * k + 3] * f)};
+      for (int k = 0; k < 2; ++k)
+        *reinterpret_cast<float4*>(qs + ir * kD + 64 * k + 4 * bq) =
+            make_float4(x[4 * k] * f, x[4 * k + 1] * f, x[4 * k + 2] * f, x[4 * k + 3] * f);
+    }
+    __syncthreads();
+    // ---- score table: LUT[code][j][r] = q~_r[8 j .. 8 j + 7] . C_k[code] --
+    // lane (j = lane mod 16) keeps its query slice in registers and fills
+    // codes 4 wave + lane / 16 + 32 i; the 16 lanes of a group write 16
+    // distinct bank quads.
+    {
+      const int j = lane & 15;
+      float qr[kRows][8];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const float4 a = *reinterpret_cast<const float4*>(qs + r * kD + 8 * j);
+        const float4 b = *reinterpret_cast<const float4*>(qs + r * kD + 8 * j + 4);
+        qr[r][0] = a.x; qr[r][1] = a.y; qr[r][2] = a.z; qr[r][3] = a.w;
+        qr[r][4] = b.x; qr[r][5] = b.y; qr[r][6] = b.z; qr[r][7] = b.w;
+      }
+      const float* cbk = reinterpret_cast<const float*>(lds + kCbk);
+#pragma unroll 2
+      for (int i = 0; i < 8; ++i) {
+        const int code = 4 * wave + grp16 + 32 * i;
+        const float4 a = *reinterpret_cast<const float4*>(cbk + 8 * code);
+        const float4 b = *reinterpret_cast<const float4*>(cbk + 8 * code + 4);
+        const float cv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        float v[kRows];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s = fmaf(qr[r][e], cv[e], s);
+          v[r] = s;
+        }
+        *reinterpret_cast<float4*>(lds + kLut + code * 256 + 16 * j) = make_float4(v[0], v[1], v[2], v[3]);
       }
     }
+    __syncthreads();
 
-    float th[kRows], mref[kRows];
+    float m[kRows], lsum[kRows], th[kRows], mref[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
       m[r] = -INFINITY; th[r] = -INFINITY; mref[r] = 0.f; lsum[r] = 0.f;
     }
-    acc0 = float4_t{0.f, 0.f, 0.f, 0.f};
-    acc1 = acc0;
+    float4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 
-    const size_t row_tok = (size_t)bg * p.S_cap;
-    const uint8_t* const kc_row = k_codes + row_tok * 16;
-    const uint8_t* const vc_row = v_codes + row_tok * 32 + 2 * (lane & 15);
-    const int tmax = p.S_cap - 1;
-
-    // codes of one block: the lane's key (16 bytes) and, for the value
-    // MFMA, the code pairs (2n, 2n+1) of keys 4 j + g, j = 0..15, kept as
-    // loaded (one per register) so that the prefetch of the next block is
-    // not waited for until that block is processed.  Load j of the wave
-    // reads keys 4 j .. 4 j + 3: one contiguous 128-byte span.
-    auto load_codes = [&](int tb, uint4& kc, uint32_t (&vr)[16]) {
-      kc = *reinterpret_cast<const uint4*>(kc_row + (size_t)min(tb + lane, tmax) * 16);
-      const int tv = tb + grp16;
-      if (tb + 64 <= p.S_cap) {
-        const uint16_t* vp = reinterpret_cast<const uint16_t*>(vc_row + (size_t)tv * 32);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) vr[k] = vp[64 * k];
-      } else {
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-          vr[k] = *reinterpret_cast<const uint16_t*>(vc_row + (size_t)min(tv + 4 * k, tmax) * 32);
-      }
-    };
-
-    // Software pipeline over 64-key blocks.  A block's key-row gathers and
-    // score MFMAs run while the previous block's value rows (gathered at the
+    // Software pipeline over the wave's 64-key blocks.  A block's score
+    // gathers run while the previous block's value rows (gathered at the
     // end of its own stage) go through the value MFMAs; the code buffers of
     // consecutive blocks alternate between two register sets, so the
     // prefetch of the next block is only waited for when it is used.
@@ -414,22 +429,23 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     };
 
     auto stage = [&](int tb, const uint4& kc, const uint32_t (&vr)[16], bool pending) {
-      // key rows: address = replica offset | code << 8
-      half8_t kv[16];
+      // ---- scores: 16 table rows of 4 fp32 (one per query row) -----------
+      float4_t L[16];
       {
         const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          kv[j] = lds_ld<half8_t>(
-              __builtin_amdgcn_perm(kw[j >> 2], kbase, 0x0c0c0000u | ((4u + (j & 3)) << 8)));
+        for (int a = 0; a < 4; ++a) {
+          const uint32_t dw = rdw == 0 ? kw[a]
+                            : (rdw == 1 ? kw[(a + 1) & 3] : (rdw == 2 ? kw[(a + 2) & 3] : kw[(a + 3) & 3]));
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            L[4 * a + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw, jt[a], sel[b]));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if (pending) value_mfmas();
-
-      // ---- scores on the matrix cores ----------------------------------
-      float4_t sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
-      key_mfmas(std::make_integer_sequence<int, 16>{}, kv, Aq, sc0, sc1);
-      const float4_t sc = sc0 + sc1;
+      const float4_t sc = (((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]))) +
+                          (((L[8] + L[9]) + (L[10] + L[11])) + ((L[12] + L[13]) + (L[14] + L[15])));
 
       // ---- masks and lazy online softmax -------------------------------
       float s[kRows] = {sc[0], sc[1], sc[2], sc[3]};
@@ -458,18 +474,23 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         acc0 *= a;
         acc1 *= a;
       }
-      float pr[kRows];
+      // p rounded to nearest fp16; the row sums take the rounded values, so
+      // the weights and their normalizer agree
+      uint32_t p01, p23;
+      {
+        float pr[kRows];
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(s[r] - mref[r]);
-        lsum[r] += pr[r];
+        for (int r = 0; r < kRows; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] - mref[r]);
+        p01 = pack_half2(pr[0], pr[1]);
+        p23 = pack_half2(pr[2], pr[3]);
+        const float2 f01 = __half22float2(*reinterpret_cast<const __half2*>(&p01));
+        const float2 f23 = __half22float2(*reinterpret_cast<const __half2*>(&p23));
+        lsum[0] += f01.x; lsum[1] += f01.y; lsum[2] += f23.x; lsum[3] += f23.y;
       }
 
       // ---- p to the value operand layout through LDS -------------------
       wave_sync_lds();
       {
-        const uint32_t p01 = pack_half2_rtz(pr[0], pr[1]);
-        const uint32_t p23 = pack_half2_rtz(pr[2], pr[3]);
         // key 4 q + g is staged at position 16 g + q, so that lane group g
         // finds its keys 4 q + g (q = 0..15) contiguous
         uint8_t* const pw = ps + 2 * (16 * (lane & 3) + (lane >> 2));
@@ -484,7 +505,6 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       pp[0] = P0.x; pp[1] = P0.y; pp[2] = P0.z; pp[3] = P0.w;
       pp[4] = P1.x; pp[5] = P1.y; pp[6] = P1.z; pp[7] = P1.w;
 
-
       // ---- this block's value rows, consumed by the next stage ---------
       // rows of key pair k: [key 0 sub 2n, key 1 sub 2n, key 0 sub 2n+1, key 1 sub 2n+1]
 #pragma unroll
@@ -498,111 +518,64 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       }
     };
 
-    uint4 kcA, kcB;
-    uint32_t vrA[16], vrB[16];
-    load_codes(t0, kcA, vrA);
-    for (int tb = t0;;) {
-      if (tb + 64 < t1) load_codes(tb + 64, kcB, vrB);
-      stage(tb, kcA, vrA, tb != t0);
-      tb += 64;
-      if (tb >= t1) break;
-      if (tb + 64 < t1) load_codes(tb + 64, kcA, vrA);
-      stage(tb, kcB, vrB, true);
-      tb += 64;
-      if (tb >= t1) break;
-    }
-    value_mfmas();
-
-    pos = seg_end;
-    if (pos >= end) {
-      u_last = u;
-      break;
-    }
-    // ---- partial of (chunk c, unit u), not the chunk's last one ----------
-    {
-      float* sp = part + (size_t)(c + u) * kSlot;
-      const int r = lane >> 4, n = lane & 15;
-      *reinterpret_cast<float4*>(sp + r * kD + 8 * n) = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
-      *reinterpret_cast<float4*>(sp + r * kD + 8 * n + 4) =
-          make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
-      float l[kRows];
-#pragma unroll
-      for (int rr = 0; rr < kRows; ++rr) l[rr] = wave_sum(lsum[rr]);
-      if (lane < kRows) {
-        const float mm = lane == 0 ? m[0] : (lane == 1 ? m[1] : (lane == 2 ? m[2] : m[3]));
-        const float ll = lane == 0 ? l[0] : (lane == 1 ? l[1] : (lane == 2 ? l[2] : l[3]));
-        sp[kRows * kD + lane] = mm;
-        sp[kRows * kD + kRows + lane] = ll;
+    if (tb_first < t1) {
+      for (int tb = tb_first;;) {
+        if (tb + kW * 64 < t1) load_codes(tb + kW * 64, kcB, vrB);
+        stage(tb, kcA, vrA, tb != tb_first);
+        tb += kW * 64;
+        if (tb >= t1) break;
+        if (tb + kW * 64 < t1) load_codes(tb + kW * 64, kcA, vrA);
+        stage(tb, kcB, vrB, true);
+        tb += kW * 64;
+        if (tb >= t1) break;
       }
+      value_mfmas();
     }
-    ++u;
-    while (pre[u + 1] == pre[u]) ++u;  // skip empty units (pos < T, so one follows)
-  }
-  }
 
-  // ---- combine the last partials of the workgroup's waves per unit -------
-  // Consecutive waves hold consecutive chunks, so the waves whose last unit
-  // is the same form one run; the run's first wave writes the combined
-  // partial into its slot and marks the others' slots empty.
-  __syncthreads();  // the codebook tables are no longer read
-  float* red = reinterpret_cast<float*>(lds + kKeyTab);  // [kW][kSlot]
-  int* ul = reinterpret_cast<int*>(lds + kScan);
-  {
-    const int r = lane >> 4, n = lane & 15;
-    float* sp = red + wave * kSlot;
+    // ---- combine the waves' partials of the segment into slot c + u -------
     float l[kRows];
 #pragma unroll
-    for (int rr = 0; rr < kRows; ++rr) l[rr] = wave_sum(lsum[rr]);
-    if (u_last >= 0) {
+    for (int r = 0; r < kRows; ++r) l[r] = wave_sum(lsum[r]);
+    __syncthreads();  // every wave is done with the table
+    {
+      float* sp = red + wave * kSlot;
+      const int r = lane >> 4, n = lane & 15;
       *reinterpret_cast<float4*>(sp + r * kD + 8 * n) = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
-      *reinterpret_cast<float4*>(sp + r * kD + 8 * n + 4) =
-          make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+      *reinterpret_cast<float4*>(sp + r * kD + 8 * n + 4) = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
       if (lane < kRows) {
         sp[kRows * kD + lane] = lane == 0 ? m[0] : (lane == 1 ? m[1] : (lane == 2 ? m[2] : m[3]));
         sp[kRows * kD + kRows + lane] = lane == 0 ? l[0] : (lane == 1 ? l[1] : (lane == 2 ? l[2] : l[3]));
       }
     }
-    if (lane == 0) ul[wave] = u_last;
-  }
-  __syncthreads();
-  {
-    const int uw = ul[wave];
-    if (uw >= 0 && (wave == 0 || ul[wave - 1] != uw)) {
-      int wb = wave;
-      while (wb + 1 < kW && ul[wb + 1] == uw) ++wb;
-      const int r = lane >> 4, n = lane & 15;
+    __syncthreads();
+    {
+      // thread -> (row r, dim d)
+      const int r = tid >> 7, d = tid & (kD - 1);
       float M = -INFINITY;
-      for (int i = wave; i <= wb; ++i) M = fmaxf(M, red[i * kSlot + kRows * kD + r]);
-      float L = 0.f;
-      float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) M = fmaxf(M, red[w * kSlot + kRows * kD + r]);
+      float Ls = 0.f, A = 0.f;
       if (M != -INFINITY) {
-        for (int i = wave; i <= wb; ++i) {
-          const float* sp = red + i * kSlot;
-          const float mi = sp[kRows * kD + r];
-          if (mi == -INFINITY) continue;
-          const float w = __builtin_amdgcn_exp2f(mi - M);
-          L += w * sp[kRows * kD + kRows + r];
-          const float4 x0 = *reinterpret_cast<const float4*>(sp + r * kD + 8 * n);
-          const float4 x1 = *reinterpret_cast<const float4*>(sp + r * kD + 8 * n + 4);
-          a0.x += w * x0.x; a0.y += w * x0.y; a0.z += w * x0.z; a0.w += w * x0.w;
-          a1.x += w * x1.x; a1.y += w * x1.y; a1.z += w * x1.z; a1.w += w * x1.w;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) {
+          const float mw = red[w * kSlot + kRows * kD + r];
+          const float sw = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+          Ls += sw * red[w * kSlot + kRows * kD + kRows + r];
+          A += sw * red[w * kSlot + r * kD + d];
         }
       }
-      float* gp = part + (size_t)(c + uw) * kSlot;
-      *reinterpret_cast<float4*>(gp + r * kD + 8 * n) = a0;
-      *reinterpret_cast<float4*>(gp + r * kD + 8 * n + 4) = a1;
-      if (n == 0) {
+      float* gp = part + (size_t)(c + u) * kSlot;
+      gp[r * kD + d] = A;
+      if (d == 0) {
         gp[kRows * kD + r] = M;
-        gp[kRows * kD + kRows + r] = L;
-      }
-      for (int i = wave + 1; i <= wb; ++i) {
-        float* ep = part + (size_t)(blockIdx.x * kW + i + uw) * kSlot;
-        if (lane < kRows) {
-          ep[kRows * kD + lane] = -INFINITY;
-          ep[kRows * kD + kRows + lane] = 0.f;
-        }
+        gp[kRows * kD + kRows + r] = Ls;
       }
     }
+
+    pos = seg_end;
+    if (pos >= end) break;
+    ++u;
+    while (pre[u + 1] == pre[u]) ++u;  // skip empty units (pos < T, so one follows)
   }
 }
 
@@ -702,7 +675,7 @@ bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, i
   if (U * max_range < (1LL << 18)) return false;
   if (sp) {
     sp->B = B; sp->Hq = Hq; sp->Sq = Sq; sp->Hkv = Hkv; sp->S_cap = S_cap; sp->n_c = n_c;
-    sp->G = (int)G; sp->GS = (int)GS; sp->n_rg = (int)n_rg; sp->U = (int)U; sp->cmin = 256;
+    sp->G = (int)G; sp->GS = (int)GS; sp->n_rg = (int)n_rg; sp->U = (int)U; sp->cmin = kW * 64;
   }
   if (lds_bytes) *lds_bytes = (kPrefix + (size_t)(U + 1) * 4 + 15) / 16 * 16;
   if (ws_bytes) *ws_bytes = stream_workspace_bytes(B, Hq, Sq, D, Hkv);
@@ -714,13 +687,13 @@ size_t stream_workspace_bytes(int B, int Hq, int Sq, int D, int Hkv) {
   const long long G = Hq / Hkv, GS = G * Sq, n_rg = (GS + kRows - 1) / kRows;
   const long long U = (long long)B * Hkv * n_rg;
   const size_t header = ((size_t)(U + 2) * 4 + 255) / 256 * 256;
-  return header + (size_t)(kMaxWaves + U) * kSlot * sizeof(float);
+  return header + (size_t)(kMaxChunks + U) * kSlot * sizeof(float);
 }
 
 hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds, hipStream_t st) {
   const int cus = cached_cu_count();
   if (cus <= 0) return hipErrorInvalidDevice;
-  const int grid = cus < kMaxWaves / kW ? cus : kMaxWaves / kW;
+  const int grid = cus < kMaxChunks ? cus : kMaxChunks;
   sp.smooth_rows = a.smooth_rows;
   sp.transform = a.transform;
   sp.causal = a.causal;
