@@ -17,10 +17,13 @@
 // ragged lengths and masks cost no imbalance.  The unit prefix is computed
 // on the device from kv_lens by every workgroup.  The workgroup walks its
 // chunk one unit segment at a time: it builds the unit's score table in
-// LDS, its 8 waves take the segment's 64-key blocks in turn, and the waves'
-// partials (m, l, acc) are combined in LDS into slot c + u of (chunk c,
-// unit u) (distinct for all overlapping pairs since chunks and units are
-// both ordered).  The merge kernel combines the slots of each unit.
+// LDS, its 8 waves claim the segment's 64-key blocks from an LDS counter,
+// and the waves' partials (m, l, acc) are combined in LDS into slot c + u
+// of (chunk c, unit u) (distinct for all overlapping pairs since chunks and
+// units are both ordered).  The merge kernel combines the slots of each
+// unit.  While the waves stream a segment, wave 0 writes the query rows of
+// the chunk's next unit into a second LDS buffer, so the next table build
+// does not wait on global memory.
 //
 // LDS holds the score table LUT[code][j][row] (fp32, 256 B per code, 64 KiB)
 // and the value codebook as fp16 rows replicated 32 times ([code][replica][4
@@ -46,6 +49,7 @@
 #include "vq_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace vq {
 namespace {
@@ -60,19 +64,26 @@ constexpr uint32_t kValTab = 65536;    // [256][32][4] fp16
 constexpr uint32_t kPStage = 131072;   // [wave][row][72] fp16
 constexpr uint32_t kPRow = 144;        // bytes per staged row (64 fp16 + pad)
 constexpr uint32_t kPWave = kRows * kPRow;
-constexpr uint32_t kQs = kPStage + kW * kPWave;  // [row][128] fp32 query rows
-constexpr uint32_t kCbk = kQs + kRows * kD * 4;  // [256][8] fp32 key codebook
+constexpr uint32_t kQs = kPStage + kW * kPWave;  // [2][row][128] fp32 query rows
+constexpr uint32_t kCbk = kQs + 2 * kRows * kD * 4;  // [256][8] fp32 key codebook
 constexpr uint32_t kScan = kCbk + 256 * 8 * 4;
-constexpr uint32_t kPrefix = kScan + 64;  // int prefix[U + 1]
+constexpr int kMaxUnits = 1791;        // units whose prefix fits in LDS (and B <= U)
+constexpr uint32_t kLens = kScan + 64;  // int lens[B], clamped to [0, S_cap]
+constexpr uint32_t kPrefix = kLens + 4 * (kMaxUnits + 1);  // int prefix[U + 1]
 constexpr float kLazyMargin = 8.f;
-constexpr int kMaxUnits = 4095;        // units whose prefix fits in LDS
 constexpr int kUnitsPerThread = (kMaxUnits + kThreads) / kThreads;
-constexpr int kMaxChunks = 4096;      // partial slots reserved for chunks (>= workgroups)
+constexpr int kMaxChunks = 4096;       // partial slots reserved for chunks (>= workgroups)
+static_assert(kUnitsPerThread * kThreads >= kMaxUnits + 1, "prefix coverage");
 static_assert(kPrefix + 4 * (kMaxUnits + 1) <= 160 * 1024, "LDS budget");
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw buffer descriptor (gfx9 family): 32-bit data format, so
+// that untyped loads are range checked against num_records.
+constexpr int kBufWord3 = 0x00020000;
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -106,18 +117,12 @@ __device__ __forceinline__ T lds_ld(uint32_t addr) {
       reinterpret_cast<const lds_byte*>((size_t)addr));
 }
 
-__device__ __forceinline__ int kv_len(const StreamParams& p, const int32_t* kv_lens, int b) {
-  if (!kv_lens) return p.S_cap;
-  const int v = kv_lens[b];
-  return v < 0 ? 0 : (v > p.S_cap ? p.S_cap : v);
-}
-
 // Valid key range [lo, hi) of query row rho (clamped to the rows that exist)
 // in a batch row of len keys: the causal and sliding-window masks.
 __device__ __forceinline__ void row_range(const StreamParams& p, int len, int rho, int& lo,
                                           int& hi) {
   rho = rho < p.GS ? rho : p.GS - 1;
-  const int qa = len - p.Sq + rho / p.G;
+  const int qa = len - p.Sq + (int)fast_div((uint32_t)rho, p.div_g);
   int h = p.causal ? (qa + 1 < len ? qa + 1 : len) : len;
   int l = p.window > 0 ? qa - p.window + 1 : 0;
   h = h > 0 ? h : 0;
@@ -126,17 +131,22 @@ __device__ __forceinline__ void row_range(const StreamParams& p, int len, int rh
   hi = h > l ? h : l;
 }
 
+// unit u -> (b * H_kv + g, row group, batch row b)
+__device__ __forceinline__ void unit_coords(const StreamParams& p, int u, int& bg, int& rg, int& b) {
+  bg = (int)fast_div((uint32_t)u, p.div_nrg);
+  rg = u - bg * p.n_rg;
+  b = (int)fast_div((uint32_t)bg, p.div_hkv);
+}
+
 // Keys of unit u: from the first row's lower bound to the last row's upper
 // bound (both are nondecreasing in rho).
-__device__ __forceinline__ int unit_len(const StreamParams& p, const int32_t* kv_lens, int u,
-                                        int* lo_out) {
-  const int rg = u % p.n_rg;
-  const int b = u / (p.n_rg * p.Hkv);
-  const int len = kv_len(p, kv_lens, b);
+__device__ __forceinline__ int unit_len(const StreamParams& p, const int* lens, int u) {
+  int bg, rg, b;
+  unit_coords(p, u, bg, rg, b);
+  const int len = lens[b];
   int lo0, hi0, lo3, hi3;
   row_range(p, len, 4 * rg, lo0, hi0);
   row_range(p, len, 4 * rg + 3, lo3, hi3);
-  if (lo_out) *lo_out = lo0;
   return hi3 > lo0 ? hi3 - lo0 : 0;
 }
 
@@ -151,32 +161,53 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- codebooks into LDS: keys as fp32 rows, values as replicated fp16 ---
+  // ---- global reads first: codebooks and kv lengths, then LDS tables -----
   {
-    float* cbk = reinterpret_cast<float*>(lds + kCbk);
-    for (int i = tid; i < 256 * 8; i += kThreads) cbk[i] = i < p.n_c * 8 ? k_codebook[i] : 0.f;
-    // four threads per code: each writes a quarter of the code's replicas
-    for (int code = tid >> 2; code < 256; code += kThreads / 4) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (code < p.n_c) v = reinterpret_cast<const float4*>(v_codebook)[code];
-      const uint2 hv = make_uint2(pack_half2(v.x, v.y), pack_half2(v.z, v.w));
-      const int s0 = (tid & 3) * 8;
+    // key codebook: one float4 per thread; value codebook: two threads per
+    // code, each writing 16 of its 32 replicas
+    float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), vq = kq;
+    if ((tid >> 1) < p.n_c) {
+      kq = reinterpret_cast<const float4*>(k_codebook)[tid];
+      vq = reinterpret_cast<const float4*>(v_codebook)[tid >> 1];
+    }
+    int lv[kUnitsPerThread];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        *reinterpret_cast<uint2*>(lds + kValTab + code * 256 + (s0 + k) * 8) = hv;
+    for (int k = 0; k < kUnitsPerThread; ++k) {
+      const int b = tid + kThreads * k;
+      lv[k] = b < p.B ? (kv_lens ? kv_lens[b] : p.S_cap) : 0;
+    }
+    *reinterpret_cast<float4*>(lds + kCbk + 16 * tid) = kq;
+    const uint32_t h0 = pack_half2(vq.x, vq.y), h1 = pack_half2(vq.z, vq.w);
+    const uint4 two = make_uint4(h0, h1, h0, h1);
+    const int code = tid >> 1;
+    // rotated by code so that the 16 lanes of a write hit distinct bank quads
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint4*>(lds + kValTab + code * 256 + (tid & 1) * 128 + 16 * ((i + code) & 7)) = two;
+    int* lens = reinterpret_cast<int*>(lds + kLens);
+#pragma unroll
+    for (int k = 0; k < kUnitsPerThread; ++k) {
+      const int b = tid + kThreads * k;
+      if (b < p.B) lens[b] = lv[k] < 0 ? 0 : (lv[k] > p.S_cap ? p.S_cap : lv[k]);
     }
   }
+  __syncthreads();
+  const int* const lens = reinterpret_cast<const int*>(lds + kLens);
 
-  // ---- unit prefix (exclusive) over the U <= kMaxUnits units --------------
-  int* pre = reinterpret_cast<int*>(lds + kPrefix);
-  int* scan = reinterpret_cast<int*>(lds + kScan);
+  // ---- unit prefix (exclusive) over the U <= kMaxUnits units, the chunk
+  // and the unit holding its first key -------------------------------------
+  int* const pre = reinterpret_cast<int*>(lds + kPrefix);
+  int* const scan = reinterpret_cast<int*>(lds + kScan);
+  int* const first_unit = scan + kW + 2;
+  const int c = blockIdx.x;
+  int T, C, start;
   {
-    int loc[kUnitsPerThread], sum = 0;
+    int n[kUnitsPerThread], sum = 0;
 #pragma unroll
     for (int k = 0; k < kUnitsPerThread; ++k) {
       const int u = kUnitsPerThread * tid + k;
-      loc[k] = sum;
-      sum += u < p.U ? unit_len(p, kv_lens, u, nullptr) : 0;
+      n[k] = u < p.U ? unit_len(p, lens, u) : 0;
+      sum += n[k];
     }
     int incl = sum;
 #pragma unroll
@@ -186,43 +217,34 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     }
     if (lane == 63) scan[wave] = incl;
     __syncthreads();
-    int off = 0, total = 0;
+    int off = 0;
+    T = 0;
 #pragma unroll
     for (int w = 0; w < kW; ++w) {
       const int s = scan[w];
       off += w < wave ? s : 0;
-      total += s;
+      T += s;
     }
-    const int excl = off + incl - sum;
+    C = max(p.cmin, (T + (int)gridDim.x - 1) / (int)gridDim.x);
+    start = c * C;  // T <= U * S_cap < 2^30 is checked on the host
+    int pu = off + incl - sum;
 #pragma unroll
     for (int k = 0; k < kUnitsPerThread; ++k) {
       const int u = kUnitsPerThread * tid + k;
-      if (u < p.U) pre[u] = excl + loc[k];
+      if (u < p.U) pre[u] = pu;
+      if (n[k] > 0 && pu <= start && start < pu + n[k]) *first_unit = u;
+      pu += n[k];
     }
-    if (tid == 0) pre[p.U] = total;
+    if (tid == 0) pre[p.U] = T;
     __syncthreads();
   }
-  const int T = pre[p.U];
-  const int C = max(p.cmin, (T + (int)gridDim.x - 1) / (int)gridDim.x);
   if (blockIdx.x == 0) {
     for (int u = tid; u <= p.U; u += kThreads) header[1 + u] = pre[u];
     if (tid == 0) header[0] = C;
   }
-  const int c = blockIdx.x;
-  const int start = c * C;  // T <= U * S_cap < 2^30 is checked on the host
   const int end = min(T, start + C);
   if (start >= T) return;
-
-  // unit holding token position `start`: the largest u with pre[u] <= start
-  int u = 0;
-  {
-    int lo = 0, hi = p.U - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= start) lo = mid; else hi = mid - 1;
-    }
-    u = lo;
-  }
+  int u = *first_unit;
 
   // ---- lane constants ------------------------------------------------------
   // Score gathers: at step k = 4 a + b the lane reads sub-vector
@@ -232,6 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   // four byte offsets 16 j of steps (a, b), sel[b] the v_perm selector that
   // places the code byte of sub-vector j above that offset.
   const int rdw = (lane >> 2) & 3, rb = lane & 3;
+  const uint32_t rot1 = (rdw & 1) ? ~0u : 0u, rot2 = (rdw & 2) ? ~0u : 0u;
   uint32_t jt[4], sel[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -252,20 +275,76 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   const uint32_t sa2 = e_a == 0 ? 0x0c0c0302u : (e_a == 1 ? 0x03020c0cu : 0x0c0c0c0cu);
   const uint32_t sa3 = e_a == 2 ? 0x0c0c0302u : (e_a == 3 ? 0x03020c0cu : 0x0c0c0c0cu);
   uint8_t* const ps = lds + kPStage + wave * kPWave;
-  float* const qs = reinterpret_cast<float*>(lds + kQs);
   float* const red = reinterpret_cast<float*>(lds + kLut);  // [kW][kSlot], over the table
-  const int tmax = p.S_cap - 1;
+  int* const claim_ctr = scan + kW;
+
+  // Query rows of unit uq: dual transform, scaled, into LDS buffer qbuf
+  // (run by wave 0).  Lane (bq = lane / 4, row ir = lane % 4) holds dims
+  // 4 bq + e and 64 + 4 bq + e (e = 0..3) of row ir.
+  auto make_query = [&](int uq, int qbuf) {
+    int bgq, rgq, bq_b;
+    unit_coords(p, uq, bgq, rgq, bq_b);
+    const int gq = bgq - bq_b * p.Hkv;
+    const int bq = lane >> 2, ir = lane & 3;
+    const int rho = 4 * rgq + ir;
+    const int rc = rho < p.GS ? rho : p.GS - 1;
+    const int ip = (int)fast_div((uint32_t)rc, p.div_g);
+    const int h = gq * p.G + rc - ip * p.G;
+    const __half* qp = q + ((size_t)(bq_b * p.Hq + h) * p.Sq + ip) * kD;
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint2 w = *reinterpret_cast<const uint2*>(qp + 64 * k + 4 * bq);
+      const float2 f0 = __half22float2(*reinterpret_cast<const __half2*>(&w.x));
+      const float2 f1 = __half22float2(*reinterpret_cast<const __half2*>(&w.y));
+      x[4 * k] = f0.x; x[4 * k + 1] = f0.y; x[4 * k + 2] = f1.x; x[4 * k + 3] = f1.y;
+    }
+    if (smooth) {
+      const float* sp = smooth + (p.smooth_rows == 1 ? 0 : gq) * kD;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float4 s = *reinterpret_cast<const float4*>(sp + 64 * k + 4 * bq);
+        x[4 * k] *= s.x; x[4 * k + 1] *= s.y; x[4 * k + 2] *= s.z; x[4 * k + 3] *= s.w;
+      }
+    }
+    if (p.transform) {
+      // in-register index bits 0, 1 (dims 0, 1) and 2 (dim bit 6)
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i & m) continue;
+          const float a = x[i], b = x[i + m];
+          x[i] = a + b;
+          x[i + m] = a - b;
+        }
+      }
+      // dim bits 2..5 are lane bits 2..5
+#pragma unroll
+      for (int m = 4; m < 64; m <<= 1) {
+        const float sg = (lane & m) ? -1.f : 1.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = fmaf(sg, x[i], __shfl_xor(x[i], m));
+      }
+    }
+    const float f = rho < p.GS ? p.fold : 0.f;
+    float* const qd = reinterpret_cast<float*>(lds + kQs) + qbuf * kRows * kD;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      *reinterpret_cast<float4*>(qd + ir * kD + 64 * k + 4 * bq) =
+          make_float4(x[4 * k] * f, x[4 * k + 1] * f, x[4 * k + 2] * f, x[4 * k + 3] * f);
+  };
 
   int pos = start;
+  int qbuf = 0;          // query buffer of the current unit
+  bool q_ready = false;  // its rows were written during the previous segment
   while (true) {
-    // ---- segment: unit u, token positions [pos, seg_end) ----------------
+    // ---- segment: unit u, chunk positions [pos, seg_end) ----------------
     const int Pu = pre[u], Pn = pre[u + 1];
     const int seg_end = min(end, Pn);
-    const int rg = u % p.n_rg;
-    const int bg = u / p.n_rg;
-    const int g = bg % p.Hkv;
-    const int bb = bg / p.Hkv;
-    const int len = kv_len(p, kv_lens, bb);
+    int bg, rg, bb;
+    unit_coords(p, u, bg, rg, bb);
+    const int len = lens[bb];
     int klo[kRows], khi[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) row_range(p, len, 4 * rg + r, klo[r], khi[r]);
@@ -279,10 +358,20 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       full_lo = max(full_lo, klo[r]);
       full_hi = min(full_hi, khi[r]);
     }
+    // next nonempty unit of the chunk, if any
+    int u_next = -1;
+    if (seg_end < end) {
+      u_next = u + 1;
+      while (pre[u_next + 1] == pre[u_next]) ++u_next;  // pos < T, so one follows
+    }
 
+    // code rows of (b, g) behind bounds-checked buffer descriptors: loads of
+    // keys at or past S_cap return zeros (those keys are always masked)
     const size_t row_tok = (size_t)bg * p.S_cap;
-    const uint8_t* const kc_row = k_codes + row_tok * 16;
-    const uint8_t* const vc_row = v_codes + row_tok * 32 + 2 * (lane & 15);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(k_codes + row_tok * 16), (short)0, p.S_cap * 16, kBufWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(v_codes + row_tok * 32), (short)0, p.S_cap * 32, kBufWord3);
 
     // codes of one block: the lane's key (16 bytes) and, for the value
     // MFMA, the code pairs (2n, 2n+1) of keys 4 j + g, j = 0..15, kept as
@@ -290,112 +379,78 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // not waited for until that block is processed.  Load j of the wave
     // reads keys 4 j .. 4 j + 3: one contiguous 128-byte span.
     auto load_codes = [&](int tb, uint4& kc, uint32_t (&vr)[16]) {
-      kc = *reinterpret_cast<const uint4*>(kc_row + (size_t)min(tb + lane, tmax) * 16);
-      const int tv = tb + grp16;
-      if (tb + 64 <= p.S_cap) {
-        const uint16_t* vp = reinterpret_cast<const uint16_t*>(vc_row + (size_t)tv * 32);
+      const u32x4_t k4 = __builtin_amdgcn_raw_buffer_load_b128(krs, (uint32_t)(tb + lane) * 16u, 0, 0);
+      kc = make_uint4(k4[0], k4[1], k4[2], k4[3]);
+      const uint32_t vo = (uint32_t)(tb + grp16) * 32u + 2u * (uint32_t)(lane & 15);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) vr[k] = vp[64 * k];
-      } else {
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-          vr[k] = *reinterpret_cast<const uint16_t*>(vc_row + (size_t)min(tv + 4 * k, tmax) * 32);
-      }
+      for (int k = 0; k < 16; ++k) vr[k] = __builtin_amdgcn_raw_buffer_load_b16(vrs, vo + 128u * k, 0, 0);
     };
 
-    // the wave's blocks of the segment: t0 + 64 (wave + kW i); the first
-    // one's codes load while the table is built
-    const int tb_first = t0 + 64 * wave;
-    uint4 kcA, kcB;
-    uint32_t vrA[16], vrB[16];
-    if (tb_first < t1) load_codes(tb_first, kcA, vrA);
-
-    __syncthreads();  // the previous segment's combine has read the table area
-    // ---- query rows of the unit: dual transform, scaled, into LDS ---------
-    if (wave == 0) {
-      // lane (bq = lane / 4, row ir = lane % 4) holds dims 4 bq + e and
-      // 64 + 4 bq + e (e = 0..3) of row ir
-      const int bq = lane >> 2, ir = lane & 3;
-      const int rho = 4 * rg + ir;
-      const int rc = rho < p.GS ? rho : p.GS - 1;
-      const int h = g * p.G + rc % p.G;
-      const __half* qp = q + ((size_t)(bb * p.Hq + h) * p.Sq + rc / p.G) * kD;
-      float x[8];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint2 w = *reinterpret_cast<const uint2*>(qp + 64 * k + 4 * bq);
-        const float2 f0 = __half22float2(*reinterpret_cast<const __half2*>(&w.x));
-        const float2 f1 = __half22float2(*reinterpret_cast<const __half2*>(&w.y));
-        x[4 * k] = f0.x; x[4 * k + 1] = f0.y; x[4 * k + 2] = f1.x; x[4 * k + 3] = f1.y;
-      }
-      if (smooth) {
-        const float* sp = smooth + (p.smooth_rows == 1 ? 0 : g) * kD;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const float4 s = *reinterpret_cast<const float4*>(sp + 64 * k + 4 * bq);
-          x[4 * k] *= s.x; x[4 * k + 1] *= s.y; x[4 * k + 2] *= s.z; x[4 * k + 3] *= s.w;
-        }
-      }
-      if (p.transform) {
-        // in-register index bits 0, 1 (dims 0, 1) and 2 (dim bit 6)
-#pragma unroll
-        for (int m = 1; m < 8; m <<= 1) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            if (i & m) continue;
-            const float a = x[i], b = x[i + m];
-            x[i] = a + b;
-            x[i + m] = a - b;
-          }
-        }
-        // dim bits 2..5 are lane bits 2..5
-#pragma unroll
-        for (int m = 4; m < 64; m <<= 1) {
-          const float sg = (lane & m) ? -1.f : 1.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = fmaf(sg, x[i], __shfl_xor(x[i], m));
-        }
-      }
-      const float f = rho < p.GS ? p.fold : 0.f;
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        *reinterpret_cast<float4*>(qs + ir * kD + 64 * k + 4 * bq) =
-            make_float4(x[4 * k] * f, x[4 * k + 1] * f, x[4 * k + 2] * f, x[4 * k + 3] * f);
+    // Blocks of the segment are t0 + 64 n.  Wave w takes blocks w and
+    // w + kW, then claims the next free block from an LDS counter each time
+    // it issues a load, so waves that run ahead take more blocks.  Block i
+    // of a wave lives in code buffer i mod 3 and is loaded two blocks ahead,
+    // so two blocks are in flight while one is processed; the first two
+    // load while the table is built.  Loads for claims past the segment
+    // re-read block 0 (cache hits), so every step issues the same loads.
+    auto claim = [&]() {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(claim_ctr, 1);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    auto blk = [&](int n) {
+      const int tb = t0 + 64 * n;
+      return tb < t1 ? tb : t0;
+    };
+    int nA = wave, nB = wave + kW, nC = 0;
+    uint4 kcA, kcB, kcC;
+    uint32_t vrA[16], vrB[16], vrC[16];
+    if (t0 + 64 * nA < t1) {
+      load_codes(blk(nA), kcA, vrA);
+      load_codes(blk(nB), kcB, vrB);
     }
-    __syncthreads();
-    // ---- score table: LUT[code][j][r] = q~_r[8 j .. 8 j + 7] . C_k[code] --
-    // lane (j = lane mod 16) keeps its query slice in registers and fills
-    // codes 4 wave + lane / 16 + 32 i; the 16 lanes of a group write 16
-    // distinct bank quads.
+
+    if (!q_ready && wave == 0) make_query(u, qbuf);
+    if (tid == 0) *claim_ctr = 2 * kW;
+    __syncthreads();  // query rows ready; the previous combine has read the table area
     {
-      const int j = lane & 15;
-      float qr[kRows][8];
-#pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        const float4 a = *reinterpret_cast<const float4*>(qs + r * kD + 8 * j);
-        const float4 b = *reinterpret_cast<const float4*>(qs + r * kD + 8 * j + 4);
-        qr[r][0] = a.x; qr[r][1] = a.y; qr[r][2] = a.z; qr[r][3] = a.w;
-        qr[r][4] = b.x; qr[r][5] = b.y; qr[r][6] = b.z; qr[r][7] = b.w;
-      }
-      const float* cbk = reinterpret_cast<const float*>(lds + kCbk);
-#pragma unroll 2
-      for (int i = 0; i < 8; ++i) {
-        const int code = 4 * wave + grp16 + 32 * i;
-        const float4 a = *reinterpret_cast<const float4*>(cbk + 8 * code);
-        const float4 b = *reinterpret_cast<const float4*>(cbk + 8 * code + 4);
-        const float cv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        float v[kRows];
+      const float* const qcur = reinterpret_cast<const float*>(lds + kQs) + qbuf * kRows * kD;
+      // ---- score table: LUT[code][j][r] = q~_r[8 j .. 8 j + 7] . C_k[code] --
+      // lane (j = lane mod 16) keeps its query slice in registers and fills
+      // codes 4 wave + lane / 16 + 32 i; the 16 lanes of a group write 16
+      // distinct bank quads.
+      {
+        const int j = lane & 15;
+        float qr[kRows][8];
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s = fmaf(qr[r][e], cv[e], s);
-          v[r] = s;
+          const float4 a = *reinterpret_cast<const float4*>(qcur + r * kD + 8 * j);
+          const float4 b = *reinterpret_cast<const float4*>(qcur + r * kD + 8 * j + 4);
+          qr[r][0] = a.x; qr[r][1] = a.y; qr[r][2] = a.z; qr[r][3] = a.w;
+          qr[r][4] = b.x; qr[r][5] = b.y; qr[r][6] = b.z; qr[r][7] = b.w;
         }
-        *reinterpret_cast<float4*>(lds + kLut + code * 256 + 16 * j) = make_float4(v[0], v[1], v[2], v[3]);
+        const float* cbk = reinterpret_cast<const float*>(lds + kCbk);
+#pragma unroll 2
+        for (int i = 0; i < 8; ++i) {
+          const int code = 4 * wave + grp16 + 32 * i;
+          const float4 a = *reinterpret_cast<const float4*>(cbk + 8 * code);
+          const float4 b = *reinterpret_cast<const float4*>(cbk + 8 * code + 4);
+          const float cv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          float v[kRows];
+#pragma unroll
+          for (int r = 0; r < kRows; ++r) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = fmaf(qr[r][e], cv[e], s);
+            v[r] = s;
+          }
+          *reinterpret_cast<float4*>(lds + kLut + code * 256 + 16 * j) = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
     }
     __syncthreads();
+    // the next unit's query rows, written while the other waves stream
+    if (u_next >= 0 && wave == 0) make_query(u_next, qbuf ^ 1);
 
     float m[kRows], lsum[kRows], th[kRows], mref[kRows];
 #pragma unroll
@@ -412,9 +467,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     u32x2_t vg[8][4];  // value rows of the block whose value MFMAs are pending
     uint32_t pp[8];    // that block's p, staged into the A operand layout
 
-    auto value_mfmas = [&]() {
+    auto value_mfmas = [&](auto half) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 4 * decltype(half)::value; k < 4 * decltype(half)::value + 4; ++k) {
         const uint32_t x = pp[k];
         const uint4 au = make_uint4(__builtin_amdgcn_perm(0u, x, sa0), __builtin_amdgcn_perm(0u, x, sa1),
                                     __builtin_amdgcn_perm(0u, x, sa2), __builtin_amdgcn_perm(0u, x, sa3));
@@ -427,25 +482,40 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
                                                       0, 0, 0);
       }
     };
+    const std::integral_constant<int, 0> lo_half;
+    const std::integral_constant<int, 1> hi_half;
 
     auto stage = [&](int tb, const uint4& kc, const uint32_t (&vr)[16], bool pending) {
-      // ---- scores: 16 table rows of 4 fp32 (one per query row) -----------
-      float4_t L[16];
+      // ---- scores: 16 table rows of 4 fp32 (one per query row), in two
+      // halves, each overlapping half of the previous block's value MFMAs
+      float4_t sc;
       {
+        // dw[a] = kw[(a + rdw) mod 4]: rotate by rdw bit 0, then by bit 1,
+        // with bit selects (no divergent branches)
         const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+        uint32_t r1[4], dw[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const uint32_t dw = rdw == 0 ? kw[a]
-                            : (rdw == 1 ? kw[(a + 1) & 3] : (rdw == 2 ? kw[(a + 2) & 3] : kw[(a + 3) & 3]));
+        for (int a = 0; a < 4; ++a) r1[a] = (kw[(a + 1) & 3] & rot1) | (kw[a] & ~rot1);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) dw[a] = (r1[(a + 2) & 3] & rot2) | (r1[a] & ~rot2);
+        float4_t L[8];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int b = 0; b < 4; ++b)
-            L[4 * a + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw, jt[a], sel[b]));
-        }
+            L[4 * a + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw[a], jt[a], sel[b]));
+        __builtin_amdgcn_sched_barrier(0);
+        if (pending) value_mfmas(lo_half);
+        sc = ((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]));
+#pragma unroll
+        for (int a = 2; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            L[4 * (a - 2) + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw[a], jt[a], sel[b]));
+        __builtin_amdgcn_sched_barrier(0);
+        if (pending) value_mfmas(hi_half);
+        sc += ((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]));
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (pending) value_mfmas();
-      const float4_t sc = (((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]))) +
-                          (((L[8] + L[9]) + (L[10] + L[11])) + ((L[12] + L[13]) + (L[14] + L[15])));
 
       // ---- masks and lazy online softmax -------------------------------
       float s[kRows] = {sc[0], sc[1], sc[2], sc[3]};
@@ -518,18 +588,25 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       }
     };
 
-    if (tb_first < t1) {
-      for (int tb = tb_first;;) {
-        if (tb + kW * 64 < t1) load_codes(tb + kW * 64, kcB, vrB);
-        stage(tb, kcA, vrA, tb != tb_first);
-        tb += kW * 64;
-        if (tb >= t1) break;
-        if (tb + kW * 64 < t1) load_codes(tb + kW * 64, kcA, vrA);
-        stage(tb, kcB, vrB, true);
-        tb += kW * 64;
-        if (tb >= t1) break;
+    if (t0 + 64 * nA < t1) {
+      bool pending = false;
+      for (;;) {
+        nC = claim();
+        load_codes(blk(nC), kcC, vrC);
+        stage(t0 + 64 * nA, kcA, vrA, pending);
+        pending = true;
+        if (t0 + 64 * nB >= t1) break;
+        nA = claim();
+        load_codes(blk(nA), kcA, vrA);
+        stage(t0 + 64 * nB, kcB, vrB, true);
+        if (t0 + 64 * nC >= t1) break;
+        nB = claim();
+        load_codes(blk(nB), kcB, vrB);
+        stage(t0 + 64 * nC, kcC, vrC, true);
+        if (t0 + 64 * nA >= t1) break;
       }
-      value_mfmas();
+      value_mfmas(lo_half);
+      value_mfmas(hi_half);
     }
 
     // ---- combine the waves' partials of the segment into slot c + u -------
@@ -572,10 +649,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       }
     }
 
+
+    if (u_next < 0) break;
     pos = seg_end;
-    if (pos >= end) break;
-    ++u;
-    while (pre[u + 1] == pre[u]) ++u;  // skip empty units (pos < T, so one follows)
+    u = u_next;
+    qbuf ^= 1;
+    q_ready = true;
   }
 }
 
@@ -668,7 +747,7 @@ bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, i
   if (B <= 0 || Hq <= 0 || Sq <= 0 || Hkv <= 0 || S_cap <= 0 || Hq % Hkv) return false;
   const long long G = Hq / Hkv, GS = G * Sq, n_rg = (GS + kRows - 1) / kRows;
   const long long U = (long long)B * Hkv * n_rg;
-  if (U > kMaxUnits || U * (long long)S_cap >= (1LL << 30)) return false;
+  if (U > kMaxUnits || U * (long long)S_cap >= (1LL << 30) || S_cap >= (1 << 26)) return false;
   // the persistent grid's fixed cost (table fill, unit prefix, merge) only
   // pays off with enough keys: small problems go to the per-unit kernel
   const long long max_range = window > 0 ? std::min<long long>(S_cap, (long long)Sq + window - 1) : S_cap;
@@ -676,6 +755,9 @@ bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, i
   if (sp) {
     sp->B = B; sp->Hq = Hq; sp->Sq = Sq; sp->Hkv = Hkv; sp->S_cap = S_cap; sp->n_c = n_c;
     sp->G = (int)G; sp->GS = (int)GS; sp->n_rg = (int)n_rg; sp->U = (int)U; sp->cmin = kW * 64;
+    sp->div_g = make_fastdiv((uint32_t)G);
+    sp->div_nrg = make_fastdiv((uint32_t)n_rg);
+    sp->div_hkv = make_fastdiv((uint32_t)Hkv);
   }
   if (lds_bytes) *lds_bytes = (kPrefix + (size_t)(U + 1) * 4 + 15) / 16 * 16;
   if (ws_bytes) *ws_bytes = stream_workspace_bytes(B, Hq, Sq, D, Hkv);

@@ -79,10 +79,28 @@ bool attend_mfma_plan(int D, int dv, int nsk, int rows, int* R, size_t* lds_byte
 hipError_t launch_attend_mfma(const AttendArgs& a, const AttParams& p, size_t lds_bytes,
                               hipStream_t st);
 
+// Division of 0 <= n < 2^31 by a fixed divisor d >= 1 through a multiply
+// (the round-up method of Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994): q = (umulhi(n, mul) + n) >> shift
+// with shift = ceil(log2 d), mul = floor(2^32 (2^shift - d) / d) + 1.
+struct FastDiv {
+  uint32_t mul, shift;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+  return FastDiv{(uint32_t)m, s};
+}
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.mul) + n) >> f.shift;
+}
+
 // Persistent streaming kernel (head dim 128, key sub_dim 8, value sub_dim 4).
 struct StreamParams {
   int B, Hq, Sq, Hkv, S_cap, n_c, smooth_rows, transform, causal, window;
   int G, GS, n_rg, U, cmin;
+  FastDiv div_g, div_nrg, div_hkv;  // by G, n_rg and H_kv
   float fold;  // WHT normalization (if any) * scale * log2(e)
 };
 // True if the shape runs on the streaming kernel; fills its parameters, LDS
