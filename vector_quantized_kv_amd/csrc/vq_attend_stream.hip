@@ -73,10 +73,13 @@ constexpr uint32_t kPrefix = kLens + 4 * (kMaxUnits + 1);  // int prefix[U + 1]
 constexpr float kLazyMargin = 8.f;
 constexpr int kUnitsPerThread = (kMaxUnits + kThreads) / kThreads;
 constexpr int kMaxChunks = 4096;       // partial slots reserved for chunks (>= workgroups)
+constexpr int kQExp = kW + 4;          // int slots: exponents of the two query buffers
 static_assert(kUnitsPerThread * kThreads >= kMaxUnits + 1, "prefix coverage");
 static_assert(kPrefix + 4 * (kMaxUnits + 1) <= 160 * 1024, "LDS budget");
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -106,6 +109,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
   const __half2 h = __floats2half2_rn(a, b);
   return *reinterpret_cast<const uint32_t*>(&h);
+}
+
+// x * 2^sc split into fp16 parts: hi = fp16(x 2^sc), lo = fp16(x 2^sc - hi).
+__device__ __forceinline__ void split_f16(float4 x, int sc, half4_t& hi, half4_t& lo) {
+  const float v[4] = {ldexpf(x.x, sc), ldexpf(x.y, sc), ldexpf(x.z, sc), ldexpf(x.w, sc)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (_Float16)v[i];
+    lo[i] = (_Float16)(v[i] - (float)hi[i]);
+  }
+}
+
+// Exponent e with |m| in [2^(e-1), 2^e) for the largest magnitude m (0 for 0).
+__device__ __forceinline__ int mag_exp(float m) {
+  return m > 0.f ? __builtin_amdgcn_frexp_expf(m) : 0;
 }
 
 // LDS accesses by byte address.  The kernel declares no static LDS, so the
@@ -193,6 +211,18 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   }
   __syncthreads();
   const int* const lens = reinterpret_cast<const int*>(lds + kLens);
+  // magnitude exponent of the key codebook (every wave reads all of it)
+  int ecb;
+  {
+    const float* cbk = reinterpret_cast<const float*>(lds + kCbk);
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(cbk + 4 * (lane + 64 * i));
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    ecb = __builtin_amdgcn_readfirstlane(mag_exp(wave_max(mx)));
+  }
 
   // ---- unit prefix (exclusive) over the U <= kMaxUnits units, the chunk
   // and the unit holding its first key -------------------------------------
@@ -329,10 +359,18 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     }
     const float f = rho < p.GS ? p.fold : 0.f;
     float* const qd = reinterpret_cast<float*>(lds + kQs) + qbuf * kRows * kD;
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] *= f;
+      mx = fmaxf(mx, fabsf(x[i]));
+    }
 #pragma unroll
     for (int k = 0; k < 2; ++k)
       *reinterpret_cast<float4*>(qd + ir * kD + 64 * k + 4 * bq) =
-          make_float4(x[4 * k] * f, x[4 * k + 1] * f, x[4 * k + 2] * f, x[4 * k + 3] * f);
+          make_float4(x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3]);
+    mx = wave_max(mx);
+    if (lane == 0) scan[kQExp + qbuf] = mag_exp(mx);
   };
 
   int pos = start;
@@ -416,35 +454,35 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     {
       const float* const qcur = reinterpret_cast<const float*>(lds + kQs) + qbuf * kRows * kD;
       // ---- score table: LUT[code][j][r] = q~_r[8 j .. 8 j + 7] . C_k[code] --
-      // lane (j = lane mod 16) keeps its query slice in registers and fills
-      // codes 4 wave + lane / 16 + 32 i; the 16 lanes of a group write 16
-      // distinct bank quads.
+      // on the matrix cores: v_mfma_f32_32x32x8_f16 with M = 32 codes (wave
+      // w: codes 32 w ..), N = 32 (j, r) pairs (two tiles: j < 8, j >= 8),
+      // K = the 8 dims of a sub-vector.  Both operands are scaled by powers
+      // of two into [2^13, 2^14) and split into fp16 high and low parts; the
+      // products hi.hi + lo.hi + hi.lo carry the result to fp32 accuracy.
       {
-        const int j = lane & 15;
-        float qr[kRows][8];
-#pragma unroll
-        for (int r = 0; r < kRows; ++r) {
-          const float4 a = *reinterpret_cast<const float4*>(qcur + r * kD + 8 * j);
-          const float4 b = *reinterpret_cast<const float4*>(qcur + r * kD + 8 * j + 4);
-          qr[r][0] = a.x; qr[r][1] = a.y; qr[r][2] = a.z; qr[r][3] = a.w;
-          qr[r][4] = b.x; qr[r][5] = b.y; qr[r][6] = b.z; qr[r][7] = b.w;
-        }
+        const int l32 = lane & 31, kh = lane >> 5;
+        const int eq = scan[kQExp + qbuf];
         const float* cbk = reinterpret_cast<const float*>(lds + kCbk);
-#pragma unroll 2
-        for (int i = 0; i < 8; ++i) {
-          const int code = 4 * wave + grp16 + 32 * i;
-          const float4 a = *reinterpret_cast<const float4*>(cbk + 8 * code);
-          const float4 b = *reinterpret_cast<const float4*>(cbk + 8 * code + 4);
-          const float cv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          float v[kRows];
+        const float4 a = *reinterpret_cast<const float4*>(cbk + 8 * (32 * wave + l32) + 4 * kh);
+        half4_t ahi, alo;
+        split_f16(a, 14 - ecb, ahi, alo);
+        const int unscale = ecb + eq - 28;
 #pragma unroll
-          for (int r = 0; r < kRows; ++r) {
-            float s = 0.f;
+        for (int t2 = 0; t2 < 2; ++t2) {
+          // column n = l32: sub-vector j = 8 t2 + n / 4, row r = n % 4
+          const float4 b = *reinterpret_cast<const float4*>(qcur + (l32 & 3) * kD + 8 * (8 * t2 + (l32 >> 2)) + 4 * kh);
+          half4_t bhi, blo;
+          split_f16(b, 14 - eq, bhi, blo);
+          float16_t d = {};
+          d = __builtin_amdgcn_mfma_f32_32x32x8f16(ahi, bhi, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_32x32x8f16(alo, bhi, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_32x32x8f16(ahi, blo, d, 0, 0, 0);
+          // element v: code 32 w + 8 (v / 4) + 4 kh + v % 4, column l32
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s = fmaf(qr[r][e], cv[e], s);
-            v[r] = s;
+          for (int v = 0; v < 16; ++v) {
+            const int code = 32 * wave + 8 * (v >> 2) + 4 * kh + (v & 3);
+            *reinterpret_cast<float*>(lds + kLut + code * 256 + 128 * t2 + 4 * l32) = ldexpf(d[v], unscale);
           }
-          *reinterpret_cast<float4*>(lds + kLut + code * 256 + 16 * j) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -681,45 +719,36 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const int* __restrict
   if (Pn > Pu) {
     const int c_lo = Pu / C, n_part = (Pn - 1) / C - c_lo + 1;
     const float* base = part + (size_t)(c_lo + u) * kSlot;
-    // maxima of all partials, one lane per partial
+    // up to 8 partials per round: their (m, l) and the lane's two
+    // accumulator values load together, then fold into the running sums
     float M = -INFINITY;
-    for (int j = lane; j < n_part; j += 64) M = fmaxf(M, base[(size_t)j * kSlot + kRows * kD + r]);
-    M = wave_max(M);
-    if (M != -INFINITY) {
-      float Ls = 0.f;
-      for (int j0 = 0; j0 < n_part; j0 += 64) {
-        const int j = j0 + lane;
-        const float mj = j < n_part ? base[(size_t)j * kSlot + kRows * kD + r] : -INFINITY;
-        const bool ok = mj != -INFINITY;
-        const float wj = ok ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
-        if (ok) Ls += wj * base[(size_t)j * kSlot + kRows * kD + kRows + r];
-        // the few nonempty partials: four loads in flight at a time
-        uint64_t mask = __builtin_amdgcn_ballot_w64(ok);
-        while (mask) {
-          int idx[4];
-          float w[4];
+    for (int j0 = 0; j0 < n_part; j0 += 8) {
+      float mj[8], lj[8];
+      float2 xj[8];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int b = mask ? __builtin_ctzll(mask) : -1;
-            if (mask) mask &= mask - 1;
-            idx[k] = b;
-            w[k] = __shfl(wj, b < 0 ? 0 : b);
-          }
-          float2 x[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            x[k] = idx[k] >= 0 ? *reinterpret_cast<const float2*>(base + (size_t)(j0 + idx[k]) * kSlot +
-                                                                   r * kD + 2 * lane)
-                               : make_float2(0.f, 0.f);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float wk = idx[k] >= 0 ? w[k] : 0.f;
-            acc.x += wk * x[k].x;
-            acc.y += wk * x[k].y;
-          }
-        }
+      for (int k = 0; k < 8; ++k) {
+        const bool ok = j0 + k < n_part;
+        const float* sp = base + (size_t)(j0 + k) * kSlot;
+        mj[k] = ok ? sp[kRows * kD + r] : -INFINITY;
+        lj[k] = ok ? sp[kRows * kD + kRows + r] : 0.f;
+        xj[k] = ok ? *reinterpret_cast<const float2*>(sp + r * kD + 2 * lane) : make_float2(0.f, 0.f);
       }
-      L = wave_sum(Ls);
+      float Mn = M;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, mj[k]);
+      if (Mn == -INFINITY) continue;
+      const float al = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      L *= al;
+      acc.x *= al;
+      acc.y *= al;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = mj[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj[k] - Mn);
+        L += w * lj[k];
+        acc.x += w * xj[k].x;
+        acc.y += w * xj[k].y;
+      }
+      M = Mn;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
