@@ -88,11 +88,9 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // that untyped loads are range checked against num_records.
 constexpr int kBufWord3 = 0x00020000;
 
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// Keeps the compiler from reordering memory accesses across this point;
+// emits no instruction.
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -431,10 +429,18 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // so two blocks are in flight while one is processed; the first two
     // load while the table is built.  Loads for claims past the segment
     // re-read block 0 (cache hits), so every step issues the same loads.
-    auto claim = [&]() {
+    // a claim is issued one step before its block index is needed, so the
+    // atomic's latency hides behind a block
+    auto claim_issue = [&]() {
       int v = 0;
       if (lane == 0) v = atomicAdd(claim_ctr, 1);
-      return __builtin_amdgcn_readfirstlane(v);
+      return v;
+    };
+    int pend = 0;
+    auto claim = [&]() {
+      const int n = __builtin_amdgcn_readfirstlane(pend);
+      pend = claim_issue();
+      return n;
     };
     auto blk = [&](int n) {
       const int tb = t0 + 64 * n;
@@ -597,7 +603,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       }
 
       // ---- p to the value operand layout through LDS -------------------
-      wave_sync_lds();
+      // A wave's LDS accesses execute in issue order, so the reads below see
+      // these writes, and the previous block's reads of the same area were
+      // issued before them; only the compiler must keep the order.
+      lds_order();
       {
         // key 4 q + g is staged at position 16 g + q, so that lane group g
         // finds its keys 4 q + g (q = 0..15) contiguous
@@ -607,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         *reinterpret_cast<uint16_t*>(pw + 2 * kPRow) = (uint16_t)p23;
         *reinterpret_cast<uint16_t*>(pw + 3 * kPRow) = (uint16_t)(p23 >> 16);
       }
-      wave_sync_lds();
+      lds_order();
       const uint4 P0 = *reinterpret_cast<const uint4*>(ps + rA * kPRow + 32 * grp16);
       const uint4 P1 = *reinterpret_cast<const uint4*>(ps + rA * kPRow + 32 * grp16 + 16);
       pp[0] = P0.x; pp[1] = P0.y; pp[2] = P0.z; pp[3] = P0.w;
@@ -627,6 +636,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     };
 
     if (t0 + 64 * nA < t1) {
+      pend = claim_issue();
       bool pending = false;
       for (;;) {
         nC = claim();
