@@ -198,6 +198,24 @@ def test_encode_shapes(D, d, n_c):
     check_recon(rec.cpu().numpy(), O.decode(codes, C, s[0], True), "fp32", f"D{D} d{d}")
 
 
+@pytest.mark.parametrize("S", [10, 200, 600])
+def test_encode_codebook_split_tiers(S):
+    """Short inputs split the codebook search across 16 or 4 waves of a
+    workgroup; longer ones give each wave its own token-heads. All three
+    give the oracle's codes (near-tie rule) and reconstructions."""
+    rng = np.random.default_rng(300 + S)
+    B, H, D, d = 2, 4, 128, 4                # 32 sub-vectors per token-head
+    k = synth.outlier_normal(rng, (B, H, S, D), 2)
+    s = synth.smooth_factors(k)
+    xt = O.forward_transform(k, s, True).reshape(-1, d)
+    C = synth.sample_rows(rng, xt, 256)
+    rec, codes = vq_encode_decode(dev(k), dev(C), d, smooth=dev(s[0]), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy()
+    check_codes(k, C, d, s[0], True, codes, f"tiers S{S}")
+    check_recon(rec.cpu().numpy(), O.decode(codes, C, s[0], True), "fp32", f"tiers S{S}")
+
+
 def test_encode_append_and_row_offsets():
     rng = np.random.default_rng(2)
     B, H, S, D, d, S_cap = 3, 2, 5, 64, 4, 20

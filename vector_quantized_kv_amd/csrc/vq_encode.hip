@@ -20,6 +20,10 @@ namespace vq {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves of 64
+// Workgroup size of a kernel whose waves split the codebook CSPLIT ways:
+// one group of token-heads per workgroup when the codebook is split.
+template <int CSPLIT>
+constexpr int threads_for() { return CSPLIT > 4 ? 64 * CSPLIT : kThreads; }
 
 template <int DS>
 __device__ __forceinline__ void load_f16(const __half* __restrict__ p, float (&x)[DS]) {
@@ -44,6 +48,40 @@ __device__ __forceinline__ void load_f16(const __half* __restrict__ p, float (&x
         x[i + 2 * k] = f.x; x[i + 2 * k + 1] = f.y;
       }
     }
+  }
+}
+
+// The DS fp16 values at p as raw bits (halves packed two per word), to be
+// converted once they are needed.
+template <int DS>
+struct RawHalves {
+  uint32_t w[(DS + 1) / 2];
+};
+template <int DS>
+__device__ __forceinline__ RawHalves<DS> load_raw_f16(const __half* __restrict__ p) {
+  RawHalves<DS> r;
+  if constexpr (DS == 1) {
+    r.w[0] = *reinterpret_cast<const uint16_t*>(p);
+  } else if constexpr (DS == 2) {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (DS == 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = u.x; r.w[1] = u.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < DS / 8; ++i) {
+      const uint4 u = reinterpret_cast<const uint4*>(p)[i];
+      r.w[4 * i] = u.x; r.w[4 * i + 1] = u.y; r.w[4 * i + 2] = u.z; r.w[4 * i + 3] = u.w;
+    }
+  }
+  return r;
+}
+template <int DS>
+__device__ __forceinline__ void cvt_raw_f16(const RawHalves<DS>& r, float (&x)[DS]) {
+#pragma unroll
+  for (int e = 0; e < DS; ++e) {
+    const uint16_t b = (uint16_t)(r.w[e / 2] >> (16 * (e & 1)));
+    x[e] = __half2float(*reinterpret_cast<const __half*>(&b));
   }
 }
 
@@ -136,13 +174,14 @@ struct Dims {
 // them (used when there are too few token-heads to fill the chip); their
 // partial argmins are combined through LDS, lowest index first on ties.
 template <int D, int DS, int MODE, int CSPLIT>
-__global__ __launch_bounds__(kThreads) void pvq_kernel(
+__global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kernel(
     const __half* __restrict__ keys, const uint8_t* __restrict__ codes_in,
     const float* __restrict__ cb, const float* __restrict__ smooth,
     uint8_t* __restrict__ codes, void* __restrict__ recon, Dims d, RowOffsets offs) {
   constexpr int NSUB = D / DS;   // lanes per token-head (<= 64)
   constexpr int TPW = 64 / NSUB; // token-heads per wave
-  constexpr int TPB = (kThreads / 64 / CSPLIT) * TPW;
+  constexpr int NT = threads_for<CSPLIT>();
+  constexpr int TPB = (NT / 64 / CSPLIT) * TPW;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave / CSPLIT, part = wave % CSPLIT;
@@ -157,28 +196,51 @@ __global__ __launch_bounds__(kThreads) void pvq_kernel(
   const int b = (int)(bh / d.H);
   const float* srow = smooth ? smooth + (long long)(d.smooth_rows == 1 ? 0 : h) * D + j * DS : nullptr;
 
+  // The row's inputs (raw fp16 bits of the clamped row, smooth factors)
+  // are requested before the codebook staging below, so all loads are in
+  // flight together.
+  float x[DS], sv[DS];
+  RawHalves<DS> raw;
+  if constexpr (MODE != 2) {
+    raw = load_raw_f16<DS>(keys + thc * D + j * DS);
+    if (srow) {
+#pragma unroll
+      for (int e = 0; e < DS; ++e) sv[e] = srow[e];
+    }
+  }
+
   // Short inputs (CSPLIT > 1) are latency bound: stage the codebook in LDS
-  // with one coalesced pass instead of walking it with dependent scalar loads.
+  // with one coalesced pass (every load issued before any is stored)
+  // instead of walking it with dependent scalar loads.
   const float* cbk = cb;
   if constexpr (CSPLIT > 1) {
     __shared__ float s_cb[256 * DS];
-    for (int i = threadIdx.x; i < d.n_c * DS; i += kThreads) s_cb[i] = cb[i];
+    constexpr int kPer = (256 * DS + NT - 1) / NT;
+    float v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = threadIdx.x + k * NT;
+      v[k] = i < d.n_c * DS ? cb[i] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < 256 * DS) s_cb[i] = v[k];
+    }
     __syncthreads();
     cbk = s_cb;
   }
 
-  float x[DS];
   int idx = 0;
   if constexpr (MODE != 2) {
-    if (valid) {
-      load_f16<DS>(keys + thc * D + j * DS, x);
-    } else {
+    cvt_raw_f16<DS>(raw, x);
+    if (!valid) {
 #pragma unroll
       for (int e = 0; e < DS; ++e) x[e] = 0.f;
     }
     if (srow) {
 #pragma unroll
-      for (int e = 0; e < DS; ++e) x[e] = x[e] / srow[e];
+      for (int e = 0; e < DS; ++e) x[e] = x[e] / sv[e];
     }
     if (d.transform) wht<D, DS>(x, j);
 
@@ -201,8 +263,8 @@ __global__ __launch_bounds__(kThreads) void pvq_kernel(
       if (acc < best) { best = acc; idx = c; }
     }
     if constexpr (CSPLIT > 1) {
-      __shared__ float s_best[kThreads];
-      __shared__ int s_idx[kThreads];
+      __shared__ float s_best[NT];
+      __shared__ int s_idx[NT];
       s_best[threadIdx.x] = best;
       s_idx[threadIdx.x] = idx;
       __syncthreads();
@@ -243,10 +305,11 @@ __global__ __launch_bounds__(kThreads) void pvq_kernel(
 template <int D, int DS, int MODE, int CSPLIT>
 void launch_one(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStream_t st) {
   constexpr int NSUB = D / DS;
-  constexpr int TPB = (kThreads / 64 / CSPLIT) * (64 / NSUB);
+  constexpr int NT = threads_for<CSPLIT>();
+  constexpr int TPB = (NT / 64 / CSPLIT) * (64 / NSUB);
   const long long n_th = (long long)a.B * a.H * a.S;
   const unsigned blocks = (unsigned)((n_th + TPB - 1) / TPB);
-  hipLaunchKernelGGL((pvq_kernel<D, DS, MODE, CSPLIT>), dim3(blocks), dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((pvq_kernel<D, DS, MODE, CSPLIT>), dim3(blocks), dim3(NT), 0, st,
                      a.keys, a.codes_in, a.codebook, a.smooth, a.codes, a.recon, d, o);
 }
 
@@ -260,15 +323,20 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
   RowOffsets o{};
   if (offs) o = *offs;
   // Fewer lanes than about four waves per CU (256 CUs): split the codebook
-  // over the four waves of a workgroup instead of giving each its own
-  // token-heads, so short appends (one token per row) are not latency bound.
-  const bool split = n_th * NSUB < 256LL * 64 * 4;
+  // over the waves of a workgroup instead of giving each its own
+  // token-heads, so short appends (one token per row) are not latency
+  // bound; below one wave per CU, 16 ways (16 waves per workgroup).
+  const int split = n_th * NSUB < 256LL * 64 ? 16 : (n_th * NSUB < 256LL * 64 * 4 ? 4 : 1);
   switch (mode) {
     case 0:
-      if (split) launch_one<D, DS, 0, 4>(a, d, o, st); else launch_one<D, DS, 0, 1>(a, d, o, st);
+      if (split == 16) launch_one<D, DS, 0, 16>(a, d, o, st);
+      else if (split == 4) launch_one<D, DS, 0, 4>(a, d, o, st);
+      else launch_one<D, DS, 0, 1>(a, d, o, st);
       break;
     case 1:
-      if (split) launch_one<D, DS, 1, 4>(a, d, o, st); else launch_one<D, DS, 1, 1>(a, d, o, st);
+      if (split == 16) launch_one<D, DS, 1, 16>(a, d, o, st);
+      else if (split == 4) launch_one<D, DS, 1, 4>(a, d, o, st);
+      else launch_one<D, DS, 1, 1>(a, d, o, st);
       break;
     default:
       launch_one<D, DS, 2, 1>(a, d, o, st);
