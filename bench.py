@@ -84,6 +84,27 @@ def read_traffic(path, workload):
         return None
 
 
+def time_events_each(fn, reps, torch, warm=3):
+    """Per-call device times (us) of fn(i): one HIP event between consecutive
+    calls on the current stream, read after a single synchronize, so the
+    queue stays full while they are recorded."""
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]
+
+
+def pct(xs, q):
+    ys = sorted(xs)
+    return ys[min(len(ys) - 1, int(round(q * (len(ys) - 1))))]
+
+
 def time_events(fn, reps, torch, warm=3):
     """Average device time of fn() over reps (HIP events on the current stream)."""
     for _ in range(warm):
@@ -193,6 +214,16 @@ def main():
     attn_us = time_events(lambda i: steps[i % n_sets][2](), max(args.steps, 100), torch)
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     log(f"[bench] vq_attend: {attn_us:.1f} us, {achieved:.0f} GB/s")
+    each = time_events_each(lambda i: steps[i % n_sets][2](), max(args.steps, 100), torch)
+    log(f"[bench] vq_attend per call: p10 {pct(each, 0.1):.1f} p50 {pct(each, 0.5):.1f} "
+        f"p90 {pct(each, 0.9):.1f} us")
+    # practical HBM reference: a plain 1 GiB elementwise copy (1 GiB read + 1 GiB written)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    copy_us = time_events(lambda i: torch.neg(src, out=dst), 10, torch)
+    copy_gbps = 2 * COPY_BYTES / (copy_us * 1e-6) / 1e9
+    del src, dst
+    log(f"[bench] 1 GiB copy: {copy_us:.1f} us, {copy_gbps:.0f} GB/s read+write")
     traffic = read_traffic(os.path.join(ROOT, "profiles", "vq_attend_gqa_long_W0_traffic.txt"),
                            "gqa_long_W0")
 
@@ -227,6 +258,9 @@ def main():
             "kernel": "vq_attend (attend_stream_kernel + stream_merge_kernel)",
             "bytes_per_launch": attn_bytes,
             "us_per_launch": round(attn_us, 2),
+            "us_per_launch_p10_p50_p90": [round(pct(each, q), 2) for q in (0.1, 0.5, 0.9)],
+            "copy_kernel_GBps": round(copy_gbps, 1),
+            "frac_of_copy_kernel": round(achieved / copy_gbps, 4),
         },
     }
 

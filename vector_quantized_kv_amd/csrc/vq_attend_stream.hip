@@ -75,7 +75,14 @@ constexpr int kUnitsPerThread = (kMaxUnits + kThreads) / kThreads;
 constexpr int kMaxChunks = 4096;       // partial slots reserved for chunks (>= workgroups)
 constexpr int kQExp = kW + 4;          // int slots: exponents of the two query buffers
 static_assert(kUnitsPerThread * kThreads >= kMaxUnits + 1, "prefix coverage");
-static_assert(kPrefix + 4 * (kMaxUnits + 1) <= 160 * 1024, "LDS budget");
+constexpr int kMaxGrid = 256;          // persistent workgroups (one per CU)
+constexpr uint32_t kInside = kPrefix + 4 * (kMaxUnits + 1);  // int [kMaxGrid]
+constexpr uint32_t kWaveMax = kInside + 4 * kMaxGrid;          // float [kW]
+constexpr uint32_t kLdsBytes = kWaveMax + 4 * kW;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+// Keys charged for a unit starting inside a chunk (its table build and
+// partial combine, about 2 us of a workgroup's streaming time).
+constexpr int kSegCost = 768;
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -92,16 +99,55 @@ constexpr int kBufWord3 = 0x00020000;
 // emits no instruction.
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round
+// trips): row_shr 1, 2, 4, 8 scan each row of 16 lanes, then row_bcast 15
+// and 31 carry the row totals into the rows above.
+__device__ __forceinline__ int wave_scan_int(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false); // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false); // row_bcast:31 -> rows 2, 3
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// Sum over the wave, as a wave-uniform value.
+__device__ __forceinline__ int wave_total_int(int v) {
+  return __builtin_amdgcn_readlane(wave_scan_int(v), 63);
+}
+
+// Maximum over the wave with the same DPP pattern, as a wave-uniform value;
+// lanes shifted in from outside a row (or in rows not written) keep -inf.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const float o = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v),
+                                                             CTRL, ROWS, 0xf, false));
+  return fmaxf(v, o);
+}
+__device__ __forceinline__ float wave_max_u(float v) {
+  v = dpp_max_step<0x111, 0xf>(v);
+  v = dpp_max_step<0x112, 0xf>(v);
+  v = dpp_max_step<0x114, 0xf>(v);
+  v = dpp_max_step<0x118, 0xf>(v);
+  v = dpp_max_step<0x142, 0xa>(v);
+  v = dpp_max_step<0x143, 0xc>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Sum over the wave with the same DPP pattern, as a wave-uniform value.
+template <int CTRL, int ROWS, bool BOUND>
+__device__ __forceinline__ float dpp_add_step(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, BOUND));
+}
+__device__ __forceinline__ float wave_total_f(float v) {
+  v = dpp_add_step<0x111, 0xf, true>(v);
+  v = dpp_add_step<0x112, 0xf, true>(v);
+  v = dpp_add_step<0x114, 0xf, true>(v);
+  v = dpp_add_step<0x118, 0xf, true>(v);
+  v = dpp_add_step<0x142, 0xa, false>(v);
+  v = dpp_add_step<0x143, 0xc, false>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
@@ -177,139 +223,18 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- global reads first: codebooks and kv lengths, then LDS tables -----
-  {
-    // key codebook: one float4 per thread; value codebook: two threads per
-    // code, each writing 16 of its 32 replicas
-    float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), vq = kq;
-    if ((tid >> 1) < p.n_c) {
-      kq = reinterpret_cast<const float4*>(k_codebook)[tid];
-      vq = reinterpret_cast<const float4*>(v_codebook)[tid >> 1];
-    }
-    int lv[kUnitsPerThread];
-#pragma unroll
-    for (int k = 0; k < kUnitsPerThread; ++k) {
-      const int b = tid + kThreads * k;
-      lv[k] = b < p.B ? (kv_lens ? kv_lens[b] : p.S_cap) : 0;
-    }
-    *reinterpret_cast<float4*>(lds + kCbk + 16 * tid) = kq;
-    const uint32_t h0 = pack_half2(vq.x, vq.y), h1 = pack_half2(vq.z, vq.w);
-    const uint4 two = make_uint4(h0, h1, h0, h1);
-    const int code = tid >> 1;
-    // rotated by code so that the 16 lanes of a write hit distinct bank quads
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4*>(lds + kValTab + code * 256 + (tid & 1) * 128 + 16 * ((i + code) & 7)) = two;
-    int* lens = reinterpret_cast<int*>(lds + kLens);
-#pragma unroll
-    for (int k = 0; k < kUnitsPerThread; ++k) {
-      const int b = tid + kThreads * k;
-      if (b < p.B) lens[b] = lv[k] < 0 ? 0 : (lv[k] > p.S_cap ? p.S_cap : lv[k]);
-    }
-  }
-  __syncthreads();
-  const int* const lens = reinterpret_cast<const int*>(lds + kLens);
-  // magnitude exponent of the key codebook (every wave reads all of it)
-  int ecb;
-  {
-    const float* cbk = reinterpret_cast<const float*>(lds + kCbk);
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 v = *reinterpret_cast<const float4*>(cbk + 4 * (lane + 64 * i));
-      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-    ecb = __builtin_amdgcn_readfirstlane(mag_exp(wave_max(mx)));
-  }
-
-  // ---- unit prefix (exclusive) over the U <= kMaxUnits units, the chunk
-  // and the unit holding its first key -------------------------------------
-  int* const pre = reinterpret_cast<int*>(lds + kPrefix);
-  int* const scan = reinterpret_cast<int*>(lds + kScan);
-  int* const first_unit = scan + kW + 2;
-  const int c = blockIdx.x;
-  int T, C, start;
-  {
-    int n[kUnitsPerThread], sum = 0;
-#pragma unroll
-    for (int k = 0; k < kUnitsPerThread; ++k) {
-      const int u = kUnitsPerThread * tid + k;
-      n[k] = u < p.U ? unit_len(p, lens, u) : 0;
-      sum += n[k];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
-    if (lane == 63) scan[wave] = incl;
-    __syncthreads();
-    int off = 0;
-    T = 0;
-#pragma unroll
-    for (int w = 0; w < kW; ++w) {
-      const int s = scan[w];
-      off += w < wave ? s : 0;
-      T += s;
-    }
-    C = max(p.cmin, (T + (int)gridDim.x - 1) / (int)gridDim.x);
-    start = c * C;  // T <= U * S_cap < 2^30 is checked on the host
-    int pu = off + incl - sum;
-#pragma unroll
-    for (int k = 0; k < kUnitsPerThread; ++k) {
-      const int u = kUnitsPerThread * tid + k;
-      if (u < p.U) pre[u] = pu;
-      if (n[k] > 0 && pu <= start && start < pu + n[k]) *first_unit = u;
-      pu += n[k];
-    }
-    if (tid == 0) pre[p.U] = T;
-    __syncthreads();
-  }
-  if (blockIdx.x == 0) {
-    for (int u = tid; u <= p.U; u += kThreads) header[1 + u] = pre[u];
-    if (tid == 0) header[0] = C;
-  }
-  const int end = min(T, start + C);
-  if (start >= T) return;
-  int u = *first_unit;
-
-  // ---- lane constants ------------------------------------------------------
-  // Score gathers: at step k = 4 a + b the lane reads sub-vector
-  // j = 4 ((a + rdw) mod 4) + (b + rb) mod 4 with (rdw, rb) = lane mod 16, so
-  // the 16 lanes served together read 16 distinct j: 16 distinct bank
-  // quads of the [code][j][row] table, whatever the codes.  jt[a] holds the
-  // four byte offsets 16 j of steps (a, b), sel[b] the v_perm selector that
-  // places the code byte of sub-vector j above that offset.
-  const int rdw = (lane >> 2) & 3, rb = lane & 3;
-  const uint32_t rot1 = (rdw & 1) ? ~0u : 0u, rot2 = (rdw & 2) ? ~0u : 0u;
-  uint32_t jt[4], sel[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      w |= (uint32_t)(16 * (4 * ((a + rdw) & 3) + ((b + rb) & 3))) << (8 * b);
-    jt[a] = w;
-  }
-#pragma unroll
-  for (int b = 0; b < 4; ++b) sel[b] = 0x0c0c0000u | ((4u + ((b + rb) & 3)) << 8) | (uint32_t)b;
-  const uint32_t vbase = (uint32_t)(lane & 31) * 8u | (1u << 16);      // value replica + 64 KiB
-  const int e_a = lane & 3;          // A operand of the value MFMA: row (rA, e_a)
-  const int rA = (lane & 15) >> 2;
-  const int grp16 = lane >> 4;       // K group of the 16x16x32 operands
-  const uint32_t sa0 = e_a == 0 ? 0x0c0c0100u : (e_a == 1 ? 0x01000c0cu : 0x0c0c0c0cu);
-  const uint32_t sa1 = e_a == 2 ? 0x0c0c0100u : (e_a == 3 ? 0x01000c0cu : 0x0c0c0c0cu);
-  const uint32_t sa2 = e_a == 0 ? 0x0c0c0302u : (e_a == 1 ? 0x03020c0cu : 0x0c0c0c0cu);
-  const uint32_t sa3 = e_a == 2 ? 0x0c0c0302u : (e_a == 3 ? 0x03020c0cu : 0x0c0c0c0cu);
-  uint8_t* const ps = lds + kPStage + wave * kPWave;
-  float* const red = reinterpret_cast<float*>(lds + kLut);  // [kW][kSlot], over the table
-  int* const claim_ctr = scan + kW;
+  int* const scan = reinterpret_cast<int*>(lds + kScan);  // small shared ints (see kScan)
 
   // Query rows of unit uq: dual transform, scaled, into LDS buffer qbuf
-  // (run by wave 0).  Lane (bq = lane / 4, row ir = lane % 4) holds dims
-  // 4 bq + e and 64 + 4 bq + e (e = 0..3) of row ir.
-  auto make_query = [&](int uq, int qbuf) {
+  // (run by wave 0), in two halves so that the loads can be issued early.
+  // Lane (bq = lane / 4, row ir = lane % 4) holds dims 4 bq + e and
+  // 64 + 4 bq + e (e = 0..3) of row ir.
+  struct QueryRaw {
+    uint2 q[2];
+    float4 s[2];
+  };
+  auto query_load = [&](int uq) {
+    QueryRaw r;
     int bgq, rgq, bq_b;
     unit_coords(p, uq, bgq, rgq, bq_b);
     const int gq = bgq - bq_b * p.Hkv;
@@ -319,20 +244,30 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const int ip = (int)fast_div((uint32_t)rc, p.div_g);
     const int h = gq * p.G + rc - ip * p.G;
     const __half* qp = q + ((size_t)(bq_b * p.Hq + h) * p.Sq + ip) * kD;
-    float x[8];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint2 w = *reinterpret_cast<const uint2*>(qp + 64 * k + 4 * bq);
-      const float2 f0 = __half22float2(*reinterpret_cast<const __half2*>(&w.x));
-      const float2 f1 = __half22float2(*reinterpret_cast<const __half2*>(&w.y));
-      x[4 * k] = f0.x; x[4 * k + 1] = f0.y; x[4 * k + 2] = f1.x; x[4 * k + 3] = f1.y;
-    }
+    for (int k = 0; k < 2; ++k) r.q[k] = *reinterpret_cast<const uint2*>(qp + 64 * k + 4 * bq);
     if (smooth) {
       const float* sp = smooth + (p.smooth_rows == 1 ? 0 : gq) * kD;
 #pragma unroll
+      for (int k = 0; k < 2; ++k) r.s[k] = *reinterpret_cast<const float4*>(sp + 64 * k + 4 * bq);
+    }
+    return r;
+  };
+  auto query_finish = [&](const QueryRaw& r, int uq, int qbuf) {
+    const int rgq = uq - (int)fast_div((uint32_t)uq, p.div_nrg) * p.n_rg;
+    const int bq = lane >> 2, ir = lane & 3;
+    const int rho = 4 * rgq + ir;
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float2 f0 = __half22float2(*reinterpret_cast<const __half2*>(&r.q[k].x));
+      const float2 f1 = __half22float2(*reinterpret_cast<const __half2*>(&r.q[k].y));
+      x[4 * k] = f0.x; x[4 * k + 1] = f0.y; x[4 * k + 2] = f1.x; x[4 * k + 3] = f1.y;
+    }
+    if (smooth) {
+#pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const float4 s = *reinterpret_cast<const float4*>(sp + 64 * k + 4 * bq);
-        x[4 * k] *= s.x; x[4 * k + 1] *= s.y; x[4 * k + 2] *= s.z; x[4 * k + 3] *= s.w;
+        x[4 * k] *= r.s[k].x; x[4 * k + 1] *= r.s[k].y; x[4 * k + 2] *= r.s[k].z; x[4 * k + 3] *= r.s[k].w;
       }
     }
     if (p.transform) {
@@ -367,9 +302,182 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     for (int k = 0; k < 2; ++k)
       *reinterpret_cast<float4*>(qd + ir * kD + 64 * k + 4 * bq) =
           make_float4(x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3]);
-    mx = wave_max(mx);
-    if (lane == 0) scan[kQExp + qbuf] = mag_exp(mx);
+    const int eq = mag_exp(wave_max_u(mx));  // all lanes take part in the reduction
+    if (lane == 0) scan[kQExp + qbuf] = eq;
   };
+  auto make_query = [&](int uq, int qbuf) { query_finish(query_load(uq), uq, qbuf); };
+
+  // ---- global reads first: codebooks and kv lengths, then LDS tables -----
+  {
+    // key codebook: one float4 per thread; value codebook: two threads per
+    // code, each writing 16 of its 32 replicas
+    float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), vq = kq;
+    if ((tid >> 1) < p.n_c) {
+      kq = reinterpret_cast<const float4*>(k_codebook)[tid];
+      vq = reinterpret_cast<const float4*>(v_codebook)[tid >> 1];
+    }
+    int lv[kUnitsPerThread];
+#pragma unroll
+    for (int k = 0; k < kUnitsPerThread; ++k) {
+      const int b = tid + kThreads * k;
+      lv[k] = b < p.B ? (kv_lens ? kv_lens[b] : p.S_cap) : 0;
+    }
+    *reinterpret_cast<float4*>(lds + kCbk + 16 * tid) = kq;
+    // per-wave maximum magnitude of the key codebook
+    const float kmx = wave_max_u(fmaxf(fmaxf(fabsf(kq.x), fabsf(kq.y)), fmaxf(fabsf(kq.z), fabsf(kq.w))));
+    if (lane == 0) reinterpret_cast<float*>(lds + kWaveMax)[wave] = kmx;
+    const uint32_t h0 = pack_half2(vq.x, vq.y), h1 = pack_half2(vq.z, vq.w);
+    const uint4 two = make_uint4(h0, h1, h0, h1);
+    const int code = tid >> 1;
+    // rotated by code so that the 16 lanes of a write hit distinct bank quads
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint4*>(lds + kValTab + code * 256 + (tid & 1) * 128 + 16 * ((i + code) & 7)) = two;
+    int* lens = reinterpret_cast<int*>(lds + kLens);
+#pragma unroll
+    for (int k = 0; k < kUnitsPerThread; ++k) {
+      const int b = tid + kThreads * k;
+      if (b < p.B) lens[b] = lv[k] < 0 ? 0 : (lv[k] > p.S_cap ? p.S_cap : lv[k]);
+    }
+  }
+  __syncthreads();
+  const int* const lens = reinterpret_cast<const int*>(lds + kLens);
+  // magnitude exponent of the key codebook
+  int ecb;
+  {
+    const float* wm = reinterpret_cast<const float*>(lds + kWaveMax);
+    float mx = 0.f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) mx = fmaxf(mx, wm[w]);
+    ecb = mag_exp(mx);
+  }
+
+  // ---- unit prefix (exclusive) over the U <= kMaxUnits units, the chunk
+  // boundaries, and the unit holding the chunk's first key -----------------
+  // Chunks start as equal shares C0 of T.  A unit that starts strictly
+  // inside a chunk costs that chunk an extra table build and combine, so
+  // each such start moves kSegCost keys of the chunk to the others:
+  //   B_k = k C0 - kSegCost E_k + floor(kSegCost N k / G),
+  // E_k = the (capped) number of inside starts in chunks < k, N = E_G, so
+  // B_0 = 0, B_G = G C0 >= T, and B is increasing.
+  int* const pre = reinterpret_cast<int*>(lds + kPrefix);
+  int* const spec_unit = scan + kW + 2;
+  int* const inside = reinterpret_cast<int*>(lds + kInside);  // [G]
+  const int c = blockIdx.x;
+  const int G = gridDim.x;
+  for (int i = tid; i < G; i += kThreads) inside[i] = 0;
+  if (tid == 0) *spec_unit = 0;  // stays 0 when the chunk starts past the end
+  int T, C0, start, end;
+  QueryRaw qraw;
+  {
+    int n[kUnitsPerThread], sum = 0;
+#pragma unroll
+    for (int k = 0; k < kUnitsPerThread; ++k) {
+      const int u = kUnitsPerThread * tid + k;
+      n[k] = u < p.U ? unit_len(p, lens, u) : 0;
+      sum += n[k];
+    }
+    const int incl = wave_scan_int(sum);
+    if (lane == 63) scan[wave] = incl;
+    __syncthreads();
+    int off = 0;
+    T = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const int s = scan[w];
+      off += w < wave ? s : 0;
+      T += s;
+    }
+    C0 = max(p.cmin, (T + G - 1) / G);  // T <= U * S_cap < 2^30 is checked on the host
+    const int pu0 = off + incl - sum;
+    int pu = pu0;
+#pragma unroll
+    for (int k = 0; k < kUnitsPerThread; ++k) {
+      const int u = kUnitsPerThread * tid + k;
+      if (u < p.U) pre[u] = pu;
+      if (n[k] > 0 && pu % C0 != 0) atomicAdd(&inside[pu / C0], 1);
+      // the unit holding the first key of the chunk before the correction
+      // below (which moves bounds by at most C0 / 2): wave 0 starts loading
+      // its query rows right after the barrier
+      if (n[k] > 0 && pu <= c * C0 && c * C0 < pu + n[k]) *spec_unit = u;
+      if (blockIdx.x == 0 && u < p.U && n[k] == 0) {
+        header[2 * u] = 0;       // an empty unit has no partials
+        header[2 * u + 1] = -1;
+      }
+      pu += n[k];
+    }
+    if (tid == 0) pre[p.U] = T;
+    __syncthreads();
+    if (wave == 0) qraw = query_load(min(max(*spec_unit, 0), p.U - 1));
+    // every wave derives the chunk's bounds from the inside-start counts
+    // at most C0 / 2 keys move out of a chunk (none when C0 < 2 kSegCost)
+    const int cap = C0 / (2 * kSegCost);
+    int e_lo = 0, e_hi = 0, e_all = 0;
+    for (int i = lane; i < G; i += 64) {
+      const int v = min(inside[i], cap);
+      e_lo += i < c ? v : 0;
+      e_hi += i <= c ? v : 0;
+      e_all += v;
+    }
+    // full-wave sums, read from one lane: wave-uniform values for the
+    // compiler too (the code buffer descriptors derived from them must stay
+    // in scalar registers)
+    e_lo = wave_total_int(e_lo);
+    e_hi = wave_total_int(e_hi);
+    e_all = wave_total_int(e_all);
+    // kSegCost * e_all * (c + 1) <= kSegCost * U * G < 2^31
+    start = c * C0 - kSegCost * e_lo + (int)fast_div((uint32_t)(kSegCost * e_all * c), p.div_grid);
+    end = min(T, (c + 1) * C0 - kSegCost * e_hi +
+                     (int)fast_div((uint32_t)(kSegCost * e_all * (c + 1)), p.div_grid));
+  }
+  if (start >= T) return;
+  // the nonempty unit holding position `start`, by a ballot over the prefix
+  int u = 0;
+  for (int base = 0; base < p.U; base += 64) {
+    const int uu = base + lane;
+    bool hit = false;
+    if (uu < p.U) {
+      const int a0 = pre[uu], a1 = pre[uu + 1];
+      hit = a0 < a1 && a0 <= start && start < a1;
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+    if (m) {
+      u = base + (int)__builtin_ctzll(m);
+      break;
+    }
+  }
+
+  // ---- lane constants ------------------------------------------------------
+  // Score gathers: at step k = 4 a + b the lane reads sub-vector
+  // j = 4 ((a + rdw) mod 4) + (b + rb) mod 4 with (rdw, rb) = lane mod 16, so
+  // the 16 lanes served together read 16 distinct j: 16 distinct bank
+  // quads of the [code][j][row] table, whatever the codes.  jt[a] holds the
+  // four byte offsets 16 j of steps (a, b), sel[b] the v_perm selector that
+  // places the code byte of sub-vector j above that offset.
+  const int rdw = (lane >> 2) & 3, rb = lane & 3;
+  const uint32_t rot1 = (rdw & 1) ? ~0u : 0u, rot2 = (rdw & 2) ? ~0u : 0u;
+  uint32_t jt[4], sel[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      w |= (uint32_t)(16 * (4 * ((a + rdw) & 3) + ((b + rb) & 3))) << (8 * b);
+    jt[a] = w;
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) sel[b] = 0x0c0c0000u | ((4u + ((b + rb) & 3)) << 8) | (uint32_t)b;
+  const uint32_t vbase = (uint32_t)(lane & 31) * 8u | (1u << 16);      // value replica + 64 KiB
+  const int e_a = lane & 3;          // A operand of the value MFMA: row (rA, e_a)
+  const int rA = (lane & 15) >> 2;
+  const int grp16 = lane >> 4;       // K group of the 16x16x32 operands
+  const uint32_t sa0 = e_a == 0 ? 0x0c0c0100u : (e_a == 1 ? 0x01000c0cu : 0x0c0c0c0cu);
+  const uint32_t sa1 = e_a == 2 ? 0x0c0c0100u : (e_a == 3 ? 0x01000c0cu : 0x0c0c0c0cu);
+  const uint32_t sa2 = e_a == 0 ? 0x0c0c0302u : (e_a == 1 ? 0x03020c0cu : 0x0c0c0c0cu);
+  const uint32_t sa3 = e_a == 2 ? 0x0c0c0302u : (e_a == 3 ? 0x03020c0cu : 0x0c0c0c0cu);
+  uint8_t* const ps = lds + kPStage + wave * kPWave;
+  float* const red = reinterpret_cast<float*>(lds + kLut);  // [kW][kSlot], over the table
+  int* const claim_ctr = scan + kW;
 
   int pos = start;
   int qbuf = 0;          // query buffer of the current unit
@@ -378,6 +486,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // ---- segment: unit u, chunk positions [pos, seg_end) ----------------
     const int Pu = pre[u], Pn = pre[u + 1];
     const int seg_end = min(end, Pn);
+    // the merge finds unit u's partials in slots c_first + u .. c_last + u
+    if (tid == 0) {
+      if (pos == Pu) header[2 * u] = c;
+      if (seg_end == Pn) header[2 * u + 1] = c;
+    }
     int bg, rg, bb;
     unit_coords(p, u, bg, rg, bb);
     const int len = lens[bb];
@@ -454,7 +567,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       load_codes(blk(nB), kcB, vrB);
     }
 
-    if (!q_ready && wave == 0) make_query(u, qbuf);
+    if (!q_ready && wave == 0) {
+      // first segment: use the rows loaded during the setup if they are the
+      // right unit's (the usual case)
+      const int su = __builtin_amdgcn_readfirstlane(*spec_unit);
+      if (su == u) query_finish(qraw, u, qbuf); else make_query(u, qbuf);
+    }
     if (tid == 0) *claim_ctr = 2 * kW;
     __syncthreads();  // query rows ready; the previous combine has read the table area
     {
@@ -576,7 +694,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         float al[kRows];
 #pragma unroll
         for (int r = 0; r < kRows; ++r) {
-          const float mn = fmaxf(m[r], wave_max(s[r]));
+          const float mn = fmaxf(m[r], wave_max_u(s[r]));
           al[r] = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[r] - mn);
           m[r] = mn;
           th[r] = mn + kLazyMargin;
@@ -660,7 +778,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // ---- combine the waves' partials of the segment into slot c + u -------
     float l[kRows];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) l[r] = wave_sum(lsum[r]);
+    for (int r = 0; r < kRows; ++r) l[r] = wave_total_f(lsum[r]);
     __syncthreads();  // every wave is done with the table
     {
       float* sp = red + wave * kSlot;
@@ -722,12 +840,10 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const int* __restrict
   const int rho = ip * p.G + h % p.G;
   const int r = rho & 3;
   const int u = (bb * p.Hkv + g) * p.n_rg + (rho >> 2);
-  const int C = header[0];
-  const int Pu = header[1 + u], Pn = header[2 + u];
+  const int c_lo = header[2 * u], n_part = header[2 * u + 1] - c_lo + 1;
   float2 acc = make_float2(0.f, 0.f);
   float L = 0.f;
-  if (Pn > Pu) {
-    const int c_lo = Pu / C, n_part = (Pn - 1) / C - c_lo + 1;
+  if (n_part > 0) {
     const float* base = part + (size_t)(c_lo + u) * kSlot;
     // up to 8 partials per round: their (m, l) and the lane's two
     // accumulator values load together, then fold into the running sums
@@ -798,7 +914,7 @@ bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, i
     sp->div_nrg = make_fastdiv((uint32_t)n_rg);
     sp->div_hkv = make_fastdiv((uint32_t)Hkv);
   }
-  if (lds_bytes) *lds_bytes = (kPrefix + (size_t)(U + 1) * 4 + 15) / 16 * 16;
+  if (lds_bytes) *lds_bytes = kLdsBytes;
   if (ws_bytes) *ws_bytes = stream_workspace_bytes(B, Hq, Sq, D, Hkv);
   return true;
 }
@@ -807,20 +923,21 @@ size_t stream_workspace_bytes(int B, int Hq, int Sq, int D, int Hkv) {
   if (D != kD || B <= 0 || Hq <= 0 || Sq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
   const long long G = Hq / Hkv, GS = G * Sq, n_rg = (GS + kRows - 1) / kRows;
   const long long U = (long long)B * Hkv * n_rg;
-  const size_t header = ((size_t)(U + 2) * 4 + 255) / 256 * 256;
+  const size_t header = ((size_t)U * 8 + 255) / 256 * 256;  // (first, last chunk) per unit
   return header + (size_t)(kMaxChunks + U) * kSlot * sizeof(float);
 }
 
 hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds, hipStream_t st) {
   const int cus = cached_cu_count();
   if (cus <= 0) return hipErrorInvalidDevice;
-  const int grid = cus < kMaxChunks ? cus : kMaxChunks;
+  const int grid = cus < kMaxGrid ? cus : kMaxGrid;
+  sp.div_grid = make_fastdiv((uint32_t)grid);
   sp.smooth_rows = a.smooth_rows;
   sp.transform = a.transform;
   sp.causal = a.causal;
   sp.window = a.window;
   sp.fold = (a.transform ? WhtNorm<kD>::value : 1.f) * a.scale_log2e;
-  const size_t header_bytes = ((size_t)(sp.U + 2) * 4 + 255) / 256 * 256;
+  const size_t header_bytes = ((size_t)sp.U * 8 + 255) / 256 * 256;
   int* header = reinterpret_cast<int*>(a.partials);
   float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.partials) + header_bytes);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attend_stream_kernel),
