@@ -147,6 +147,24 @@ int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D,
 size_t vq_attend_workspace_bytes(int B, int H_q, int S_q, int D, int H_kv,
                                  int S_cap, int sliding_window);
 
+/* Kernel families of vq_attend (see vq_attend_path). */
+enum {
+  VQ_PATH_STREAM = 1,   /* persistent streaming kernel: decode, many keys */
+  VQ_PATH_TILE = 2,     /* many-query tile kernel: >= 64 query rows per kv head */
+  VQ_PATH_LUT_MFMA = 3, /* per-unit query-LUT kernel with matrix-core values */
+  VQ_PATH_LUT_VALU = 4  /* per-unit query-LUT kernel on vector ALUs */
+};
+
+/*
+ * The kernel family vq_attend runs for this shape (the fused attention of
+ * "Metal Kernels API", "Fused SDPA"): one of VQ_PATH_*, or 0 when vq_attend
+ * would reject the shape (the reason is left in vq_last_error).  The choice
+ * depends only on these sizes, never on device data, and every family
+ * computes the same attention.  Host-only; needs no device.
+ */
+int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
+                   int n_centroids, int H_kv, int S_cap, int sliding_window);
+
 /*
  * Fused attention read directly from key and value codes ("Metal Kernels
  * API", "Fused SDPA", metal_fused_sdpa; with the raw query and the dual

@@ -155,3 +155,39 @@ def test_binding_rejects_host_tensors(lib):
         api.vq_encode(k, cb, 4)
     with pytest.raises(ValueError, match="fp16|float16"):
         api.vq_encode(k.float(), cb, 4)
+
+
+@pytest.mark.parametrize("shape,path", [
+    # (B, H_q, S_q, D, d_k, d_v, n_c, H_kv, S_cap, W): the benchmarked workloads
+    ((16, 32, 1, 128, 8, 4, 256, 8, 32768, 0), "stream"),      # GQA decode step
+    ((16, 32, 1, 128, 8, 4, 256, 8, 32768, 4096), "stream"),   # GQA decode, window 4096
+    ((1, 8, 1, 128, 8, 4, 256, 8, 8192, 0), "lut_mfma"),       # single-query decode
+    ((4, 8, 512, 128, 8, 4, 256, 8, 32768, 0), "tile"),        # prefill chunk
+    # at the streaming threshold (2^18 unit-keys) and just below it
+    ((4, 32, 1, 128, 8, 4, 256, 8, 8192, 0), "stream"),
+    ((4, 8, 2, 128, 8, 4, 256, 8, 8192, 8191), "stream"),
+    ((4, 8, 2, 128, 8, 4, 256, 8, 8192, 8190), "lut_mfma"),
+    ((2, 32, 1, 128, 8, 4, 256, 8, 8192, 0), "lut_mfma"),
+    # 64 query rows per kv head start the tile kernel
+    ((3, 2, 64, 128, 8, 4, 256, 2, 400, 0), "tile"),
+    ((3, 2, 63, 128, 8, 4, 256, 2, 400, 0), "lut_mfma"),
+    # other sub-vector sizes and head dims
+    ((1, 8, 1, 128, 8, 8, 256, 8, 300, 0), "lut_valu"),
+    ((1, 8, 1, 64, 4, 4, 256, 8, 300, 0), "lut_mfma"),
+    ((1, 8, 1, 64, 16, 4, 16, 8, 300, 0), "lut_valu"),         # 4 key sub-vectors
+    ((1, 8, 1, 256, 4, 16, 256, 8, 300, 0), "lut_valu"),
+])
+def test_attend_path_routing(lib, shape, path):
+    """vq_attend's kernel choice depends on the shape only; these pins keep
+    the benchmarked and tested shapes on the kernels they are meant for."""
+    assert api.vq_attend_path(*shape) == path
+
+
+def test_attend_path_rejects_what_attend_rejects(lib):
+    with pytest.raises(api.VQError):
+        api.vq_attend_path(1, 6, 1, 128, 8, 4, 256, 4, 100)      # H_q % H_kv != 0
+    with pytest.raises(api.VQError):
+        api.vq_attend_path(1, 8, 1, 128, 6, 4, 256, 8, 100)      # D % d_k != 0
+    with pytest.raises(api.VQError):
+        api.vq_attend_path(1, 8, 1, 128, 8, 4, 257, 8, 100)      # more than 256 centroids
+    assert lib.vq_attend_path(0, 8, 1, 128, 8, 4, 256, 8, 100, 0) == 0

@@ -21,7 +21,8 @@ import torch
 
 import oracle.vq_oracle as O
 from vector_quantized_kv_amd import synth
-from vector_quantized_kv_amd import (vq_attend, vq_decode, vq_encode, vq_encode_decode)
+from vector_quantized_kv_amd import (vq_attend, vq_attend_path, vq_decode, vq_encode,
+                                     vq_encode_decode)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -90,6 +91,12 @@ def run_attend(cfg, k_codes=None, v_codes=None, **over):
                     sliding_window=p["window"])
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+def path_of(c):
+    """The kernel family vq_attend runs for a test case's shape."""
+    return vq_attend_path(c["B"], c["H_q"], c["S_q"], c["D"], c["dk"], c["dv"],
+                          c["k_codebook"].shape[0], c["H_kv"], c["k_codes"].shape[2], c["window"])
 
 
 def oracle_attend(p, k_codes, v_codes, rows=None):
@@ -349,6 +356,43 @@ def test_split_invariance_and_gqa_equivalence():
     check_attn(a, oracle_attend(c, c["k_codes"], c["v_codes"]), "split/gqa")
 
 
+def test_stream_kernel_window_cuts():
+    """A sliding window much shorter than the rows on the streaming kernel
+    (B = 16, GQA-4, W = 2100 over ragged lengths up to 4096), every row."""
+    c = small_case(95, B=16, Hq=32, Hkv=8, Sq=1, D=128, dk=8, dv=4, S_cap=4096)
+    c["kv_lens"] = np.random.default_rng(96).integers(1, 4097, size=16).astype(np.int32)
+    c["kv_lens"][:3] = [4096, 2100, 2099]
+    c["causal"], c["window"] = True, 2100
+    assert path_of(c) == "stream"
+    out = run_attend(c)
+    ref = oracle_attend(c, c["k_codes"], c["v_codes"])
+    check_attn(out, ref, "stream window 2100")
+
+
+@pytest.mark.parametrize("transform,smooth,n_c", [
+    (False, "none", 256),     # no rotation, no smoothing
+    (True, "shared", 256),    # one smooth row for every kv head
+    (True, "per_head", 100),  # fewer centroids than codes the table holds
+    (False, "per_head", 7),
+])
+def test_stream_kernel_options(transform, smooth, n_c):
+    """The streaming kernel's query transform and codebook options, against
+    the oracle on every output row (B = 4, GQA-4, ragged lengths)."""
+    rng = np.random.default_rng(90 + n_c + 2 * int(transform))
+    # B * H_kv * 8192 = 2^18 unit-keys: large enough for the streaming kernel
+    c = small_case(91 + n_c, B=4, Hq=32, Hkv=8, Sq=1, D=128, dk=8, dv=4, n_c=n_c, S_cap=8192)
+    c["kv_lens"] = np.array([8192, 6000, 77, 8000], np.int32)
+    c["transform"] = transform
+    assert path_of(c) == "stream"
+    if smooth == "none":
+        c["smooth"] = None
+    elif smooth == "shared":
+        c["smooth"] = rng.uniform(0.5, 5, size=128).astype(np.float32)  # [D]: one row
+    out = run_attend(c)
+    ref = oracle_attend(c, c["k_codes"], c["v_codes"])
+    check_attn(out, ref, f"stream options transform{transform} smooth {smooth} n_c {n_c}")
+
+
 @pytest.mark.parametrize("Hq,Hkv,Sq,lens,causal,window", [
     (4, 2, 100, [400, 130, 60], True, 0),     # GQA-2: 128-row tiles span two heads; len < S_q
     (2, 2, 64, [400, 64, 0], True, 0),        # one full row tile per kv head; an empty row
@@ -362,6 +406,7 @@ def test_many_query_shapes(Hq, Hkv, Sq, lens, causal, window):
     c = small_case(50 + Sq, B=3, Hq=Hq, Hkv=Hkv, Sq=Sq, D=128, dk=8, dv=4, S_cap=400)
     c["kv_lens"] = np.array(lens, np.int32)
     c["causal"], c["window"] = causal, window
+    assert path_of(c) == "tile"
     out = run_attend(c)
     ref = oracle_attend(c, c["k_codes"], c["v_codes"])
     check_attn(out, ref, f"many-query Hq{Hq} Hkv{Hkv} Sq{Sq} causal{causal} W{window}")
@@ -372,7 +417,7 @@ def test_many_query_shapes(Hq, Hkv, Sq, lens, causal, window):
     (24, 1, [8192, 8000, 300, 64], True, 0),    # GQA-3: a 4-row unit is partly filled
     (16, 3, [8192, 2, 4097, 8191], True, 0),    # 2 query positions per row group; len < S_q
     (32, 1, [8192, 7000, 6000, 100], False, 0),
-    (8, 2, [8192, 8190, 5000, 2000], True, 8190),  # windowed (the window still spans the buffer)
+    (8, 2, [8192, 8190, 5000, 2000], True, 8191),  # a window as long as the buffer
 ])
 def test_stream_kernel_cases(Hq, Sq, lens, causal, window):
     """Decode-shaped problems large enough for the persistent streaming path
@@ -380,6 +425,7 @@ def test_stream_kernel_cases(Hq, Sq, lens, causal, window):
     c = small_case(70 + Hq + Sq, B=4, Hq=Hq, Hkv=8, Sq=Sq, D=128, dk=8, dv=4, S_cap=8192)
     c["kv_lens"] = np.array(lens, np.int32)
     c["causal"], c["window"] = causal, window
+    assert path_of(c) == "stream"
     out = run_attend(c)
     ref = oracle_attend(c, c["k_codes"], c["v_codes"])
     check_attn(out, ref, f"stream Hq{Hq} Sq{Sq} causal{causal} W{window}")

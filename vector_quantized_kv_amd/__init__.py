@@ -3,5 +3,6 @@
 The compute runs in libvq.so (hand-written HIP kernels for gfx950) behind the
 C ABI declared in include/vq.h; this package only marshals torch tensors to it.
 """
-from .api import (VQError, attend_workspace, vq_attend, vq_attend_workspace_bytes,  # noqa: F401
-                  vq_decode, vq_encode, vq_encode_decode, vq_supports_shape)
+from .api import (VQError, attend_workspace, vq_attend, vq_attend_path,  # noqa: F401
+                  vq_attend_workspace_bytes, vq_decode, vq_encode, vq_encode_decode,
+                  vq_supports_shape)

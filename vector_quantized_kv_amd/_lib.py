@@ -29,6 +29,7 @@ SIGNATURES = {
                                  c_void_p, c_int, c_int, c_void_p,
                                  c_void_p, c_int, c_void_p]),
     "vq_attend_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
+    "vq_attend_path": (c_int, [c_int] * 10),
     "vq_attend": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
                           c_void_p, c_void_p, c_int,
                           c_void_p, c_int, c_int,

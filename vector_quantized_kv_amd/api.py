@@ -148,6 +148,22 @@ def vq_attend_workspace_bytes(B, H_q, S_q, D, H_kv, S_cap, sliding_window=0) -> 
     return int(_lib.load().vq_attend_workspace_bytes(B, H_q, S_q, D, H_kv, S_cap, sliding_window))
 
 
+PATH_NAMES = {1: "stream", 2: "tile", 3: "lut_mfma", 4: "lut_valu"}
+
+
+def vq_attend_path(B, H_q, S_q, D, k_sub_dim, v_sub_dim, n_centroids, H_kv, S_cap,
+                   sliding_window=0) -> str:
+    """Name of the kernel family vq_attend runs for this shape ("stream",
+    "tile", "lut_mfma", "lut_valu"); raises VQError when vq_attend would
+    reject the shape. Host-only."""
+    lib = _lib.load()
+    p = int(lib.vq_attend_path(B, H_q, S_q, D, k_sub_dim, v_sub_dim, n_centroids, H_kv, S_cap,
+                               sliding_window))
+    if p not in PATH_NAMES:
+        raise VQError(VQ_ERR_UNSUPPORTED, lib.vq_last_error().decode())
+    return PATH_NAMES[p]
+
+
 def attend_workspace(q, k_codes, sliding_window=0):
     """A zero-filled workspace sized for vq_attend on these shapes."""
     B, Hq, Sq, D = q.shape

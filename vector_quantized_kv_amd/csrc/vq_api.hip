@@ -238,6 +238,31 @@ size_t vq_attend_workspace_bytes(int B, int H_q, int S_q, int D, int H_kv, int S
   return p.workspace_bytes;
 }
 
+int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
+                   int n_centroids, int H_kv, int S_cap, int sliding_window) {
+  g_last_error[0] = 0;
+  const char* what = "vq_attend_path";
+  if (B <= 0 || H_q <= 0 || S_q <= 0 || H_kv <= 0 || S_cap <= 0) {
+    fail(VQ_ERR_INVALID_ARGUMENT, "%s: sizes must be positive", what);
+    return 0;
+  }
+  if (H_q % H_kv != 0 || sliding_window < 0) {
+    fail(VQ_ERR_INVALID_ARGUMENT, "%s: H_q %% H_kv != 0 or sliding_window < 0", what);
+    return 0;
+  }
+  if (check_quantizer("vq_attend_path (keys)", D, n_centroids, k_sub_dim) ||
+      check_quantizer("vq_attend_path (values)", D, n_centroids, v_sub_dim))
+    return 0;
+  if ((D / k_sub_dim) % 4 != 0 || (D / v_sub_dim) % 4 != 0) {
+    fail(VQ_ERR_UNSUPPORTED, "%s: the numbers of key and value sub-vectors must be multiples of 4", what);
+    return 0;
+  }
+  const int path = attend_path(B, H_q, S_q, D, H_kv, S_cap, sliding_window, k_sub_dim, v_sub_dim,
+                               n_centroids);
+  if (!path) fail(VQ_ERR_UNSUPPORTED, "%s: no kernel fits this shape", what);
+  return path;
+}
+
 int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* k_codes,
               const float* k_codebook, int k_sub_dim, const float* smooth, int smooth_rows,
               int transform, const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,

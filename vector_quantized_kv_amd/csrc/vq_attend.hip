@@ -419,18 +419,32 @@ int attend_pick_rows(int rows, int nsk, int n_c, int dv, int nsv, int D, size_t*
   return 0;
 }
 
+int attend_path(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, int dk, int dv,
+                int n_c) {
+  if (tile_plan(B, Hq, Sq, D, Hkv, S_cap, window, dk, dv, n_c, nullptr)) return VQ_PATH_TILE;
+  if (stream_plan(B, Hq, Sq, D, Hkv, S_cap, window, dk, dv, n_c, nullptr, nullptr, nullptr))
+    return VQ_PATH_STREAM;
+  AttendPlan plan;
+  if (!plan_attend(B, Hq, Sq, D, Hkv, S_cap, window, &plan)) return 0;
+  int R = 0;
+  size_t lds = 0;
+  if (attend_mfma_plan(D, dv, D / dk, plan.rows, &R, &lds)) return VQ_PATH_LUT_MFMA;
+  if (attend_pick_rows(plan.rows, D / dk, n_c, dv, D / dv, D, &lds)) return VQ_PATH_LUT_VALU;
+  return 0;
+}
+
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_t st) {
-  {
+  const int path = attend_path(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c);
+  if (path == VQ_PATH_TILE) {
     TileParams tp;
-    if (tile_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c, &tp))
-      return launch_attend_tile(a, tp, st);
+    tile_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c, &tp);
+    return launch_attend_tile(a, tp, st);
   }
-  {
+  if (path == VQ_PATH_STREAM) {
     StreamParams sp;
     size_t lds = 0;
-    if (stream_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c, &sp, &lds,
-                    nullptr))
-      return launch_attend_stream(a, sp, lds, st);
+    stream_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c, &sp, &lds, nullptr);
+    return launch_attend_stream(a, sp, lds, st);
   }
   AttParams p;
   p.B = a.B; p.Hq = a.Hq; p.Sq = a.Sq; p.Hkv = a.Hkv; p.S_cap = a.S_cap;

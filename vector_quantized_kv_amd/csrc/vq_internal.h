@@ -112,6 +112,10 @@ size_t stream_workspace_bytes(int B, int Hq, int Sq, int D, int Hkv);
 hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds_bytes,
                                 hipStream_t st);
 
+// The VQ_PATH_* family launch_attend uses for a validated shape (0 if none).
+int attend_path(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, int dk, int dv,
+                int n_c);
+
 // Many-query kernel (prefill: at least 64 query rows per kv head; head dim
 // 128, key sub_dim 8, value sub_dim 4).
 struct TileParams {
