@@ -45,9 +45,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--mode", choices=["full", "attend", "encode", "copy"], default="full",
+    ap.add_argument("--mode", choices=["full", "attend", "encode", "encode_workload", "copy"],
+                    default="full",
                     help="attend/encode: only launch that entry point of the main workload "
-                         "--steps times (for profiler runs); copy: a plain elementwise copy "
+                         "--steps times (for profiler runs); encode_workload: only the key "
+                         "encode of [1, 8, 8192, 128] --steps times; copy: a plain elementwise copy "
                          "of 1 GiB --steps times (calibrates the HBM byte counters); these "
                          "modes print no JSON line")
     return ap.parse_args()
@@ -136,6 +138,17 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if args.mode == "encode_workload":
+        e = synth.encode()
+        ke, Ce, se = t(e["keys"]), t(e["k_codebook"]), t(e["smooth"])
+        codes_e = torch.zeros((1, 8, 8192, 16), dtype=torch.uint8, device=dev)
+        f_e = vq_encode(ke, Ce, 8, smooth=se, codes=codes_e, prepare=True)
+        for _ in range(args.warmup + args.steps):
+            f_e()
+        torch.cuda.synchronize()
+        log(f"[bench] mode={args.mode}: {args.warmup + args.steps} launches done")
+        return
 
     if args.mode == "copy":
         # 1 GiB read + 1 GiB written per launch: the reference point that turns

@@ -223,6 +223,39 @@ def test_encode_codebook_split_tiers(S):
     check_recon(rec.cpu().numpy(), O.decode(codes, C, s[0], True), "fp32", f"tiers S{S}")
 
 
+@pytest.mark.parametrize("D,d,n_c,B,H,S,transform,smooth", [
+    (128, 8, 256, 1, 2, 2085, True, "per_head"),   # the key workload's head shape
+    (128, 4, 256, 1, 3, 757, False, None),         # value encode: no transform, no smooth
+    (64, 4, 100, 1, 1, 4097, True, "shared"),      # partial last tile of centroids
+    (256, 16, 33, 1, 2, 2049, True, "per_head"),
+    (32, 8, 7, 1, 1, 16385, True, None),           # 4 sub-vectors per head
+])
+def test_encode_matrix_core_shapes(D, d, n_c, B, H, S, transform, smooth):
+    """Inputs of at least 65536 sub-vectors with sub_dim 4, 8 or 16 take the
+    matrix-core nearest-centroid search; codes (near-tie rule) from vq_encode and
+    vq_encode_decode agree with each other and the oracle, and the fp32
+    reconstructions with the oracle's.  The last step of each shape is ragged."""
+    rng = np.random.default_rng(700 + D + d + n_c)
+    k = synth.outlier_normal(rng, (B, H, S, D), 2)
+    s = None                                  # [H, D] per head, [D] shared
+    if smooth == "per_head":
+        s = synth.smooth_factors(k)
+    elif smooth == "shared":
+        s = np.ascontiguousarray(synth.smooth_factors(k)[0])
+    xt = O.forward_transform(k, s, transform).reshape(-1, d)
+    C = synth.sample_rows(rng, xt, n_c)
+    ds = None if s is None else dev(s)
+    rec, codes = vq_encode_decode(dev(k), dev(C), d, smooth=ds, transform=transform,
+                                  out_dtype=torch.float32)
+    codes_only = vq_encode(dev(k), dev(C), d, smooth=ds, transform=transform)
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy()
+    assert np.array_equal(codes_only.cpu().numpy(), codes)
+    check_codes(k, C, d, s, transform, codes, f"mfma D{D} d{d} n_c{n_c}")
+    check_recon(rec.cpu().numpy(), O.decode(codes, C, s, transform), "fp32",
+                f"mfma D{D} d{d} n_c{n_c}")
+
+
 def test_encode_append_and_row_offsets():
     rng = np.random.default_rng(2)
     B, H, S, D, d, S_cap = 3, 2, 5, 64, 4, 20

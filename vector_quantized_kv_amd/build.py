@@ -19,6 +19,8 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
     # never emit packed fp32 VALU ops (v_pk_add/mul/fma_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # results of the matrix instructions in ordinary VGPRs (no accvgpr reads)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -16,10 +16,13 @@
 // and the running argmin stay in registers.
 #include "vq_internal.h"
 
+#include <algorithm>
+
 namespace vq {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves of 64
+typedef float float4_t __attribute__((ext_vector_type(4)));  // 16x16 accumulator
 // Workgroup size of a kernel whose waves split the codebook CSPLIT ways:
 // one group of token-heads per workgroup when the codebook is split.
 template <int CSPLIT>
@@ -167,6 +170,7 @@ __device__ __forceinline__ void wht(float (&x)[DS], int j) {
 
 struct Dims {
   int B, H, S, n_c, smooth_rows, transform, S_cap, S_off, use_row_offsets, recon_dtype;
+  FastDiv div_S, div_H;  // by S and H (token-head indices below 2^31)
 };
 
 // MODE 0: encode; 1: encode + reconstruct; 2: decode (codes_in -> recon).
@@ -302,6 +306,315 @@ __global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kernel(
   }
 }
 
+// Nearest centroid as a dense contraction on the matrix cores.  For a
+// sub-vector x, |x - c|^2 = |x|^2 + (|c|^2 - 2 c.x), and |x|^2 is the same
+// for every centroid, so the argmin over c of |c|^2 - 2 c.x is the argmin of
+// the distance.  The contraction runs on v_mfma_f32_16x16x4_f32 (fp32
+// operands and accumulation): A = the codebook scaled by -2 (16 centroids
+// per tile, k = element), B = 16 sub-vectors, C starts from |c|^2.
+//
+// Layout: a wave step covers 64 sub-vector rows as four 16-row column groups
+// cg; lane l holds, for every cg, elements 4 i + l / 16 (i < DS / 4) of row
+// 16 cg + l mod 16, which is the B operand layout.  The rows' inputs are
+// loaded straight into it and the rotation runs in it: element bits 0-1 are
+// lane bits 4-5, the higher element bits are i, sub-vector bits 0-3 are lane
+// bits 0-3 and sub-vector bits 4-5 (32 or 64 sub-vectors per head) are cg.
+// The accumulator of tile T gives lane l the centroids 16 T + 4 (l / 16) + v
+// (v < 4) of its row; each lane keeps a running argmin over them in
+// increasing index order, and the four lanes of a row are merged at the end
+// (lowest index on ties).
+template <int D, int DS>
+__device__ __forceinline__ void wht_b(float (&x)[4][DS / 4], int lane) {
+  constexpr int NE = DS / 4;
+  constexpr int NSUB = D / DS;
+  constexpr int JL = NSUB < 16 ? NSUB : 16;  // sub-vector index range held in lane bits 0-3
+  // butterfly over a lane bit m: (lo, hi) -> (lo + hi, lo - hi)
+  auto lane_stage = [&](int m) {
+    const float sg = (lane & m) ? -1.f : 1.f;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const float y = __shfl_xor(x[cg][i], m);
+        x[cg][i] = fmaf(sg, x[cg][i], y);
+      }
+  };
+  lane_stage(16);
+  lane_stage(32);
+#pragma unroll
+  for (int hb = 1; hb < NE; hb <<= 1)
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+      for (int i = 0; i < NE; ++i)
+        if (!(i & hb)) {
+          const float a = x[cg][i], b = x[cg][i | hb];
+          x[cg][i] = a + b;
+          x[cg][i | hb] = a - b;
+        }
+#pragma unroll
+  for (int m = 1; m < JL; m <<= 1) lane_stage(m);
+#pragma unroll
+  for (int hb = 1; hb < NSUB / 16; hb <<= 1)
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+      if (!(cg & hb)) {
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+          const float a = x[cg][i], b = x[cg | hb][i];
+          x[cg][i] = a + b;
+          x[cg | hb][i] = a - b;
+        }
+      }
+  const float nrm = WhtNorm<D>::value;
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+    for (int i = 0; i < NE; ++i) x[cg][i] *= nrm;
+}
+
+template <int D, int DS, int MODE>
+__global__ __launch_bounds__(kThreads) void pvq_mfma_kernel(
+    const __half* __restrict__ keys, const float* __restrict__ cb, const float* __restrict__ smooth,
+    uint8_t* __restrict__ codes, void* __restrict__ recon, Dims d, RowOffsets offs) {
+  static_assert(DS % 4 == 0 && DS <= 16, "K steps of 4 elements");
+  constexpr int NSUB = D / DS;   // rows per token-head (<= 64)
+  constexpr int TPW = 64 / NSUB; // token-heads per wave step
+  constexpr int NE = DS / 4;     // matrix steps per tile and column group
+  constexpr int WPB = kThreads / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int q = lane >> 4, jl = lane & 15;
+
+  // LDS: A operands per tile ([T][lane][i] = -2 C[16 T + lane mod 16][4 i +
+  // lane / 16], zero past n_c) and |c|^2 (summed over e in order; +inf past
+  // n_c, so the padding to 16 tiles never wins a strict '<')
+  __shared__ float s_a[16 * 64 * NE];
+  __shared__ float s_norm[256];
+  {
+    const int c = threadIdx.x;
+    float n = INFINITY;
+    if (c < d.n_c) {
+      n = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) n = fmaf(cb[c * DS + e], cb[c * DS + e], n);
+    }
+    s_norm[c] = n;
+#pragma unroll
+    for (int r = 0; r < 4 * NE; ++r) {
+      const int idx = threadIdx.x + kThreads * r;          // [T][lane][i]
+      const int T = idx / (64 * NE), ln = (idx / NE) % 64, ii = idx % NE;
+      const int cc = 16 * T + (ln & 15);
+      s_a[idx] = cc < d.n_c ? -2.f * cb[cc * DS + 4 * ii + (ln >> 4)] : 0.f;
+    }
+  }
+
+  const int n_th = d.B * d.H * d.S;  // below 2^31 (the launcher checks)
+  const int n_steps = (n_th + TPW - 1) / TPW;
+  const int stride = (int)gridDim.x * WPB;
+
+  // Row 16 cg + jl of the step starting at token-head th0: token-head
+  // th0 + (16 cg + jl) / NSUB, sub-vector (16 cg + jl) mod NSUB.
+  auto th_of = [&](int th0, int cg) { return th0 + (16 * cg + jl) / NSUB; };
+  auto j_of = [&](int cg) { return (16 * cg + jl) % NSUB; };
+
+  uint16_t raw[4][NE];
+  float sv[4][NE];
+  auto load_rows = [&](int th0) {
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      int th = th_of(th0, cg);
+      th = th < n_th ? th : 0;
+      const uint16_t* p =
+          reinterpret_cast<const uint16_t*>(keys) + (long long)th * D + j_of(cg) * DS + q;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) raw[cg][i] = p[4 * i];
+      if (smooth) {
+        const int bh = (int)fast_div((uint32_t)th, d.div_S);
+        const int h = d.smooth_rows == 1 ? 0 : bh - (int)fast_div((uint32_t)bh, d.div_H) * d.H;
+        const float* sp = smooth + h * D + j_of(cg) * DS + q;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) sv[cg][i] = sp[4 * i];
+      }
+    }
+  };
+
+  int step = (int)blockIdx.x * WPB + wave;
+  load_rows((step < n_steps ? step : 0) * TPW);
+  __syncthreads();
+
+  for (; step < n_steps; step += stride) {
+    const int th0 = step * TPW;
+    float x[4][NE];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const uint16_t bits = raw[cg][i];
+        float v = th_of(th0, cg) < n_th ? __half2float(*reinterpret_cast<const __half*>(&bits)) : 0.f;
+        if (smooth) v = v / sv[cg][i];
+        x[cg][i] = v;
+      }
+    float svc[4][NE];  // this step's smooth factors, for the reconstruction
+    if constexpr (MODE == 1) {
+      if (smooth) {
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+          for (int i = 0; i < NE; ++i) svc[cg][i] = sv[cg][i];
+      }
+    }
+    // the next step's inputs are requested now and consumed next iteration
+    load_rows((step + stride < n_steps ? step + stride : step) * TPW);
+    if (d.transform) wht_b<D, DS>(x, lane);
+
+    // Tiles in order: stage T issues the matrix steps of tile T + 1 (all
+    // column groups; A and |c|^2 read from LDS one stage earlier) between the
+    // argmin updates of tile T.
+    struct TileIn {
+      float a[NE];
+      float4_t n;
+    };
+    auto tile_in = [&](int T) {
+      // re-read per stage (a compiler barrier keeps the 16 tiles' operands
+      // from being hoisted out of the step loop into live registers)
+      asm volatile("" ::: "memory");
+      TileIn t;
+      const float* ap = s_a + (T * 64 + lane) * NE;
+#pragma unroll
+      for (int i = 0; i < NE; ++i) t.a[i] = ap[i];
+      const float4 nv = *reinterpret_cast<const float4*>(s_norm + 16 * T + 4 * q);
+      t.n = float4_t{nv.x, nv.y, nv.z, nv.w};
+      return t;
+    };
+    auto chains = [&](const TileIn& t, float4_t (&acc)[4]) {
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) {
+        acc[cg] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.a[0], x[cg][0], t.n, 0, 0, 0);
+#pragma unroll
+        for (int i = 1; i < NE; ++i)
+          acc[cg] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.a[i], x[cg][i], acc[cg], 0, 0, 0);
+      }
+    };
+    float best[4];
+    int bi[4];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) { best[cg] = INFINITY; bi[cg] = 0; }
+    // kv[v] = 16 T + v for the tile being scanned, in registers the compiler
+    // cannot fold into constants: indices above 64 are no inline constants,
+    // and as literals they would be held in 256 registers across the loop
+    int kv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) asm volatile("v_mov_b32 %0, %1" : "=v"(kv[v]) : "n"(v));
+    auto scan = [&](const float4_t (&r)[4]) {
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (r[cg][v] < best[cg]) { best[cg] = r[cg][v]; bi[cg] = kv[v]; }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) kv[v] += 16;
+    };
+    float4_t acc[4];
+    chains(tile_in(0), acc);
+    TileIn nxt_in = tile_in(1);
+#pragma unroll
+    for (int T = 0; T < 16; ++T) {
+      float4_t r[4];
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) r[cg] = acc[cg];
+      if (T + 1 < 16) {
+        chains(nxt_in, acc);
+        if (T + 2 < 16) nxt_in = tile_in(T + 2);
+      }
+      scan(r);
+      // Pin the stage in program order (IR passes otherwise regroup the
+      // independent argmin chains by column group across all tiles, keeping
+      // every tile's accumulators live): the argmin state of tile T and the
+      // accumulators of tile T + 1 are materialized here.
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) asm volatile("" : "+v"(best[cg]), "+v"(bi[cg]), "+v"(acc[cg]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // merge the four lanes of each row (lane bits 4-5), lowest index on ties
+    int idx[4];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      float bv = best[cg];
+      int bx = bi[cg] + 4 * q;
+#pragma unroll
+      for (int m = 16; m <= 32; m <<= 1) {
+        const float ov = __shfl_xor(bv, m);
+        const int ox = __shfl_xor(bx, m);
+        if (ov < bv || (ov == bv && ox < bx)) { bv = ov; bx = ox; }
+      }
+      // (a row that never compares below +inf, e.g. NaN input, keeps a start index)
+      idx[cg] = min(bx, d.n_c - 1);
+    }
+
+    // lane l writes the code of row (cg = l / 16, l mod 16)
+    {
+      const int code = q == 0 ? idx[0] : (q == 1 ? idx[1] : (q == 2 ? idx[2] : idx[3]));
+      const int th = th0 + (16 * q + jl) / NSUB;
+      if (th < n_th) {
+        const int bh = (int)fast_div((uint32_t)th, d.div_S);
+        const int t = th - bh * d.S;
+        const int off = d.use_row_offsets ? offs.v[fast_div((uint32_t)bh, d.div_H)] : d.S_off;
+        codes[((long long)bh * d.S_cap + off + t) * NSUB + (16 * q + jl) % NSUB] = (uint8_t)code;
+      }
+    }
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+#pragma unroll
+        for (int i = 0; i < NE; ++i) x[cg][i] = cb[idx[cg] * DS + 4 * i + q];
+      if (d.transform) wht_b<D, DS>(x, lane);  // H is its own inverse
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) {
+        const int th = th_of(th0, cg);
+        if (th >= n_th) continue;
+        const long long base = (long long)th * D + j_of(cg) * DS + q;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+          const float v = smooth ? x[cg][i] * svc[cg][i] : x[cg][i];
+          if (d.recon_dtype == 1)
+            reinterpret_cast<__half*>(recon)[base + 4 * i] = __float2half_rn(v);
+          else
+            reinterpret_cast<float*>(recon)[base + 4 * i] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int D, int DS, int MODE>
+void launch_mfma(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStream_t st) {
+  constexpr int NSUB = D / DS;
+  // as many workgroups as are resident at once (one pass of waves over the
+  // steps, no partial second round), from the kernel's own occupancy
+  static int resident[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) dev = 0;
+  if (resident[dev] <= 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pvq_mfma_kernel<D, DS, MODE>, kThreads,
+                                                      0) != hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    resident[dev] = per_cu * cus;
+  }
+  const long long n_th = (long long)a.B * a.H * a.S;
+  const long long n_steps = (n_th + 64 / NSUB - 1) / (64 / NSUB);
+  const long long want = (n_steps + kThreads / 64 - 1) / (kThreads / 64);
+  const unsigned blocks = (unsigned)std::min(want, (long long)resident[dev]);
+  hipLaunchKernelGGL((pvq_mfma_kernel<D, DS, MODE>), dim3(blocks), dim3(kThreads), 0, st, a.keys,
+                     a.codebook, a.smooth, a.codes, a.recon, d, o);
+}
+
 template <int D, int DS, int MODE, int CSPLIT>
 void launch_one(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStream_t st) {
   constexpr int NSUB = D / DS;
@@ -319,7 +632,7 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
   const long long n_th = (long long)a.B * a.H * a.S;
   if ((n_th + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidValue;
   Dims d{a.B, a.H, a.S, a.n_c, a.smooth_rows, a.transform, a.S_cap, a.S_off,
-         a.use_row_offsets, a.recon_dtype};
+         a.use_row_offsets, a.recon_dtype, make_fastdiv((uint32_t)a.S), make_fastdiv((uint32_t)a.H)};
   RowOffsets o{};
   if (offs) o = *offs;
   // Fewer lanes than about four waves per CU (256 CUs): split the codebook
@@ -327,6 +640,14 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
   // token-heads, so short appends (one token per row) are not latency
   // bound; below one wave per CU, 16 ways (16 waves per workgroup).
   const int split = n_th * NSUB < 256LL * 64 ? 16 : (n_th * NSUB < 256LL * 64 * 4 ? 4 : 1);
+  // Enough sub-vectors to fill the chip: nearest centroid on the matrix cores.
+  if constexpr (DS % 4 == 0) {
+    if (split == 1 && mode != 2 && n_th < (1LL << 31)) {
+      if (mode == 0) launch_mfma<D, DS, 0>(a, d, o, st);
+      else launch_mfma<D, DS, 1>(a, d, o, st);
+      return hipGetLastError();
+    }
+  }
   switch (mode) {
     case 0:
       if (split == 16) launch_one<D, DS, 0, 16>(a, d, o, st);
