@@ -256,6 +256,23 @@ def test_encode_matrix_core_shapes(D, d, n_c, B, H, S, transform, smooth):
                 f"mfma D{D} d{d} n_c{n_c}")
 
 
+def test_encode_matrix_core_rescaled_steps():
+    """Sub-vectors far larger than every centroid leave the fp16 range at the
+    codebook's scale; the steps holding them take their own scale (and seeds),
+    the others keep the codebook's.  Every 7th token is 64x larger and the
+    codebook comes from the unscaled tokens, so both kinds of step occur."""
+    rng = np.random.default_rng(811)
+    B, H, S, D, d = 1, 2, 2085, 128, 8
+    k = synth.outlier_normal(rng, (B, H, S, D), 2)
+    C = synth.sample_rows(rng, O.forward_transform(k, None, True).reshape(-1, d), 256)
+    k[:, :, ::7] = (k[:, :, ::7].astype(np.float32) * 64).astype(np.float16)
+    rec, codes = vq_encode_decode(dev(k), dev(C), d, smooth=None, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy()
+    check_codes(k, C, d, None, True, codes, "rescaled steps")
+    check_recon(rec.cpu().numpy(), O.decode(codes, C, None, True), "fp32", "rescaled steps")
+
+
 def test_encode_append_and_row_offsets():
     rng = np.random.default_rng(2)
     B, H, S, D, d, S_cap = 3, 2, 5, 64, 4, 20

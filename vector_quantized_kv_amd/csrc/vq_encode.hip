@@ -17,6 +17,7 @@
 #include "vq_internal.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace vq {
 namespace {
@@ -588,9 +589,316 @@ __global__ __launch_bounds__(kThreads) void pvq_mfma_kernel(
   }
 }
 
+// Sub-vectors of 8: the same search on v_mfma_f32_32x32x8_f16, whose K of
+// 8 is one sub-vector, with each fp32 operand split into two fp16 parts
+// (hi = fp16(v), lo = fp16(v - hi)) and three passes hi.hi + lo.hi + hi.lo
+// (the dropped lo.lo term is below 2^-22 of the product).  Operands are
+// scaled by powers of two first: the codebook by 2^sc (largest magnitude in
+// [2^13, 2^14)), the sub-vectors of a step by the same 2^sc, so |c|^2 2^2sc
+// seeds the accumulator unchanged; a step whose values would leave the fp16
+// range at that scale takes its own 2^s and seeds with |c|^2 2^(s + sc)
+// (both forms are 2^(s + sc) (|c|^2 - 2 c.x), whose argmin is the same).
+//
+// Layout: a wave step covers 64 rows as two 32-row column groups g; lane l
+// holds elements 4 (l / 32) + u (u < 4) of row 32 g + l mod 32 (the B
+// operand), loaded as 8 contiguous bytes and rotated in place: element bits
+// 0-1 are u, element bit 2 is lane bit 5, sub-vector bits are lane bits 0-4.
+// Tile T gives lane l the centroids 32 T + 8 (v / 4) + 4 (l / 32) + v mod 4
+// (v < 16) of its row; lanes l and l ^ 32 hold the two halves.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+template <int D>
+__device__ __forceinline__ void wht_b8(float (&x)[2][4], int lane) {
+  constexpr int NSUB = D / 8;  // 4..32: sub-vector bits are lane bits 0..4
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+#pragma unroll
+    for (int hb = 1; hb < 4; hb <<= 1)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (!(u & hb)) {
+          const float a = x[g][u], b = x[g][u | hb];
+          x[g][u] = a + b;
+          x[g][u | hb] = a - b;
+        }
+  }
+  auto lane_stage = [&](int m) {
+    const float sg = (lane & m) ? -1.f : 1.f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[g][u] = fmaf(sg, x[g][u], __shfl_xor(x[g][u], m));
+  };
+  lane_stage(32);
+#pragma unroll
+  for (int m = 1; m < NSUB; m <<= 1) lane_stage(m);
+  const float nrm = WhtNorm<D>::value;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[g][u] *= nrm;
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads) void pvq_f16_kernel(
+    const __half* __restrict__ keys, const float* __restrict__ cb, const float* __restrict__ smooth,
+    uint8_t* __restrict__ codes, void* __restrict__ recon, Dims d, RowOffsets offs) {
+  constexpr int DS = 8;
+  constexpr int NSUB = D / DS;   // rows per token-head (4..32)
+  constexpr int TPW = 64 / NSUB; // token-heads per wave step
+  constexpr int WPB = kThreads / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hi = lane >> 5, l32 = lane & 31;
+
+  // codebook scale 2^sc: the largest |C| lands in [2^13, 2^14)
+  __shared__ float s_red[kThreads / 64];
+  __shared__ half4_t s_ah[8 * 64], s_al[8 * 64];  // A operands [T][lane], hi and lo parts
+  __shared__ float s_norm[256];                    // |c 2^sc|^2, +inf past n_c
+  __shared__ float s_seeded[kThreads / 64][256];   // per wave: s_norm 2^(s - sc) of a rescaled step
+  int sc;
+  {
+    const int c = threadIdx.x;
+    float m = 0.f;
+    if (c < d.n_c) {
+#pragma unroll
+      for (int e = 0; e < DS; ++e) m = fmaxf(m, fabsf(cb[c * DS + e]));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    sc = m > 0.f ? 14 - __builtin_amdgcn_frexp_expf(m) : 0;
+    float n = INFINITY;
+    if (c < d.n_c) {
+      n = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) {
+        const float v = ldexpf(cb[c * DS + e], sc);
+        n = fmaf(v, v, n);
+      }
+    }
+    s_norm[c] = n;
+    // entries (T, ln) for T = 2 (threadIdx / 64) + r
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int T = 2 * wave + r;
+      const int cc = 32 * T + l32;
+      half4_t ah, al;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float v = cc < d.n_c ? -2.f * ldexpf(cb[cc * DS + 4 * hi + u], sc) : 0.f;
+        ah[u] = (_Float16)v;
+        al[u] = (_Float16)(v - (float)ah[u]);
+      }
+      s_ah[T * 64 + lane] = ah;
+      s_al[T * 64 + lane] = al;
+    }
+  }
+
+  const int n_th = d.B * d.H * d.S;  // below 2^31 (the launcher checks)
+  const int n_steps = (n_th + TPW - 1) / TPW;
+  const int stride = (int)gridDim.x * WPB;
+  // row 32 g + l32 of the step at token-head th0
+  auto th_of = [&](int th0, int g) { return th0 + (32 * g + l32) / NSUB; };
+  auto j_of = [&](int g) { return (32 * g + l32) % NSUB; };
+
+  uint2 raw[2];
+  float4 sv[2];
+  auto load_rows = [&](int th0) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      int th = th_of(th0, g);
+      th = th < n_th ? th : 0;
+      raw[g] = *reinterpret_cast<const uint2*>(keys + (long long)th * D + j_of(g) * DS + 4 * hi);
+      if (smooth) {
+        const int bh = (int)fast_div((uint32_t)th, d.div_S);
+        const int h = d.smooth_rows == 1 ? 0 : bh - (int)fast_div((uint32_t)bh, d.div_H) * d.H;
+        sv[g] = *reinterpret_cast<const float4*>(smooth + h * D + j_of(g) * DS + 4 * hi);
+      }
+    }
+  };
+
+  int step = (int)blockIdx.x * WPB + wave;
+  load_rows((step < n_steps ? step : 0) * TPW);
+  __syncthreads();
+
+  for (; step < n_steps; step += stride) {
+    const int th0 = step * TPW;
+    float x[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const bool valid = th_of(th0, g) < n_th;
+      const uint32_t w[2] = {raw[g].x, raw[g].y};
+      const float svv[4] = {sv[g].x, sv[g].y, sv[g].z, sv[g].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint16_t b = (uint16_t)(w[u >> 1] >> (16 * (u & 1)));
+        float v = valid ? __half2float(*reinterpret_cast<const __half*>(&b)) : 0.f;
+        if (smooth) v = v / svv[u];
+        x[g][u] = v;
+      }
+    }
+    float4 svc[2];  // this step's smooth factors, for the reconstruction
+    if constexpr (MODE == 1) {
+      svc[0] = sv[0];
+      svc[1] = sv[1];
+    }
+    load_rows((step + stride < n_steps ? step + stride : step) * TPW);
+    if (d.transform) wht_b8<D>(x, lane);
+
+    // the step's scale: 2^sc unless that would leave the fp16 range
+    float mx = 0.f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fabsf(x[g][u]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    int s = sc;
+    const float* nrm = s_norm;  // accumulator seeds |c 2^sc|^2 2^(s - sc)
+    if (ldexpf(mx, sc) >= 32768.f) {
+      s = 14 - __builtin_amdgcn_frexp_expf(mx);
+      // this wave's own seeds (its LDS accesses run in issue order, so the
+      // reads below see them)
+      float* w = s_seeded[wave];
+      const float4 nv = *reinterpret_cast<const float4*>(s_norm + 4 * lane);
+      const float f = ldexpf(1.f, s - sc);
+      *reinterpret_cast<float4*>(w + 4 * lane) = make_float4(nv.x * f, nv.y * f, nv.z * f, nv.w * f);
+      nrm = w;
+    }
+    half4_t bh[2], bl[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float v = ldexpf(x[g][u], s);
+        bh[g][u] = (_Float16)v;
+        bl[g][u] = (_Float16)(v - (float)bh[g][u]);
+      }
+
+    struct TileIn {
+      half4_t ah, al;
+      float16_t n;
+    };
+    float best[2] = {INFINITY, INFINITY};
+    int bi[2] = {0, 0}, bt[2] = {0, 0};  // offset in the tile, tile of the running minimum
+    auto tile_in = [&](int T) {
+      // re-read per stage (a compiler barrier keeps the 8 tiles' operands
+      // from being hoisted out of the step loop into live registers)
+      asm volatile("" ::: "memory");
+      TileIn t;
+      t.ah = s_ah[T * 64 + lane];
+      t.al = s_al[T * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 nv = *reinterpret_cast<const float4*>(nrm + 32 * T + 8 * q + 4 * hi);
+        t.n[4 * q] = nv.x; t.n[4 * q + 1] = nv.y; t.n[4 * q + 2] = nv.z; t.n[4 * q + 3] = nv.w;
+      }
+      return t;
+    };
+    auto chains = [&](const TileIn& t, float16_t (&acc)[2]) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bh[0], t.n, 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bh[1], t.n, 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.al, bh[0], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.al, bh[1], acc[1], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bl[0], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bl[1], acc[1], 0, 0, 0);
+    };
+    // candidates in increasing index order: offsets 8 (v / 4) + v mod 4 are
+    // inline constants; the tile is recorded once per tile if it improved
+    auto scan = [&](const float16_t (&r)[2], int T) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float before = best[g];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (r[g][v] < best[g]) { best[g] = r[g][v]; bi[g] = 8 * (v >> 2) + (v & 3); }
+        if (best[g] < before) bt[g] = T;
+      }
+    };
+    float16_t acc[2];
+    chains(tile_in(0), acc);
+    TileIn nxt_in = tile_in(1);
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      float16_t r[2] = {acc[0], acc[1]};
+      if (T + 1 < 8) {
+        chains(nxt_in, acc);
+        if (T + 2 < 8) nxt_in = tile_in(T + 2);
+      }
+      scan(r, T);
+      // Pin the stage in program order (IR passes otherwise regroup the
+      // independent argmin chains across all tiles, keeping every tile's
+      // accumulators live).
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        asm volatile("" : "+v"(best[g]), "+v"(bi[g]), "+v"(bt[g]), "+v"(acc[g]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // merge lanes l and l ^ 32 (the two halves of every tile), lowest index on ties
+    int idx[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float bv = best[g];
+      int bx = 32 * bt[g] + bi[g] + 4 * hi;
+      const float ov = __shfl_xor(bv, 32);
+      const int ox = __shfl_xor(bx, 32);
+      if (ov < bv || (ov == bv && ox < bx)) bx = ox;
+      // (a row that never compares below +inf, e.g. NaN input, keeps a start index)
+      idx[g] = min(bx, d.n_c - 1);
+    }
+
+    // lane l writes the code of row (g = l / 32, l mod 32)
+    {
+      const int code = hi ? idx[1] : idx[0];
+      const int th = th_of(th0, hi);
+      if (th < n_th) {
+        const int bhh = (int)fast_div((uint32_t)th, d.div_S);
+        const int t = th - bhh * d.S;
+        const int off = d.use_row_offsets ? offs.v[fast_div((uint32_t)bhh, d.div_H)] : d.S_off;
+        codes[((long long)bhh * d.S_cap + off + t) * NSUB + j_of(hi)] = (uint8_t)code;
+      }
+    }
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float4 cv = *reinterpret_cast<const float4*>(cb + idx[g] * DS + 4 * hi);
+        x[g][0] = cv.x; x[g][1] = cv.y; x[g][2] = cv.z; x[g][3] = cv.w;
+      }
+      if (d.transform) wht_b8<D>(x, lane);  // H is its own inverse
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int th = th_of(th0, g);
+        if (th >= n_th) continue;
+        float o[4] = {x[g][0], x[g][1], x[g][2], x[g][3]};
+        if (smooth) {
+          o[0] *= svc[g].x; o[1] *= svc[g].y; o[2] *= svc[g].z; o[3] *= svc[g].w;
+        }
+        const long long base = (long long)th * D + j_of(g) * DS + 4 * hi;
+        if (d.recon_dtype == 1) {
+          const __half2 a = __floats2half2_rn(o[0], o[1]), b = __floats2half2_rn(o[2], o[3]);
+          uint2 u;
+          u.x = *reinterpret_cast<const uint32_t*>(&a);
+          u.y = *reinterpret_cast<const uint32_t*>(&b);
+          *reinterpret_cast<uint2*>(reinterpret_cast<__half*>(recon) + base) = u;
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(recon) + base) =
+              make_float4(o[0], o[1], o[2], o[3]);
+        }
+      }
+    }
+  }
+}
+
 template <int D, int DS, int MODE>
 void launch_mfma(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStream_t st) {
   constexpr int NSUB = D / DS;
+  // sub-vectors of 8 run the split-fp16 kernel, 4 and 16 the fp32 one
+  auto kern = DS == 8 ? pvq_f16_kernel<D, MODE> : pvq_mfma_kernel<D, DS, MODE>;
   // as many workgroups as are resident at once (one pass of waves over the
   // steps, no partial second round), from the kernel's own occupancy
   static int resident[64];
@@ -599,8 +907,8 @@ void launch_mfma(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStr
   if (dev < 0 || dev >= 64) dev = 0;
   if (resident[dev] <= 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pvq_mfma_kernel<D, DS, MODE>, kThreads,
-                                                      0) != hipSuccess || per_cu <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess ||
+        per_cu <= 0)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
@@ -611,8 +919,8 @@ void launch_mfma(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStr
   const long long n_steps = (n_th + 64 / NSUB - 1) / (64 / NSUB);
   const long long want = (n_steps + kThreads / 64 - 1) / (kThreads / 64);
   const unsigned blocks = (unsigned)std::min(want, (long long)resident[dev]);
-  hipLaunchKernelGGL((pvq_mfma_kernel<D, DS, MODE>), dim3(blocks), dim3(kThreads), 0, st, a.keys,
-                     a.codebook, a.smooth, a.codes, a.recon, d, o);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, st, a.keys, a.codebook, a.smooth,
+                     a.codes, a.recon, d, o);
 }
 
 template <int D, int DS, int MODE, int CSPLIT>
