@@ -453,7 +453,9 @@ __global__ __launch_bounds__(kThreads) void pvq_mfma_kernel(
       for (int i = 0; i < NE; ++i) {
         const uint16_t bits = raw[cg][i];
         float v = th_of(th0, cg) < n_th ? __half2float(*reinterpret_cast<const __half*>(&bits)) : 0.f;
-        if (smooth) v = v / sv[cg][i];
+        // x / s as x * rcp(s) (within 2 ulp of the quotient; such a
+        // difference can only move a code at a near-tie)
+        if (smooth) v = v * __builtin_amdgcn_rcpf(sv[cg][i]);
         x[cg][i] = v;
       }
     float svc[4][NE];  // this step's smooth factors, for the reconstruction
@@ -737,7 +739,9 @@ __global__ __launch_bounds__(kThreads) void pvq_f16_kernel(
       for (int u = 0; u < 4; ++u) {
         const uint16_t b = (uint16_t)(w[u >> 1] >> (16 * (u & 1)));
         float v = valid ? __half2float(*reinterpret_cast<const __half*>(&b)) : 0.f;
-        if (smooth) v = v / svv[u];
+        // x / s as x * rcp(s) (within 2 ulp of the quotient; such a
+        // difference can only move a code at a near-tie)
+        if (smooth) v = v * __builtin_amdgcn_rcpf(svv[u]);
         x[g][u] = v;
       }
     }
