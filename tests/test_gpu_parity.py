@@ -297,6 +297,40 @@ def test_encode_append_and_row_offsets():
         assert np.all(got[b][:, mask] == 0xAB)
 
 
+@pytest.mark.parametrize("d", [8, 4])
+def test_encode_matrix_core_append_offsets(d):
+    """The matrix-core encode paths (>= 65536 sub-vectors) writing at S_off and
+    at per-row offsets: codes land in the right slots, byte-exact with the
+    oracle away from near-ties, and no other slot is touched."""
+    rng = np.random.default_rng(900 + d)
+    B, H, S, D, S_cap = 4, 8, 600, 128, 1600
+    k = synth.outlier_normal(rng, (B, H, S, D), 2)
+    s = synth.smooth_factors(k)
+    C = synth.sample_rows(rng, O.forward_transform(k, s, True).reshape(-1, d), 256)
+    ref, gap = O.encode(k, C, d, s, True)
+    near = gap < NEAR_TIE
+    for offs in (None, [0, 1000, 7, 419]):
+        buf = torch.full((B, H, S_cap, D // d), 0xAB, dtype=torch.uint8, device=DEV)
+        if offs is None:
+            vq_encode(dev(k), dev(C), d, smooth=dev(s), codes=buf, S_off=333)
+            offs_b = [333] * B
+        else:
+            vq_encode(dev(k), dev(C), d, smooth=dev(s), codes=buf, row_offsets=offs)
+            offs_b = offs
+        torch.cuda.synchronize()
+        got = buf.cpu().numpy()
+        n_mis = 0
+        for b, o in enumerate(offs_b):
+            blk = got[b, :, o:o + S].astype(np.int64)
+            mis = blk != ref[b]
+            assert np.all(near[b][mis]), f"d{d} offs {offs}: mismatches away from near-ties"
+            n_mis += int(mis.sum())
+            mask = np.ones(S_cap, bool)
+            mask[o:o + S] = False
+            assert np.all(got[b][:, mask] == 0xAB)
+        print(f"[codes] append d{d} offs {offs}: {n_mis} near-tie mismatches")
+
+
 # ----------------------------------------------------------------------------
 # decode attention over random codes
 # ----------------------------------------------------------------------------
