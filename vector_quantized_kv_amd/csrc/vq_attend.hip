@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 }
 
 // One block per output row: combine the splits with the log-sum-exp rule.
-template <int D>
+template <int D, int kRound>
 __global__ __launch_bounds__(D) void attend_merge_kernel(const float* __restrict__ part,
                                                           __half* __restrict__ out, AttParams p) {
   const int row = blockIdx.x;  // ((b * Hq + h) * Sq + i)
@@ -321,15 +321,42 @@ __global__ __launch_bounds__(D) void attend_merge_kernel(const float* __restrict
   const float* base = part + ((size_t)unit * p.n_rgroups + rg) * p.n_split * p.R * (D + 2) +
                       (size_t)r * (D + 2);
   const size_t stride = (size_t)p.R * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, base[s * stride]);
-  float lsum = 0.f, a = 0.f;
-  for (int s = 0; s < p.n_split; ++s) {
-    const float ms = base[s * stride];
-    if (ms == -INFINITY) continue;
-    const float om = exp2f(ms - M);
-    lsum += om * base[s * stride + 1];
-    a += om * base[s * stride + 2 + threadIdx.x];
+  // kRound splits per round: their (m, l) and the thread's accumulator value
+  // are requested together (clamped addresses, masked values: no branch
+  // between the loads), then folded into running sums rescaled to the
+  // running max
+  float M = -INFINITY, lsum = 0.f, a = 0.f;
+  for (int s0 = 0; s0 < p.n_split; s0 += kRound) {
+    float ms[kRound], ls[kRound], as[kRound];
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+      const int sc = min(s0 + k, p.n_split - 1);
+      const float* sp = base + sc * stride;
+      ms[k] = sp[0];
+      ls[k] = sp[1];
+      as[k] = sp[2 + threadIdx.x];
+    }
+    // past the last split, or an empty split (its accumulator is not
+    // written): weight zero, and the unwritten values never enter a product
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+      if (s0 + k >= p.n_split) ms[k] = -INFINITY;
+      if (ms[k] == -INFINITY) { ls[k] = 0.f; as[k] = 0.f; }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) Mn = fmaxf(Mn, ms[k]);
+    if (Mn == -INFINITY) continue;
+    const float al = M == -INFINITY ? 0.f : exp2f(M - Mn);
+    lsum *= al;
+    a *= al;
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+      const float w = ms[k] == -INFINITY ? 0.f : exp2f(ms[k] - Mn);
+      lsum += w * ls[k];
+      a += w * as[k];
+    }
+    M = Mn;
   }
   out[(size_t)row * D + threadIdx.x] = __float2half_rn(lsum > 0.f ? a / lsum : 0.f);
 }
@@ -361,16 +388,22 @@ hipError_t launch_d(const AttendArgs& a, const AttParams& p, size_t lds_bytes, h
 
 }  // namespace
 
-hipError_t launch_attend_merge(const AttendArgs& a, const AttParams& p, hipStream_t st) {
+template <int kRound>
+hipError_t launch_merge_r(const AttendArgs& a, const AttParams& p, hipStream_t st) {
   const dim3 grid(a.B * a.Hq * a.Sq);
   switch (a.D) {
-    case 32: hipLaunchKernelGGL((attend_merge_kernel<32>), grid, dim3(32), 0, st, a.partials, a.out, p); break;
-    case 64: hipLaunchKernelGGL((attend_merge_kernel<64>), grid, dim3(64), 0, st, a.partials, a.out, p); break;
-    case 128: hipLaunchKernelGGL((attend_merge_kernel<128>), grid, dim3(128), 0, st, a.partials, a.out, p); break;
-    case 256: hipLaunchKernelGGL((attend_merge_kernel<256>), grid, dim3(256), 0, st, a.partials, a.out, p); break;
+    case 32: hipLaunchKernelGGL((attend_merge_kernel<32, kRound>), grid, dim3(32), 0, st, a.partials, a.out, p); break;
+    case 64: hipLaunchKernelGGL((attend_merge_kernel<64, kRound>), grid, dim3(64), 0, st, a.partials, a.out, p); break;
+    case 128: hipLaunchKernelGGL((attend_merge_kernel<128, kRound>), grid, dim3(128), 0, st, a.partials, a.out, p); break;
+    case 256: hipLaunchKernelGGL((attend_merge_kernel<256, kRound>), grid, dim3(256), 0, st, a.partials, a.out, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attend_merge(const AttendArgs& a, const AttParams& p, hipStream_t st) {
+  // splits fetched per round: all of a short split list at once
+  return p.n_split <= 4 ? launch_merge_r<4>(a, p, st) : launch_merge_r<16>(a, p, st);
 }
 
 bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, AttendPlan* pl) {
