@@ -17,6 +17,7 @@
 #include "vq_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace vq {
@@ -902,14 +903,18 @@ template <int D, int DS, int MODE>
 void launch_mfma(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStream_t st) {
   constexpr int NSUB = D / DS;
   // sub-vectors of 8 run the split-fp16 kernel, 4 and 16 the fp32 one
-  auto kern = DS == 8 ? pvq_f16_kernel<D, MODE> : pvq_mfma_kernel<D, DS, MODE>;
+  void (*kern)(const __half*, const float*, const float*, uint8_t*, void*, Dims, RowOffsets);
+  if constexpr (DS == 8) kern = pvq_f16_kernel<D, MODE>;
+  else kern = pvq_mfma_kernel<D, DS, MODE>;
   // as many workgroups as are resident at once (one pass of waves over the
-  // steps, no partial second round), from the kernel's own occupancy
-  static int resident[64];
+  // steps, no partial second round), from the kernel's own occupancy; cached
+  // per device (any thread may launch: relaxed atomics, same value if raced)
+  static std::atomic<int> resident[64];
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev < 0 || dev >= 64) dev = 0;
-  if (resident[dev] <= 0) {
+  int res = resident[dev].load(std::memory_order_relaxed);
+  if (res <= 0) {
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, 0) != hipSuccess ||
         per_cu <= 0)
@@ -917,12 +922,13 @@ void launch_mfma(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStr
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    resident[dev] = per_cu * cus;
+    res = per_cu * cus;
+    resident[dev].store(res, std::memory_order_relaxed);
   }
   const long long n_th = (long long)a.B * a.H * a.S;
   const long long n_steps = (n_th + 64 / NSUB - 1) / (64 / NSUB);
   const long long want = (n_steps + kThreads / 64 - 1) / (kThreads / 64);
-  const unsigned blocks = (unsigned)std::min(want, (long long)resident[dev]);
+  const unsigned blocks = (unsigned)std::min(want, (long long)res);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, st, a.keys, a.codebook, a.smooth,
                      a.codes, a.recon, d, o);
 }
