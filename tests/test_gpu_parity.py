@@ -513,3 +513,33 @@ def test_stream_kernel_cases(Hq, Sq, lens, causal, window):
     out = run_attend(c)
     ref = oracle_attend(c, c["k_codes"], c["v_codes"])
     check_attn(out, ref, f"stream Hq{Hq} Sq{Sq} causal{causal} W{window}")
+
+
+def test_stream_kernel_workspace_reuse():
+    """The workspace's contents on entry are ignored: one workspace filled
+    with random bytes, then reused by streaming-kernel calls of two shapes
+    in turn (and by repeated calls), gives every call the oracle's result."""
+    cases = []
+    for seed, Hq, lens in [(301, 32, [8192, 5000, 0, 1]), (302, 24, [8000, 8192, 300, 64])]:
+        c = small_case(seed, B=4, Hq=Hq, Hkv=8, Sq=1, D=128, dk=8, dv=4, S_cap=8192)
+        c["kv_lens"] = np.array(lens, np.int32)
+        c["causal"], c["window"] = True, 0
+        assert path_of(c) == "stream"
+        cases.append(c)
+    n = max(api_workspace_bytes(c) for c in cases)
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV)
+    refs = [oracle_attend(c, c["k_codes"], c["v_codes"]) for c in cases]
+    args = [dict(q=dev(c["q"]), kc=dev(c["k_codes"]), kb=dev(c["k_codebook"]), vc=dev(c["v_codes"]),
+                 vb=dev(c["v_codebook"]), sm=dev(c["smooth"]), lens=dev(c["kv_lens"])) for c in cases]
+    for it, i in enumerate([0, 1, 0, 1, 1, 0, 0] + [0, 1] * 8):
+        c, a = cases[i], args[i]
+        out = vq_attend(a["q"], a["kc"], a["kb"], a["vc"], a["vb"], scale=c["scale"], smooth=a["sm"],
+                        kv_lens=a["lens"], causal=True, sliding_window=0, workspace=ws)
+        torch.cuda.synchronize()
+        check_attn(out.cpu().numpy(), refs[i], f"workspace reuse call {it} (shape {i})")
+
+
+def api_workspace_bytes(c):
+    from vector_quantized_kv_amd import vq_attend_workspace_bytes
+    return vq_attend_workspace_bytes(c["B"], c["H_q"], c["S_q"], c["D"], c["H_kv"],
+                                     c["k_codes"].shape[2], c["window"])
