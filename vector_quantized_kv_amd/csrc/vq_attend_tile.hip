@@ -44,14 +44,20 @@ constexpr int tThreads = tW * 64;
 constexpr int tD = 128;
 constexpr int tRT = tW * 32;  // query rows per workgroup
 constexpr int tKT = 64;       // keys per tile
-constexpr uint32_t tKTab = 0;       // key codebook hi [256][8 replicas][8 fp16]  32 KiB
-constexpr uint32_t tKLo = 32768;    // key codebook lo [256][8 replicas][8 fp16]  32 KiB
-constexpr uint32_t tVTab = 65536;   // value codebook  [256][4 replicas][4 fp16]   8 KiB
-constexpr uint32_t tVT = 73728;     // V^T tile        [128 dims][72 fp16]        18 KiB
+// The 16 lanes that one b128 LDS read serves together need 16 distinct bank
+// quads (64 banks of 4 bytes): the high parts of the key codebook have 16
+// replicas (lane l reads replica l mod 16, so gathers by any codes are
+// conflict-free); the low parts have 8, where lanes l and l + 8 collide when
+// their codes have equal parity (LDS holds no more).
+constexpr uint32_t tKTab = 0;       // key codebook hi [256][16 replicas][8 fp16] 64 KiB
+constexpr uint32_t tKLo = 65536;    // key codebook lo [256][8 replicas][8 fp16]  32 KiB
+constexpr uint32_t tVTab = 98304;   // value codebook  [256][4 replicas][4 fp16]   8 KiB
+constexpr uint32_t tVT = 106496;    // V^T tile        [128 dims][72 fp16]        18 KiB
 constexpr uint32_t tRowB = 144;     // bytes per V^T / P row (64 fp16 + pad)
 constexpr uint32_t tPS = tVT + tD * tRowB;          // p per wave [32 rows][72 fp16]
 constexpr uint32_t tAl = tPS + tW * 32 * tRowB;     // per-wave row rescale factors
 constexpr uint32_t tLdsBytes = tAl + tW * 32 * 4;
+static_assert(tLdsBytes <= 160 * 1024, "LDS budget");
 constexpr float tLazyMargin = 8.f;
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -140,7 +146,8 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
     const u32x2_t hv = {pack_half2(v.x, v.y), pack_half2(v.z, v.w)};
 #pragma unroll
     for (int r = 4 * half; r < 4 * half + 4; ++r) {
-      lds_st<half8_t>(tKTab + code * 128 + r * 16, hi);
+      lds_st<half8_t>(tKTab + code * 256 + r * 16, hi);
+      lds_st<half8_t>(tKTab + code * 256 + (r + 8) * 16, hi);
       lds_st<half8_t>(tKLo + code * 128 + r * 16, lo);
     }
 #pragma unroll
@@ -256,10 +263,13 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
   }
 
   // ---- per-lane constants ---------------------------------------------------
-  const uint32_t kbase = tKTab + (uint32_t)(lane & 7) * 16u;     // key replica (128 B per code)
+  const uint32_t kbase = tKTab + (uint32_t)(lane & 15) * 16u;    // key hi replica (256 B per code)
+  const uint32_t kbase_lo = tKLo + (uint32_t)(lane & 7) * 16u;   // key lo replica (128 B per code)
   const uint32_t vtab = tVTab + (uint32_t)(lane & 3) * 8u;        // value replica
   const uint32_t ps = tPS + wave * 32 * tRowB;
-  // V^T decode task: lane quad (u = tid % 4) = keys 4 tq .. 4 tq + 3 x subs 4 sm .. 4 sm + 3
+  // V^T decode task: lane quad (u = tid % 4) = keys 4 tq .. 4 tq + 3 x subs 4 sm .. 4 sm + 3,
+  // quad tid / 4 = 16 sm + tq, so that the 32 lanes of each 8-byte V^T write
+  // (4 dims x 8 key quads) land on distinct bank pairs
   const int qu = tid & 3;
   const uint32_t tsel1 = qu < 2 ? 0x05040100u : 0x03020706u;
   const uint32_t tsel2 = (qu & 1) ? 0x03070105u : 0x06020400u;
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
     for (int mt = 0; mt < 4; ++mt)
       kc[mt] = *reinterpret_cast<const uint4*>(kc_row + (size_t)min(tb + 16 * mt + n16, tmax) * 16);
     const int quad = tid >> 2;  // 128 quads: (key quad tq, sub group sm)
-    const int tq = quad >> 3, sm = quad & 7;
+    const int tq = quad & 15, sm = quad >> 4;
     vc[0] = *reinterpret_cast<const uint32_t*>(vc_row + (size_t)min(tb + 4 * tq + qu, tmax) * 32 + 4 * sm);
   };
 
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
 #pragma unroll
     for (int j = 0; j < 1; ++j) {
       const int quad = tid >> 2;
-      const int tq = quad >> 3, sm = quad & 7;
+      const int tq = quad & 15, sm = quad >> 4;
       const uint32_t X = vc[j];
       const uint32_t Z = __builtin_amdgcn_perm(quad_perm<0x4E>(X), X, tsel1);
       const uint32_t Y = __builtin_amdgcn_perm(quad_perm<0xB1>(Z), Z, tsel2);
@@ -327,9 +337,9 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
       half8_t kv[4], kl[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t ka = (__builtin_amdgcn_ubfe(kw[c], 8u * kg, 8u) << 7) | kbase;
-        kv[c] = lds_ld<half8_t>(ka);
-        kl[c] = lds_ld<half8_t>(ka + (tKLo - tKTab));
+        const uint32_t code = __builtin_amdgcn_ubfe(kw[c], 8u * kg, 8u);
+        kv[c] = lds_ld<half8_t>((code << 8) | kbase);
+        kl[c] = lds_ld<half8_t>((code << 7) + kbase_lo);
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
