@@ -25,6 +25,12 @@
  *   - transform = 1 applies the normalized Sylvester Walsh-Hadamard matrix
  *     H[i][k] = (-1)^popcount(i & k) / sqrt(D) (symmetric, its own inverse);
  *     transform = 0 applies none (the value path).
+ *   - A randomized Hadamard rotation M = diag(sigma) . H, sigma in {-1, +1}^D
+ *     (an orthonormal choice of the fused encode-decode kernel's H_mat,
+ *     "Metal Kernels API", "VecInfer kernels"), is given as transform = 1
+ *     with smooth factors s * sigma: dividing by s * sigma is smoothing by s
+ *     followed by the sign flips, decode's multiply undoes both, and the
+ *     query's multiply by s * sigma is the dual transform (q * s) . M.
  *   - Device pointers must be 16-byte aligned (the kernels use 16-byte
  *     vector accesses); a misaligned pointer is rejected as an invalid
  *     argument.

@@ -30,7 +30,10 @@ the design notes of the repository):
       query multiplies (q * s).
   R2  the transform is the normalized Sylvester Hadamard matrix
       H[i, j] = (-1)^popcount(i & j) / sqrt(D), applied as a row vector
-      times H; H is symmetric and its own inverse.
+      times H; H is symmetric and its own inverse.  An explicit invertible
+      [D, D] matrix M (the encode_decode kernel's H_mat argument) may be
+      given instead: encode applies x . M, decode x~ . M^-1, and the query's
+      dual transform is q . (M^-1)^T.
   R3  sub-vector j covers dims [j*d, (j+1)*d).
   R4  one codebook [n_centroids, d] is shared by all sub-vectors.
   R5  squared L2 distance; exact ties resolve to the lowest index.
@@ -92,6 +95,22 @@ def _smooth_rows(smooth, n_heads: int, D: int):
     return s
 
 
+def _rotation(transform, D: int):
+    """(M, M^-1) of a transform argument: False/None -> no rotation; True ->
+    the normalized Sylvester matrix, its own inverse (R2); a [D, D] array ->
+    that matrix and its inverse (H_mat of vecinfer_encode_decode_metal,
+    "Metal Kernels API", "VecInfer kernels")."""
+    if isinstance(transform, np.ndarray):
+        m = np.asarray(transform, dtype=F64)
+        if m.shape != (D, D):
+            raise ValueError(f"transform matrix must be [{D}, {D}], got {m.shape}")
+        return m, np.linalg.inv(m)
+    if not transform:
+        return None, None
+    h = sylvester_hadamard(D)
+    return h, h
+
+
 # ----------------------------------------------------------------------------
 # Key transform and its inverse (readings R1, R2)
 # ----------------------------------------------------------------------------
@@ -107,21 +126,24 @@ def forward_transform(x: np.ndarray, smooth=None, transform: bool = False) -> np
     s = _smooth_rows(smooth, H, D)
     if s is not None:
         x = x / s[None, :, None, :]
-    if transform:
-        x = x @ sylvester_hadamard(D)
+    m, _ = _rotation(transform, D)
+    if m is not None:
+        x = x @ m
     return x
 
 
 def inverse_transform(xt: np.ndarray, smooth=None, transform: bool = False) -> np.ndarray:
-    """Undo forward_transform: (xt . H) * s (H is symmetric and involutory).
+    """Undo forward_transform: (xt . M^-1) * s; for the Sylvester matrix
+    M^-1 = H (symmetric and involutory).
 
     The last two steps of the encode_decode chain ("Metal Kernels API",
     "VecInfer kernels": dequant -> inverse-WHT -> inverse-smooth).
     """
     xt = np.asarray(xt, dtype=F64)
     B, H, S, D = xt.shape
-    if transform:
-        xt = xt @ sylvester_hadamard(D)
+    _, m_inv = _rotation(transform, D)
+    if m_inv is not None:
+        xt = xt @ m_inv
     s = _smooth_rows(smooth, H, D)
     if s is not None:
         xt = xt * s[None, :, None, :]
@@ -315,8 +337,9 @@ def query_lut(q_row: np.ndarray, k_codebook, sub_dim: int, smooth_row=None,
     D = qt.shape[-1]
     if smooth_row is not None:
         qt = qt * np.asarray(smooth_row, dtype=F64)
-    if transform:
-        qt = qt @ sylvester_hadamard(D)
+    _, m_inv = _rotation(transform, D)
+    if m_inv is not None:
+        qt = qt @ m_inv.T
     C = np.asarray(k_codebook, dtype=F64)
     return qt.reshape(D // sub_dim, sub_dim) @ C.T                   # [n_sub, n_c]
 

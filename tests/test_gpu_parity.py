@@ -543,3 +543,52 @@ def api_workspace_bytes(c):
     from vector_quantized_kv_amd import vq_attend_workspace_bytes
     return vq_attend_workspace_bytes(c["B"], c["H_q"], c["S_q"], c["D"], c["H_kv"],
                                      c["k_codes"].shape[2], c["window"])
+
+
+# ----------------------------------------------------------------------------
+# randomized Hadamard rotation M = diag(sigma) . H (sigma in {-1, +1}^D):
+# the GPU path takes it as smooth factors s * sigma with the plain Hadamard
+# transform; the oracle applies M itself as a dense matrix
+# ----------------------------------------------------------------------------
+def randomized_hadamard(rng, D):
+    sigma = rng.choice([-1.0, 1.0], size=D)
+    return sigma, sigma[:, None] * O.sylvester_hadamard(D)
+
+
+@pytest.mark.parametrize("H,S", [(8, 37), (2, 4500)])   # per-lane search; matrix-core search
+def test_randomized_hadamard_encode_decode(H, S):
+    rng = np.random.default_rng(800 + S)
+    B, D, d = 1, 128, 8
+    k = synth.outlier_normal(rng, (B, H, S, D), 4)
+    s = synth.smooth_factors(k).astype(np.float64)
+    sigma, M = randomized_hadamard(rng, D)
+    C = synth.sample_rows(rng, O.forward_transform(k, s, M).reshape(-1, d), 256)
+    s_signed = (s * sigma).astype(np.float32)
+    rec, codes = vq_encode_decode(dev(k), dev(C), d, smooth=dev(s_signed), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy()
+    check_codes(k, C, d, s, M, codes, f"randomized Hadamard H{H} S{S}")
+    ref = O.decode(codes, C, s, M)
+    check_recon(rec.cpu().numpy(), ref, "fp32", f"randomized Hadamard H{H} S{S}")
+    out = vq_decode(dev(codes), dev(C), smooth=dev(s_signed))
+    torch.cuda.synchronize()
+    check_recon(out.cpu().numpy(), ref, "fp32", f"randomized Hadamard decode H{H} S{S}")
+
+
+@pytest.mark.parametrize("family", ["stream", "tile", "lut_mfma"])
+def test_randomized_hadamard_attend(family):
+    rng = np.random.default_rng(900 + len(family))
+    if family == "stream":
+        c = small_case(901, B=4, Hq=32, Hkv=8, Sq=1, D=128, dk=8, dv=4, S_cap=8192)
+        c["kv_lens"] = np.array([8192, 5000, 77, 8100], np.int32)
+    elif family == "tile":
+        c = small_case(902, B=3, Hq=4, Hkv=2, Sq=100, D=128, dk=8, dv=4, S_cap=400)
+        c["kv_lens"] = np.array([400, 130, 100], np.int32)
+    else:
+        c = small_case(903)                          # D = 64, GQA-3, 3 query positions
+    assert path_of(c) == family
+    sigma, M = randomized_hadamard(rng, c["D"])
+    s = c["smooth"].astype(np.float64)
+    out = run_attend(c, smooth=(s * sigma).astype(np.float32))
+    ref = oracle_attend(dict(c, smooth=s, transform=M), c["k_codes"], c["v_codes"])
+    check_attn(out, ref, f"randomized Hadamard attend ({family})")

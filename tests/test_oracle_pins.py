@@ -267,10 +267,77 @@ def pin_dual_transform(o):
     assert np.max(np.abs(sc - ref)) <= 1e-10 * np.max(np.abs(ref))
 
 
+def random_orthogonal(rng, D):
+    """A random orthogonal matrix (QR of a Gaussian), not symmetric."""
+    qm, r = np.linalg.qr(rng.standard_normal((D, D)))
+    return qm * np.sign(np.diag(r))[None, :]
+
+
+def pin_dense_transform(o):
+    """An explicit transform matrix M (the H_mat argument of the fused
+    encode-decode kernel): encode applies x . M, decode x~ . M^-1, the query
+    LUT (q * s) . (M^-1)^T.  Pinned with a non-symmetric orthogonal M, where
+    M, M^T and M^-1 differ, and with M = the Sylvester matrix itself."""
+    rng = np.random.default_rng(21)
+    D, d, nc = 32, 4, 64
+    M = random_orthogonal(rng, D)
+    assert np.max(np.abs(M @ M.T - np.eye(D))) < 1e-12 and np.max(np.abs(M - M.T)) > 0.1
+    x = rng.standard_normal((1, 2, 40, D)) * rng.uniform(0.5, 20, size=D)
+    s = rng.uniform(0.3, 9.0, size=(2, D))
+    # round trip without quantization returns the input
+    back = o.inverse_transform(o.forward_transform(x, s, M), s, M)
+    assert np.max(np.abs(back - x)) <= 1e-12 * np.max(np.abs(x))
+    # forward is (x / s) . M, written out element by element for one vector
+    xt = o.forward_transform(x, s, M)
+    v = x[0, 1, 7] / s[1]
+    assert np.max(np.abs(xt[0, 1, 7] - np.array([sum(v[i] * M[i, j] for i in range(D))
+                                                  for j in range(D)]))) < 1e-12
+    # dual identity: LUT scores equal q . K_hat with K_hat decoded through M^-1
+    C = rng.standard_normal((nc, d))
+    codes = rng.integers(0, nc, size=(1, 1, 200, D // d))
+    q = rng.standard_normal(D) * rng.uniform(0.1, 20, size=D)
+    K = o.decode(codes, C, s[:1], M)[0, 0]
+    sc = o.lut_scores(q, codes[0, 0], C, d, smooth_row=s[0], transform=M)
+    assert np.max(np.abs(sc - K @ q)) <= 1e-10 * np.max(np.abs(K @ q))
+    # M = the Sylvester matrix reproduces transform=True
+    H = closed_form_hadamard(D)
+    c1, _ = o.encode(x, C, d, s, H)
+    c2, _ = o.encode(x, C, d, s, True)
+    assert np.array_equal(c1, c2)
+    assert np.max(np.abs(o.decode(c1, C, s, H) - o.decode(c2, C, s, True))) < 1e-12
+
+
+def pin_randomized_hadamard(o):
+    """M = diag(sigma) . H with sigma in {-1, +1}^D (a randomized Hadamard
+    rotation) is orthonormal, and transforming with smooth s and M equals
+    transforming with smooth s * sigma and the plain Hadamard matrix: the
+    divided vector's signs flip before the rotation, decode's multiply flips
+    them back, and the query's smooth multiply carries them to the LUT."""
+    rng = np.random.default_rng(22)
+    D, d, nc, S = 64, 8, 128, 60
+    sigma = rng.choice([-1.0, 1.0], size=D)
+    M = sigma[:, None] * closed_form_hadamard(D)
+    assert np.max(np.abs(M @ M.T - np.eye(D))) < 1e-12
+    s = rng.uniform(0.3, 9.0, size=(2, D))
+    x = rng.standard_normal((1, 2, S, D)) * rng.uniform(0.5, 20, size=D)
+    C = rng.standard_normal((nc, d))
+    c1, g1 = o.encode(x, C, d, s, M)
+    c2, g2 = o.encode(x, C, d, s * sigma, True)
+    assert np.array_equal(c1, c2)
+    assert np.max(np.abs(o.decode(c1, C, s, M) - o.decode(c1, C, s * sigma, True))) < 1e-12
+    q = rng.standard_normal((1, 4, 3, D))
+    vc = rng.integers(0, nc, size=(1, 2, S, D // 4))
+    Cv = rng.standard_normal((nc, 4))
+    a1 = o.attend(q, c1, C, vc, Cv, scale=0.2, smooth=s, transform=M, kv_lens=[50])
+    a2 = o.attend(q, c1, C, vc, Cv, scale=0.2, smooth=s * sigma, transform=True, kv_lens=[50])
+    assert np.max(np.abs(a1 - a2)) < 1e-12
+
+
 ALL_PINS = [pin_hadamard_closed_form, pin_hadamard_golden, pin_hadamard_orthonormal,
             pin_storage, pin_encode_golden, pin_bruteforce, pin_ties, pin_identity_codebook,
             pin_idempotent_and_permutation, pin_attend_golden, pin_attend_sdpa,
-            pin_attend_closed_forms, pin_gqa_and_window, pin_dual_transform]
+            pin_attend_closed_forms, pin_gqa_and_window, pin_dual_transform,
+            pin_dense_transform, pin_randomized_hadamard]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -415,7 +482,34 @@ def _mut_value_transposed(mp):
     mp.setattr(O, "pvq_decode", dec)
 
 
-MUTATIONS = [_mut_smooth_direction, _mut_unnormalized_hadamard, _mut_no_inverse_rotation,
+def _mut_matrix_involutory(mp):
+    # every explicit transform matrix treated as its own inverse, as the
+    # Sylvester matrix is
+    orig = O._rotation
+
+    def rot(t, D):
+        m, mi = orig(t, D)
+        return (m, m) if isinstance(t, np.ndarray) else (m, mi)
+    mp.setattr(O, "_rotation", rot)
+
+
+def _mut_dual_untransposed(mp):
+    # the query rotated by M^-1 instead of (M^-1)^T
+    orig = O._rotation
+    mp.setattr(O, "query_lut", lambda q, C, d, s=None, t=False: _lut_with(orig, q, C, d, s, t))
+
+
+def _lut_with(rot, q, C, d, s, t):
+    qt = np.asarray(q, dtype=np.float64)
+    if s is not None:
+        qt = qt * np.asarray(s, dtype=np.float64)
+    _, mi = rot(t, qt.shape[-1])
+    if mi is not None:
+        qt = qt @ mi
+    return qt.reshape(-1, d) @ np.asarray(C, dtype=np.float64).T
+
+
+MUTATIONS = [_mut_matrix_involutory, _mut_dual_untransposed, _mut_smooth_direction, _mut_unnormalized_hadamard, _mut_no_inverse_rotation,
              _mut_ties_high, _mut_strided_split, _mut_head_aligned_causal,
              _mut_window_off_by_one, _mut_window_needs_causal, _mut_gqa_modulo,
              _mut_lut_divides, _mut_missing_scale, _mut_value_transposed]
