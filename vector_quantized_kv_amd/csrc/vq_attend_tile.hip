@@ -24,11 +24,13 @@
 //                only when a tile exceeds it by more than 8); p rounds to
 //                fp16 (nearest even) and the denominator sums the rounded
 //                values, so the weights applied are exactly normalized.
-//   O         += P V: A = p (staged per wave through LDS into row-major
-//                16 x 32 operands), B = V^T, decoded once per key tile by the
-//                whole workgroup into an LDS tile [dim][key] (a 4 x 4 byte
-//                transpose of the value codes across each lane quad, then a
-//                4 x 4 half transpose of the gathered value rows).
+//   O         += P V: A = p taken straight from the score registers (the
+//                K slots of a lane are the keys its score tile holds), B =
+//                V^T, decoded once per key tile by the whole workgroup into
+//                an LDS tile [dim][key] whose key axis is permuted to match
+//                those slots (a 4 x 4 byte transpose of the value codes
+//                across each lane quad, then a 4 x 4 half transpose of the
+//                gathered value rows).
 //
 // Each workgroup writes (m, l, acc[128]) per query row and split; the split
 // merge kernel combines them.
@@ -45,17 +47,15 @@ constexpr int tD = 128;
 constexpr int tRT = tW * 32;  // query rows per workgroup
 constexpr int tKT = 64;       // keys per tile
 // The 16 lanes that one b128 LDS read serves together need 16 distinct bank
-// quads (64 banks of 4 bytes): the high parts of the key codebook have 16
-// replicas (lane l reads replica l mod 16, so gathers by any codes are
-// conflict-free); the low parts have 8, where lanes l and l + 8 collide when
-// their codes have equal parity (LDS holds no more).
+// quads (64 banks of 4 bytes): both parts of the key codebook have 16
+// replicas and lane l reads replica l mod 16, so gathers by any codes are
+// conflict-free.
 constexpr uint32_t tKTab = 0;       // key codebook hi [256][16 replicas][8 fp16] 64 KiB
-constexpr uint32_t tKLo = 65536;    // key codebook lo [256][8 replicas][8 fp16]  32 KiB
-constexpr uint32_t tVTab = 98304;   // value codebook  [256][4 replicas][4 fp16]   8 KiB
-constexpr uint32_t tVT = 106496;    // V^T tile        [128 dims][72 fp16]        18 KiB
-constexpr uint32_t tRowB = 144;     // bytes per V^T / P row (64 fp16 + pad)
-constexpr uint32_t tPS = tVT + tD * tRowB;          // p per wave [32 rows][72 fp16]
-constexpr uint32_t tAl = tPS + tW * 32 * tRowB;     // per-wave row rescale factors
+constexpr uint32_t tKLo = 65536;    // key codebook lo [256][16 replicas][8 fp16] 64 KiB
+constexpr uint32_t tVTab = 131072;  // value codebook  [256][4 replicas][4 fp16]   8 KiB
+constexpr uint32_t tVT = 139264;    // V^T tile        [128 dims][72 fp16]        18 KiB
+constexpr uint32_t tRowB = 144;     // bytes per V^T row (64 fp16 + pad)
+constexpr uint32_t tAl = tVT + tD * tRowB;          // per-wave row rescale factors
 constexpr uint32_t tLdsBytes = tAl + tW * 32 * 4;
 static_assert(tLdsBytes <= 160 * 1024, "LDS budget");
 constexpr float tLazyMargin = 8.f;
@@ -148,7 +148,8 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
     for (int r = 4 * half; r < 4 * half + 4; ++r) {
       lds_st<half8_t>(tKTab + code * 256 + r * 16, hi);
       lds_st<half8_t>(tKTab + code * 256 + (r + 8) * 16, hi);
-      lds_st<half8_t>(tKLo + code * 128 + r * 16, lo);
+      lds_st<half8_t>(tKLo + code * 256 + r * 16, lo);
+      lds_st<half8_t>(tKLo + code * 256 + (r + 8) * 16, lo);
     }
 #pragma unroll
     for (int r = 2 * half; r < 2 * half + 2; ++r) lds_st<u32x2_t>(tVTab + code * 32 + r * 8, hv);
@@ -264,9 +265,8 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
 
   // ---- per-lane constants ---------------------------------------------------
   const uint32_t kbase = tKTab + (uint32_t)(lane & 15) * 16u;    // key hi replica (256 B per code)
-  const uint32_t kbase_lo = tKLo + (uint32_t)(lane & 7) * 16u;   // key lo replica (128 B per code)
+  const uint32_t kbase_lo = tKLo + (uint32_t)(lane & 15) * 16u;  // key lo replica (256 B per code)
   const uint32_t vtab = tVTab + (uint32_t)(lane & 3) * 8u;        // value replica
-  const uint32_t ps = tPS + wave * 32 * tRowB;
   // V^T decode task: lane quad (u = tid % 4) = keys 4 tq .. 4 tq + 3 x subs 4 sm .. 4 sm + 3,
   // quad tid / 4 = 16 sm + tq, so that the 32 lanes of each 8-byte V^T write
   // (4 dims x 8 key quads) land on distinct bank pairs
@@ -317,7 +317,12 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
       const u32x2_t R2 = lds_ld<u32x2_t>(vtab + (((Y >> 16) & 0xffu) << 5));
       const u32x2_t R3 = lds_ld<u32x2_t>(vtab + ((Y >> 24) << 5));
       const uint32_t dim0 = 4 * (4 * sm + qu);
-      const uint32_t base = tVT + dim0 * tRowB + 8 * tq;
+      // keys 4 tq .. 4 tq + 3 (tq = 8 c2 + 4 h + kg) go to positions
+      // 32 c2 + 8 kg + 4 h .. + 3 of the tile's key axis: the order in which
+      // the P V operand slots take the weights straight from the score
+      // registers
+      const uint32_t kpos = 32u * (uint32_t)(tq >> 3) + 8u * (uint32_t)(tq & 3) + 4u * (uint32_t)((tq >> 2) & 1);
+      const uint32_t base = tVT + dim0 * tRowB + 2 * kpos;
       lds_st<u32x2_t>(base + 0 * tRowB, u32x2_t{__builtin_amdgcn_perm(R1.x, R0.x, 0x05040100u),
                                                  __builtin_amdgcn_perm(R3.x, R2.x, 0x05040100u)});
       lds_st<u32x2_t>(base + 1 * tRowB, u32x2_t{__builtin_amdgcn_perm(R1.x, R0.x, 0x07060302u),
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
       for (int c = 0; c < 4; ++c) {
         const uint32_t code = __builtin_amdgcn_ubfe(kw[c], 8u * kg, 8u);
         kv[c] = lds_ld<half8_t>((code << 8) | kbase);
-        kl[c] = lds_ld<half8_t>((code << 7) + kbase_lo);
+        kl[c] = lds_ld<half8_t>((code << 8) + kbase_lo);
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -410,31 +415,33 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
         for (int nd = 0; nd < 8; ++nd) oacc[mt][nd] *= a4;
       }
     }
-    // p (fp16) into the wave's staging rows: row 16 nt + n16, keys 16 mt + 4 kg + i
-    wave_sync_lds();
+    // p (fp16): ph[nt][mt][i] = row 16 nt + n16, key 16 mt + 4 kg + i
+    half4_t ph[2][4];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        half4_t ph;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ph[i] = (_Float16)__builtin_amdgcn_exp2f(sacc[mt][nt][i] - mref[nt]);
-          lsum[nt] += (float)ph[i];  // the denominator of exactly the weights used
+          ph[nt][mt][i] = (_Float16)__builtin_amdgcn_exp2f(sacc[mt][nt][i] - mref[nt]);
+          lsum[nt] += (float)ph[nt][mt][i];  // the denominator of exactly the weights used
         }
-        lds_st<half4_t>(ps + (16 * nt + n16) * tRowB + 2 * (16 * mt + 4 * kg), ph);
       }
     }
-    __syncthreads();  // the V^T tile is complete; the wave's p rows are written
+    __syncthreads();  // the V^T tile is complete
 
     // ---- O += P V ---------------------------------------------------------
-    // A: p rows 16 mt + n16, keys 32 kc + 8 kg ..; B: V^T rows (dims) 16 nd + n16
+    // A: p of rows 16 mt + n16; the lane's K slots 8 kg + 4 h + i of key
+    // chunk kc2 hold keys 32 kc2 + 16 h + 4 kg + i, which are its own score
+    // registers; B: V^T rows (dims) 16 nd + n16 at the same key positions
 #pragma unroll
     for (int kc2 = 0; kc2 < 2; ++kc2) {
       half8_t pa[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        pa[mt] = lds_ld<half8_t>(ps + (16 * mt + n16) * tRowB + 2 * (32 * kc2 + 8 * kg));
+      for (int mt = 0; mt < 2; ++mt) {
+        const half4_t a0 = ph[mt][2 * kc2], a1 = ph[mt][2 * kc2 + 1];
+        pa[mt] = half8_t{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      }
 #pragma unroll
       for (int nd = 0; nd < 8; ++nd) {
         const half8_t vb = lds_ld<half8_t>(tVT + (16 * nd + n16) * tRowB + 2 * (32 * kc2 + 8 * kg));
