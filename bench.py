@@ -5,7 +5,8 @@ One step = one pass of the whole decode hot path over a batch of the long-
 context GQA workload (B=16, H_q=32, H_kv=8, D=128, 32768-slot code buffers,
 ragged lengths uniform in [16384, 32768], causal, no window):
   1. encode each row's new key (smooth + Walsh-Hadamard + product VQ, d_k=8)
-     and value (product VQ, d_v=4) into the code buffers at slot len_b - 1;
+     and value (product VQ, d_v=4) into the code buffers at slot len_b - 1
+     (one vq_encode_kv call);
   2. fused attention of the 32 query heads straight from the key and value
      codes (dual transform, LUT scores, online softmax over split-K chunks,
      value-codebook gather, split merge).
@@ -133,7 +134,7 @@ def main():
     import torch
 
     from vector_quantized_kv_amd import (attend_workspace, synth, vq_attend, vq_encode,
-                                         vq_encode_decode)
+                                         vq_encode_decode, vq_encode_kv)
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -185,11 +186,11 @@ def main():
     ws = attend_workspace(q, kc0, 0)
     steps = []
     for i in range(n_sets):
-        ek = vq_encode(kn, Ck, dk, smooth=sm, codes=kcs[i], row_offsets=offs, prepare=True)
-        ev = vq_encode(vn, Cv, dv, transform=False, codes=vcs[i], row_offsets=offs, prepare=True)
+        ekv = vq_encode_kv(kn, vn, Ck, dk, Cv, dv, smooth=sm, k_codes=kcs[i], v_codes=vcs[i],
+                           row_offsets=offs, prepare=True)
         at = vq_attend(q, kcs[i], Ck, vcs[i], Cv, scale=c["scale"], smooth=sm, kv_lens=kl,
                        causal=True, sliding_window=0, out=out, workspace=ws, prepare=True)
-        steps.append((ek, ev, at))
+        steps.append((ekv, at))
 
     enc_bytes = 2 * B * Hkv * D * 2 + B * Hkv * (D // dk + D // dv) + (256 * (dk + dv) + Hkv * D) * 4
     attn_fixed = 2 * B * Hq * D * 2 + 256 * (dk + dv) * 4 + Hkv * D * 4 + B * 4
@@ -197,16 +198,15 @@ def main():
     step_bytes = attn_bytes + enc_bytes
 
     def step(i):
-        ek, ev, at = steps[i % n_sets]
-        ek(); ev(); at()
+        ekv, at = steps[i % n_sets]
+        ekv(); at()
 
     if args.mode != "full":
         for i in range(args.warmup + args.steps):
             if args.mode == "attend":
-                steps[i % n_sets][2]()
+                steps[i % n_sets][1]()
             else:
                 steps[i % n_sets][0]()
-                steps[i % n_sets][1]()
         torch.cuda.synchronize()
         log(f"[bench] mode={args.mode}: {args.warmup + args.steps} launches done")
         return
@@ -224,10 +224,10 @@ def main():
     log(f"[bench] step: {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s")
 
     # attention kernel alone, HIP events on the launch stream, same rotation
-    attn_us = time_events(lambda i: steps[i % n_sets][2](), max(args.steps, 100), torch)
+    attn_us = time_events(lambda i: steps[i % n_sets][1](), max(args.steps, 100), torch)
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     log(f"[bench] vq_attend: {attn_us:.1f} us, {achieved:.0f} GB/s")
-    each = time_events_each(lambda i: steps[i % n_sets][2](), max(args.steps, 100), torch)
+    each = time_events_each(lambda i: steps[i % n_sets][1](), max(args.steps, 100), torch)
     log(f"[bench] vq_attend per call: p10 {pct(each, 0.1):.1f} p50 {pct(each, 0.5):.1f} "
         f"p90 {pct(each, 0.9):.1f} us")
     # practical HBM reference: a plain 1 GiB elementwise copy (1 GiB read + 1 GiB written)
@@ -349,11 +349,11 @@ def main():
         lp = t(p["kv_lens"])
         op = torch.empty_like(pq)
         wsp = attend_workspace(pq, kb, 0)
-        f1 = vq_encode(pk, Ckp, 8, smooth=smp, codes=kb, S_off=p["S_off"], prepare=True)
-        f2 = vq_encode(pv, Cvp, 4, transform=False, codes=vb, S_off=p["S_off"], prepare=True)
+        f1 = vq_encode_kv(pk, pv, Ckp, 8, Cvp, 4, smooth=smp, k_codes=kb, v_codes=vb,
+                          S_off=p["S_off"], prepare=True)
         f3 = vq_attend(pq, kb, Ckp, vb, Cvp, scale=p["scale"], smooth=smp, kv_lens=lp, out=op,
                        workspace=wsp, prepare=True)
-        us_p = time_events(lambda i: (f1(), f2(), f3()), 10, torch, warm=2)
+        us_p = time_events(lambda i: (f1(), f3()), 10, torch, warm=2)
         us_pa = time_events(lambda i: f3(), 10, torch, warm=1)
         extra["prefill"] = {"us_step": round(us_p, 1), "us_attend": round(us_pa, 1),
                             "attend_dense_TFLOPs": round(139.6e9 / us_pa / 1e6, 2)}

@@ -116,6 +116,29 @@ int vq_encode(const void* keys_f16, int B, int H, int S, int D,
               void* stream);
 
 /*
+ * Encode of the keys and the values of one cache append together (the
+ * cache's update_and_fetch encodes both into their index buffers,
+ * "veloxquant_mlx.cache.vecinfer_cache module").  Same result as
+ *   vq_encode(keys_f16 -> k_codes, k_codebook, smooth, transform) and then
+ *   vq_encode(values_f16 -> v_codes, v_codebook, no smooth, transform 0),
+ * with the same B, H, S, D, S_cap, S_off and row_offsets for both; short
+ * appends (few token-heads) run as one launch.
+ *
+ *   keys_f16, values_f16   [B, H, S, D] fp16
+ *   k_codebook [k_n_centroids, k_sub_dim], v_codebook [v_n_centroids,
+ *   v_sub_dim] fp32; smooth, smooth_rows, transform as for vq_encode (keys)
+ *   k_codes [B, H, S_cap, D / k_sub_dim], v_codes [B, H, S_cap, D / v_sub_dim]
+ * Errors: those of vq_encode for either half, checked before anything is
+ * enqueued.
+ */
+int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int S, int D,
+                 const float* k_codebook, int k_n_centroids, int k_sub_dim,
+                 const float* smooth, int smooth_rows, int transform,
+                 const float* v_codebook, int v_n_centroids, int v_sub_dim,
+                 uint8_t* k_codes, uint8_t* v_codes, int S_cap, int S_off,
+                 const int32_t* row_offsets, void* stream);
+
+/*
  * Decode: codebook gather -> inverse rotation -> inverse smoothing ("Metal
  * Kernels API", "VecInfer kernels", vecinfer_dequant_metal and the last three
  * steps of vecinfer_encode_decode_metal).

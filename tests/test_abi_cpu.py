@@ -33,7 +33,7 @@ def header_functions():
 
 def test_header_declares_the_four_calls():
     names = header_functions()
-    for n in ["vq_encode", "vq_decode", "vq_encode_decode", "vq_attend",
+    for n in ["vq_encode", "vq_decode", "vq_encode_decode", "vq_encode_kv", "vq_attend",
               "vq_attend_workspace_bytes", "vq_supports_shape", "vq_status_string", "vq_last_error"]:
         assert n in names
 
@@ -101,6 +101,28 @@ def test_decode_and_encode_decode_validation(lib):
     assert st == UNSUPPORTED                            # D = 48
     st = lib.vq_decode(None, 1, 2, 8, 8, 0, P, 256, 4, None, 1, 1, 64, P, 0, None)
     assert st == INVALID
+
+
+def enc_kv(lib, B=1, H=2, S=8, D=128, dk=8, dv=4, nk=256, nv=256, S_cap=8, S_off=0, offs=None,
+           keys=P, values=P, kcb=P, vcb=P, kc=P, vc=P, smooth=P, srows=2, transform=1):
+    return lib.vq_encode_kv(keys, values, B, H, S, D, kcb, nk, dk, smooth, srows, transform, vcb, nv,
+                            dv, kc, vc, S_cap, S_off, offs, None)
+
+
+def test_encode_kv_validation(lib):
+    assert enc_kv(lib, values=None) == INVALID
+    assert enc_kv(lib, vc=None) == INVALID
+    assert enc_kv(lib, dv=3) == INVALID                 # D % value sub_dim
+    assert enc_kv(lib, nv=300) == INVALID               # value codes do not fit uint8
+    assert enc_kv(lib, dk=1) == UNSUPPORTED             # 128 key sub-vectors
+    assert enc_kv(lib, srows=3) == INVALID
+    assert enc_kv(lib, S_off=1) == INVALID              # [1, 9) outside [0, 8)
+    offs = (ctypes.c_int32 * 2)(0, 6)
+    assert enc_kv(lib, B=2, S=4, offs=offs) == INVALID  # row 1 writes [6, 10)
+    assert enc_kv(lib, S=0) == OK
+    assert enc_kv(lib, B=0) == OK
+    if not torch.cuda.is_available():
+        assert enc_kv(lib) == NO_DEVICE
 
 
 def att(lib, B=2, Hq=8, Sq=1, D=128, dk=8, dv=4, n_c=256, Hkv=2, S_cap=64, W=0, causal=1,

@@ -592,3 +592,49 @@ def test_randomized_hadamard_attend(family):
     out = run_attend(c, smooth=(s * sigma).astype(np.float32))
     ref = oracle_attend(dict(c, smooth=s, transform=M), c["k_codes"], c["v_codes"])
     check_attn(out, ref, f"randomized Hadamard attend ({family})")
+
+
+# ----------------------------------------------------------------------------
+# keys and values of one append in one call
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("B,H,S,D,dk,dv,S_cap,per_row", [
+    (16, 8, 1, 128, 8, 4, 64, True),      # decode-step append: one launch, 16-way codebook split
+    (3, 4, 125, 128, 8, 4, 300, False),   # one launch, 4-way split
+    (2, 2, 3, 64, 4, 4, 16, True),        # head dim 64
+    (2, 3, 100, 128, 8, 4, 128, False),   # the halves take different splits: two launches
+    (1, 8, 2048, 128, 8, 4, 2048, False), # matrix-core search: two launches
+])
+def test_encode_kv(B, H, S, D, dk, dv, S_cap, per_row):
+    """vq_encode_kv writes the same codes as vq_encode on the keys (smoothed,
+    rotated) and on the values (neither), the oracle's codes under the
+    near-tie rule, and leaves every other slot untouched."""
+    from vector_quantized_kv_amd import vq_encode_kv
+    rng = np.random.default_rng(1000 + B * H * S + D + dk)
+    k = synth.outlier_normal(rng, (B, H, S, D), 4)
+    v = synth.outlier_normal(rng, (B, H, S, D), 4)
+    s = synth.smooth_factors(k)
+    xk = O.forward_transform(k, s, True).reshape(-1, dk)
+    xv = v.astype(np.float64).reshape(-1, dv)
+    Ck = synth.sample_rows(rng, xk, min(256, len(xk)))
+    Cv = synth.sample_rows(rng, xv, min(256, len(xv)))
+    if per_row:
+        offs = [int(x) for x in rng.integers(0, S_cap - S + 1, size=B)]
+        kw = dict(row_offsets=offs)
+    else:
+        offs = [S_cap - S] * B
+        kw = dict(S_off=S_cap - S)
+    fill = lambda n: torch.full((B, H, S_cap, D // n), 0xAB, dtype=torch.uint8, device=DEV)
+    kc, vc, kc2, vc2 = fill(dk), fill(dv), fill(dk), fill(dv)
+    vq_encode_kv(dev(k), dev(v), dev(Ck), dk, dev(Cv), dv, smooth=dev(s), k_codes=kc, v_codes=vc, **kw)
+    vq_encode(dev(k), dev(Ck), dk, smooth=dev(s), codes=kc2, **kw)
+    vq_encode(dev(v), dev(Cv), dv, transform=False, codes=vc2, **kw)
+    torch.cuda.synchronize()
+    kc, vc, kc2, vc2 = (t.cpu().numpy() for t in (kc, vc, kc2, vc2))
+    assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2)
+    for codes, x, C, d, sm, tr, tag in [(kc, k, Ck, dk, s, True, "keys"), (vc, v, Cv, dv, None, False, "values")]:
+        mask = np.zeros(codes.shape[:3], bool)
+        for b in range(B):
+            mask[b, :, offs[b]:offs[b] + S] = True
+        assert np.all(codes[~mask] == 0xAB), f"{tag}: a slot outside the append was written"
+        got = np.stack([codes[b, :, offs[b]:offs[b] + S] for b in range(B)])
+        check_codes(x, C, d, sm, tr, got, f"encode_kv {tag} B{B} H{H} S{S} D{D}")

@@ -19,6 +19,12 @@ SIGNATURES = {
                           c_void_p, c_int, c_int,
                           c_void_p, c_int, c_int, c_void_p,
                           c_void_p]),
+    "vq_encode_kv": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                             c_void_p, c_int, c_int,
+                             c_void_p, c_int, c_int,
+                             c_void_p, c_int, c_int,
+                             c_void_p, c_void_p, c_int, c_int, c_void_p,
+                             c_void_p]),
     "vq_decode": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int,
                           c_void_p, c_int, c_int,
                           c_void_p, c_int, c_int, c_int,

@@ -101,6 +101,37 @@ def vq_encode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=Non
                  _stream(stream), prepare=prepare, result=codes)
 
 
+def vq_encode_kv(keys, values, k_codebook, k_sub_dim, v_codebook, v_sub_dim, *, smooth=None,
+                 transform=True, k_codes=None, v_codes=None, S_cap=None, S_off=0,
+                 row_offsets=None, stream=None, prepare=False):
+    """Encode the keys (smoothed, rotated) and the values (neither) of one
+    append into their code buffers; returns (k_codes, v_codes)."""
+    _need(keys, "keys", torch.float16, 4)
+    _need(values, "values", torch.float16, 4)
+    _need(k_codebook, "k_codebook", torch.float32, 2)
+    _need(v_codebook, "v_codebook", torch.float32, 2)
+    B, H, S, D = keys.shape
+    if tuple(values.shape) != (B, H, S, D):
+        raise ValueError("keys and values must have the same shape")
+    if k_codes is None:
+        k_codes = torch.zeros((B, H, S_cap or S, D // k_sub_dim), dtype=torch.uint8, device=keys.device)
+    if v_codes is None:
+        v_codes = torch.zeros((B, H, S_cap or S, D // v_sub_dim), dtype=torch.uint8, device=keys.device)
+    _need(k_codes, "k_codes", torch.uint8, 4)
+    _need(v_codes, "v_codes", torch.uint8, 4)
+    if k_codes.shape[2] != v_codes.shape[2]:
+        raise ValueError("k_codes and v_codes must have the same S_cap")
+    sm, rows = _smooth(smooth)
+    offs = None
+    if row_offsets is not None:
+        offs = (ctypes.c_int32 * B)(*[int(x) for x in row_offsets])
+    return _call("vq_encode_kv", _ptr(keys), _ptr(values), B, H, S, D, _ptr(k_codebook),
+                 k_codebook.shape[0], k_sub_dim, _ptr(sm), rows, int(bool(transform)),
+                 _ptr(v_codebook), v_codebook.shape[0], v_sub_dim, _ptr(k_codes), _ptr(v_codes),
+                 k_codes.shape[2], S_off, offs, _stream(stream), prepare=prepare,
+                 result=(k_codes, v_codes))
+
+
 def vq_encode_decode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=None,
                      S_cap=None, S_off=0, row_offsets=None, recon=None,
                      out_dtype=torch.float16, stream=None, prepare=False):

@@ -190,6 +190,45 @@ int vq_encode(const void* keys_f16, int B, int H, int S, int D, const float* cod
                     0, stream);
 }
 
+int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int S, int D,
+                 const float* k_codebook, int k_n_centroids, int k_sub_dim, const float* smooth,
+                 int smooth_rows, int transform, const float* v_codebook, int v_n_centroids,
+                 int v_sub_dim, uint8_t* k_codes, uint8_t* v_codes, int S_cap, int S_off,
+                 const int32_t* row_offsets, void* stream) {
+  g_last_error[0] = 0;
+  const char* what = "vq_encode_kv";
+  int st = check_encode(what, keys_f16, B, H, S, D, k_codebook, k_n_centroids, k_sub_dim, smooth,
+                        smooth_rows, transform, k_codes, S_cap, S_off, row_offsets);
+  if (st) return st;
+  if ((st = check_encode(what, values_f16, B, H, S, D, v_codebook, v_n_centroids, v_sub_dim, nullptr, 1,
+                         0, v_codes, S_cap, S_off, row_offsets)))
+    return st;
+  if (B == 0 || S == 0) return VQ_OK;
+  if ((st = check_device(what))) return st;
+  EncodeArgs k{}, v{};
+  k.keys = reinterpret_cast<const __half*>(keys_f16);
+  k.codebook = k_codebook;
+  k.smooth = smooth;
+  k.codes = k_codes;
+  k.B = B; k.H = H; k.S = S; k.D = D; k.n_c = k_n_centroids; k.sub_dim = k_sub_dim;
+  k.smooth_rows = smooth_rows; k.transform = transform;
+  k.S_cap = S_cap; k.S_off = S_off; k.use_row_offsets = row_offsets != nullptr;
+  v = k;
+  v.keys = reinterpret_cast<const __half*>(values_f16);
+  v.codebook = v_codebook;
+  v.smooth = nullptr;
+  v.smooth_rows = 1;
+  v.transform = 0;
+  v.codes = v_codes;
+  v.n_c = v_n_centroids;
+  v.sub_dim = v_sub_dim;
+  RowOffsets offs{};
+  if (row_offsets)
+    for (int b = 0; b < B; ++b) offs.v[b] = row_offsets[b];
+  return hip_status(what, launch_encode_kv(k, v, row_offsets ? &offs : nullptr,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
 int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D, const float* codebook,
                      int n_centroids, int sub_dim, const float* smooth, int smooth_rows,
                      int transform, uint8_t* codes, int S_cap, int S_off,

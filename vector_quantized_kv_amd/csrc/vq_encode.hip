@@ -179,11 +179,13 @@ struct Dims {
 // CSPLIT waves share one group of token-heads and split the codebook between
 // them (used when there are too few token-heads to fill the chip); their
 // partial argmins are combined through LDS, lowest index first on ties.
+// The body takes its workgroup index as an argument, so that one launch can
+// run it for two inputs (the keys and the values of one append).
 template <int D, int DS, int MODE, int CSPLIT>
-__global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kernel(
-    const __half* __restrict__ keys, const uint8_t* __restrict__ codes_in,
+__device__ __forceinline__ void pvq_body(
+    int block, const __half* __restrict__ keys, const uint8_t* __restrict__ codes_in,
     const float* __restrict__ cb, const float* __restrict__ smooth,
-    uint8_t* __restrict__ codes, void* __restrict__ recon, Dims d, RowOffsets offs) {
+    uint8_t* __restrict__ codes, void* __restrict__ recon, const Dims& d, const RowOffsets& offs) {
   constexpr int NSUB = D / DS;   // lanes per token-head (<= 64)
   constexpr int TPW = 64 / NSUB; // token-heads per wave
   constexpr int NT = threads_for<CSPLIT>();
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kernel(
   const int grp = wave / CSPLIT, part = wave % CSPLIT;
   const int j = lane % NSUB;
   const long long n_th = (long long)d.B * d.H * d.S;
-  const long long th = (long long)blockIdx.x * TPB + grp * TPW + lane / NSUB;
+  const long long th = (long long)block * TPB + grp * TPW + lane / NSUB;
   const bool valid = th < n_th;
   const long long thc = valid ? th : 0;
   const int t = (int)(thc % d.S);
@@ -306,6 +308,33 @@ __global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kernel(
         store_f32<DS>(reinterpret_cast<float*>(recon) + thc * D + j * DS, x);
     }
   }
+}
+
+template <int D, int DS, int MODE, int CSPLIT>
+__global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kernel(
+    const __half* __restrict__ keys, const uint8_t* __restrict__ codes_in,
+    const float* __restrict__ cb, const float* __restrict__ smooth,
+    uint8_t* __restrict__ codes, void* __restrict__ recon, Dims d, RowOffsets offs) {
+  pvq_body<D, DS, MODE, CSPLIT>(blockIdx.x, keys, codes_in, cb, smooth, codes, recon, d, offs);
+}
+
+// Encode of the keys and the values of one append in one launch (the cache
+// appends both, "veloxquant_mlx.cache.vecinfer_cache module",
+// update_and_fetch): workgroups [0, k_blocks) encode the keys with their
+// smoothing and rotation, the rest the values.  For short appends, whose
+// time is the latency of a few dependent memory round trips, the two halves
+// then overlap instead of running one after the other.
+template <int D, int DSK, int DSV, int CSPLIT>
+__global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kv_kernel(
+    const __half* __restrict__ keys, const __half* __restrict__ values,
+    const float* __restrict__ k_cb, const float* __restrict__ v_cb, const float* __restrict__ smooth,
+    uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes, Dims dk, Dims dv,
+    RowOffsets offs, int k_blocks) {
+  if ((int)blockIdx.x < k_blocks)
+    pvq_body<D, DSK, 0, CSPLIT>(blockIdx.x, keys, nullptr, k_cb, smooth, k_codes, nullptr, dk, offs);
+  else
+    pvq_body<D, DSV, 0, CSPLIT>(blockIdx.x - k_blocks, values, nullptr, v_cb, nullptr, v_codes, nullptr,
+                                dv, offs);
 }
 
 // Nearest centroid as a dense contraction on the matrix cores.  For a
@@ -944,20 +973,29 @@ void launch_one(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStre
                      a.keys, a.codes_in, a.codebook, a.smooth, a.codes, a.recon, d, o);
 }
 
+Dims make_dims(const EncodeArgs& a) {
+  return Dims{a.B, a.H, a.S, a.n_c, a.smooth_rows, a.transform, a.S_cap, a.S_off,
+              a.use_row_offsets, a.recon_dtype, make_fastdiv((uint32_t)a.S), make_fastdiv((uint32_t)a.H)};
+}
+
+// Fewer lanes than about four waves per CU (256 CUs): split the codebook
+// over the waves of a workgroup instead of giving each its own token-heads,
+// so short appends (one token per row) are not latency bound; below one wave
+// per CU, 16 ways (16 waves per workgroup).
+int codebook_split(const EncodeArgs& a) {
+  const long long n_th = (long long)a.B * a.H * a.S;
+  const long long lanes = n_th * (a.D / a.sub_dim);
+  return lanes < 256LL * 64 ? 16 : (lanes < 256LL * 64 * 4 ? 4 : 1);
+}
+
 template <int D, int DS>
 hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipStream_t st) {
-  constexpr int NSUB = D / DS;
   const long long n_th = (long long)a.B * a.H * a.S;
   if ((n_th + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidValue;
-  Dims d{a.B, a.H, a.S, a.n_c, a.smooth_rows, a.transform, a.S_cap, a.S_off,
-         a.use_row_offsets, a.recon_dtype, make_fastdiv((uint32_t)a.S), make_fastdiv((uint32_t)a.H)};
+  const Dims d = make_dims(a);
   RowOffsets o{};
   if (offs) o = *offs;
-  // Fewer lanes than about four waves per CU (256 CUs): split the codebook
-  // over the waves of a workgroup instead of giving each its own
-  // token-heads, so short appends (one token per row) are not latency
-  // bound; below one wave per CU, 16 ways (16 waves per workgroup).
-  const int split = n_th * NSUB < 256LL * 64 ? 16 : (n_th * NSUB < 256LL * 64 * 4 ? 4 : 1);
+  const int split = codebook_split(a);
   // Enough sub-vectors to fill the chip: nearest centroid on the matrix cores.
   if constexpr (DS % 4 == 0) {
     if (split == 1 && mode != 2 && n_th < (1LL << 31)) {
@@ -996,7 +1034,47 @@ hipError_t launch_d(const EncodeArgs& a, const RowOffsets* offs, int mode, hipSt
   return hipErrorInvalidValue;
 }
 
+template <int D, int DSK, int DSV, int CSPLIT>
+void launch_kv_fused(const EncodeArgs& k, const EncodeArgs& v, const RowOffsets& o, hipStream_t st) {
+  constexpr int NT = threads_for<CSPLIT>();
+  constexpr int TPBK = (NT / 64 / CSPLIT) * (64 / (D / DSK));
+  constexpr int TPBV = (NT / 64 / CSPLIT) * (64 / (D / DSV));
+  const long long n_th = (long long)k.B * k.H * k.S;
+  const int kb = (int)((n_th + TPBK - 1) / TPBK), vb = (int)((n_th + TPBV - 1) / TPBV);
+  hipLaunchKernelGGL((pvq_kv_kernel<D, DSK, DSV, CSPLIT>), dim3((unsigned)(kb + vb)), dim3(NT), 0, st,
+                     k.keys, v.keys, k.codebook, v.codebook, k.smooth, k.codes, v.codes, make_dims(k),
+                     make_dims(v), o, kb);
+}
+
+template <int D, int DSK, int DSV>
+bool try_kv_fused(const EncodeArgs& k, const EncodeArgs& v, const RowOffsets& o, int split,
+                  hipStream_t st) {
+  if (k.sub_dim != DSK || v.sub_dim != DSV) return false;
+  if (split == 16) launch_kv_fused<D, DSK, DSV, 16>(k, v, o, st);
+  else launch_kv_fused<D, DSK, DSV, 4>(k, v, o, st);
+  return true;
+}
+
 }  // namespace
+
+hipError_t launch_encode_kv(const EncodeArgs& k, const EncodeArgs& v, const RowOffsets* offs,
+                            hipStream_t st) {
+  // One launch when both halves are short appends on the split search with
+  // the same split and a compiled (head dim, key, value sub_dim) triple;
+  // otherwise the two encodes run one after the other.
+  const int split = codebook_split(k);
+  if (split > 1 && split == codebook_split(v)) {
+    RowOffsets o{};
+    if (offs) o = *offs;
+    bool done = false;
+    if (k.D == 128) done = try_kv_fused<128, 8, 4>(k, v, o, split, st) || try_kv_fused<128, 4, 4>(k, v, o, split, st);
+    else if (k.D == 64) done = try_kv_fused<64, 8, 4>(k, v, o, split, st) || try_kv_fused<64, 4, 4>(k, v, o, split, st);
+    if (done) return hipGetLastError();
+  }
+  hipError_t e = launch_encode(k, offs, 0, st);
+  if (e != hipSuccess) return e;
+  return launch_encode(v, offs, 0, st);
+}
 
 hipError_t launch_encode(const EncodeArgs& a, const RowOffsets* offs, int mode, hipStream_t st) {
   switch (a.D) {

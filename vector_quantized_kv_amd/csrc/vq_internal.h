@@ -36,6 +36,10 @@ struct EncodeArgs {
 
 // mode 0 = encode, 1 = encode + reconstruct, 2 = decode only.
 hipError_t launch_encode(const EncodeArgs& a, const RowOffsets* offs, int mode, hipStream_t st);
+// Keys (k) and values (v) of one append, same B, H, S, D and slots; one
+// launch for short appends with a compiled sub_dim pair, else two encodes.
+hipError_t launch_encode_kv(const EncodeArgs& k, const EncodeArgs& v, const RowOffsets* offs,
+                            hipStream_t st);
 
 struct AttendArgs {
   const __half* q;          // [B, H_q, S_q, D]
