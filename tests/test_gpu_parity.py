@@ -638,3 +638,26 @@ def test_encode_kv(B, H, S, D, dk, dv, S_cap, per_row):
         assert np.all(codes[~mask] == 0xAB), f"{tag}: a slot outside the append was written"
         got = np.stack([codes[b, :, offs[b]:offs[b] + S] for b in range(B)])
         check_codes(x, C, d, sm, tr, got, f"encode_kv {tag} B{B} H{H} S{S} D{D}")
+
+
+def test_single_split_direct_output():
+    """Key ranges up to 1024 run as one split per unit, whose workgroup
+    writes the output rows itself (no merge launch): the same keys in a
+    larger buffer (several splits and the merge) give the same rows, both
+    match the oracle, including an empty row and a windowed range."""
+    c = small_case(13, B=3, Hq=8, Hkv=2, Sq=2, D=128, dk=8, dv=4, S_cap=1000)
+    c["kv_lens"] = np.array([1000, 517, 0], np.int32)
+    assert path_of(c) == "lut_mfma"
+    a = run_attend(c)
+    big = dict(c)
+    pad = lambda x: np.concatenate([x, np.zeros((3, 2, 1100 - 1000, x.shape[3]), np.uint8)], 2)
+    big["k_codes"], big["v_codes"] = pad(c["k_codes"]), pad(c["v_codes"])
+    b = run_attend(big)
+    assert np.max(np.abs(a.astype(np.float64) - b)) <= 2e-3
+    assert np.all(a[2] == 0)
+    check_attn(a, oracle_attend(c, c["k_codes"], c["v_codes"]), "one split")
+    check_attn(b, oracle_attend(big, big["k_codes"], big["v_codes"]), "several splits")
+    w = small_case(14, B=3, Hq=8, Hkv=2, Sq=2, D=128, dk=8, dv=4, S_cap=6000)
+    w["kv_lens"] = np.array([6000, 3000, 10], np.int32)
+    w["window"] = 700                       # key range 701: one split
+    check_attn(run_attend(w), oracle_attend(w, w["k_codes"], w["v_codes"]), "one split, window 700")

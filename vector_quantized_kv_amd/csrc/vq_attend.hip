@@ -406,6 +406,9 @@ hipError_t launch_attend_merge(const AttendArgs& a, const AttParams& p, hipStrea
   return p.n_split <= 4 ? launch_merge_r<4>(a, p, st) : launch_merge_r<16>(a, p, st);
 }
 
+// Key ranges up to this length run as one split per unit.
+constexpr long long kOneSplitKeys = 1024;
+
 bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, AttendPlan* pl) {
   if (B <= 0 || Hq <= 0 || Sq <= 0 || D <= 0 || Hkv <= 0 || S_cap <= 0 || window < 0) return false;
   if (Hq % Hkv != 0) return false;
@@ -415,9 +418,13 @@ bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, A
       window > 0 ? std::min<long long>(S_cap, (long long)Sq + window - 1) : S_cap;
   // Aim for about 1024 workgroups (4 per CU on 256 CUs) across the
   // independent (batch row, kv head, 8-row group) units, with at least 256
-  // keys per split so the per-workgroup LUT build stays amortized.
+  // keys per split so the per-workgroup LUT build stays amortized.  Short
+  // key ranges take one split: the per-unit kernel then writes the output
+  // rows itself, and the merge launch it saves costs more than the longer
+  // scan.
   const long long units = (long long)B * Hkv * ((pl->rows + 7) / 8);
-  const long long target = std::max<long long>(1, (1024 + units - 1) / units);
+  const long long target =
+      max_range <= kOneSplitKeys ? 1 : std::max<long long>(1, (1024 + units - 1) / units);
   long long T = (max_range + target - 1) / target;
   T = (T + 63) / 64 * 64;
   T = std::max<long long>(T, 256);

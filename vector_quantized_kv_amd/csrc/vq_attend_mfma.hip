@@ -138,14 +138,16 @@ __device__ __forceinline__ void wave_sync_lds() {
 }
 
 // One split of one (batch row b, kv head g, row group rg): writes the
-// partial (m, l, acc[D]) of each of the R rows to out_part.
+// partial (m, l, acc[D]) of each of the R rows to out_part, or, when `out`
+// is given (the only split of its rows), the normalized fp16 rows to out
+// with the merge's arithmetic (a / l, 0 for a row with no valid key).
 template <int D, int R, int NSK>
 __device__ __forceinline__ void split_body(
     const __half* __restrict__ q, const uint8_t* __restrict__ kcodes,
     const float* __restrict__ kcb, const float* __restrict__ smooth,
     const uint8_t* __restrict__ vcodes, const float* __restrict__ vcb,
-    float* __restrict__ out_part, const AttParams& p, int b, int g, int rg, int len,
-    int s_lo, int s_hi) {
+    float* __restrict__ out_part, __half* __restrict__ out, const AttParams& p, int b, int g,
+    int rg, int len, int s_lo, int s_hi) {
   constexpr int NSV = D / 4;     // value sub-vectors
   constexpr int NW = NSV / 16;   // 16-subspace groups per token
   constexpr int DK = D / NSK;    // key sub_dim
@@ -465,6 +467,13 @@ __device__ __forceinline__ void split_body(
       a += om * sw;
       lt += om * wl[w * R + r];
     }
+    if (out) {
+      const int gr = rg * R + r;  // query row of the kv head: (head hl, position i)
+      const int hl = gr / p.Sq, i = gr - hl * p.Sq;
+      out[((size_t)(b * p.Hq + g * p.G + hl) * p.Sq + i) * D + d] =
+          __float2half_rn(lt > 0.f ? a / lt : 0.f);
+      continue;
+    }
     out_part[r * (D + 2) + 2 + d] = a;
     if (d == 0) {
       out_part[r * (D + 2)] = M;
@@ -478,7 +487,8 @@ __global__ __launch_bounds__(kThreads, 4) void attend_mfma_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ kcodes,
     const float* __restrict__ kcb, const float* __restrict__ smooth,
     const uint8_t* __restrict__ vcodes, const float* __restrict__ vcb,
-    const int32_t* __restrict__ kv_lens, float* __restrict__ part, AttParams p) {
+    const int32_t* __restrict__ kv_lens, float* __restrict__ part, __half* __restrict__ out,
+    AttParams p) {
   const int unit = blockIdx.x;  // b * Hkv + g
   const int rg = blockIdx.y;
   const int s = blockIdx.z;
@@ -489,7 +499,19 @@ __global__ __launch_bounds__(kThreads, 4) void attend_mfma_kernel(
   const int s_lo = lo_all + s * p.split_tokens;
   const int s_hi = min(s_lo + p.split_tokens, len);
   float* out_part = part + (((size_t)unit * p.n_rgroups + rg) * p.n_split + s) * R * (D + 2);
+  // a single split writes the output rows itself (no merge launch)
+  __half* const direct = p.n_split == 1 ? out : nullptr;
   if (s_lo >= s_hi) {
+    if (direct) {
+      // no valid key for these rows: zeros
+      for (int idx = threadIdx.x; idx < R * D; idx += kThreads) {
+        const int r = idx / D, d = idx % D, gr = rg * R + r;
+        if (gr >= p.rows) continue;
+        const int hl = gr / p.Sq, i = gr - hl * p.Sq;
+        direct[((size_t)(b * p.Hq + g * p.G + hl) * p.Sq + i) * D + d] = __float2half_rn(0.f);
+      }
+      return;
+    }
     // nothing to attend in this split: an empty partial
     if (threadIdx.x < R) {
       out_part[threadIdx.x * (D + 2)] = -INFINITY;
@@ -497,8 +519,8 @@ __global__ __launch_bounds__(kThreads, 4) void attend_mfma_kernel(
     }
     return;
   }
-  split_body<D, R, NSK>(q, kcodes, kcb, smooth, vcodes, vcb, out_part, p, b, g, rg, len, s_lo,
-                        s_hi);
+  split_body<D, R, NSK>(q, kcodes, kcb, smooth, vcodes, vcb, out_part, direct, p, b, g, rg, len,
+                        s_lo, s_hi);
 }
 
 template <int D, int R, int NSK>
@@ -509,7 +531,7 @@ hipError_t launch3(const AttendArgs& a, const AttParams& p, size_t lds, hipStrea
   if (e != hipSuccess) return e;
   dim3 grid(a.B * a.Hkv, p.n_rgroups, p.n_split);
   hipLaunchKernelGGL(k, grid, dim3(kThreads), lds, st, a.q, a.k_codes, a.k_codebook, a.smooth,
-                     a.v_codes, a.v_codebook, a.kv_lens, a.partials, p);
+                     a.v_codes, a.v_codebook, a.kv_lens, a.partials, a.out, p);
   return hipGetLastError();
 }
 
@@ -554,6 +576,7 @@ hipError_t launch_attend_mfma(const AttendArgs& a, const AttParams& p, size_t ld
     case 128: e = launch1<128>(a, p, lds, st); break;
   }
   if (e != hipSuccess) return e;
+  if (p.n_split == 1) return hipSuccess;  // the kernel wrote the rows
   // The splits are combined by a second, small kernel.  (Merging in the last
   // workgroup of each unit needs device-scope release/acquire fences, which
   // on this part write back / invalidate the L2 and cost far more than the
