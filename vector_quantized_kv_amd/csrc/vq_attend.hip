@@ -417,8 +417,9 @@ bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, A
   const long long max_range =
       window > 0 ? std::min<long long>(S_cap, (long long)Sq + window - 1) : S_cap;
   // Aim for about 1024 workgroups (4 per CU on 256 CUs) across the
-  // independent (batch row, kv head, 8-row group) units, with at least 256
-  // keys per split so the per-workgroup LUT build stays amortized.  Short
+  // independent (batch row, kv head, 8-row group) units, with at least 512
+  // keys per split so the per-workgroup LUT build stays amortized (256 and
+  // 1024 measured slower on single-query decode at 2048 and 8192 keys).  Short
   // key ranges take one split: the per-unit kernel then writes the output
   // rows itself, and the merge launch it saves costs more than the longer
   // scan.
@@ -427,7 +428,7 @@ bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, A
       max_range <= kOneSplitKeys ? 1 : std::max<long long>(1, (1024 + units - 1) / units);
   long long T = (max_range + target - 1) / target;
   T = (T + 63) / 64 * 64;
-  T = std::max<long long>(T, 256);
+  T = std::max<long long>(T, 512);
   pl->split_tokens = (int)T;
   pl->n_split = (int)std::max<long long>(1, (max_range + T - 1) / T);
   const long long rows8 = (pl->rows + 7) / 8 * 8;
