@@ -616,7 +616,8 @@ def test_encode_kv(B, H, S, D, dk, dv, S_cap, per_row):
     xk = O.forward_transform(k, s, True).reshape(-1, dk)
     xv = v.astype(np.float64).reshape(-1, dv)
     Ck = synth.sample_rows(rng, xk, min(256, len(xk)))
-    Cv = synth.sample_rows(rng, xv, min(256, len(xv)))
+    # a value codebook of fewer centroids than the key codebook's 256
+    Cv = synth.sample_rows(rng, xv, min(256 if per_row else 100, len(xv)))
     if per_row:
         offs = [int(x) for x in rng.integers(0, S_cap - S + 1, size=B)]
         kw = dict(row_offsets=offs)
