@@ -38,6 +38,9 @@
  *     stream) and returns without synchronizing.  The caller owns every
  *     buffer; the library allocates no device memory and keeps no state
  *     between calls other than cached device attributes.
+ *   - A call enqueues kernel launches only (no memset, copy or allocation),
+ *     so calls may be captured into a HIP graph and replayed; a replay
+ *     reuses the arguments of the captured call, including per-row offsets.
  *   - Errors: arguments are validated on the host before any HIP call; on
  *     failure nothing is enqueued and a nonzero status is returned, with a
  *     message available from vq_last_error().  Device data (codes, lengths)

@@ -662,3 +662,54 @@ def test_single_split_direct_output():
     w["kv_lens"] = np.array([6000, 3000, 10], np.int32)
     w["window"] = 700                       # key range 701: one split
     check_attn(run_attend(w), oracle_attend(w, w["k_codes"], w["v_codes"]), "one split, window 700")
+
+
+def test_graph_capture_decode_step():
+    """The decode step (vq_encode_kv of one token per row, then vq_attend on
+    the streaming kernel) captured in a HIP graph and replayed with new
+    inputs, with eager calls between the replays: every replay writes the
+    eager codes and matches the eager output and the oracle."""
+    from vector_quantized_kv_amd import attend_workspace, vq_encode_kv
+    c = small_case(401, B=4, Hq=32, Hkv=8, Sq=1, D=128, dk=8, dv=4, S_cap=8192)
+    c["kv_lens"] = np.array([8192, 6000, 77, 8000], np.int32)
+    assert path_of(c) == "stream"
+    kc, vc = dev(c["k_codes"]), dev(c["v_codes"])
+    kb, vb, sm, kl = dev(c["k_codebook"]), dev(c["v_codebook"]), dev(c["smooth"]), dev(c["kv_lens"])
+    offs = [int(x) - 1 for x in c["kv_lens"]]
+    q = torch.empty((4, 32, 1, 128), dtype=torch.float16, device=DEV)
+    kn = torch.empty((4, 8, 1, 128), dtype=torch.float16, device=DEV)
+    vn = torch.empty_like(kn)
+    out = torch.empty_like(q)
+    ws = attend_workspace(q, kc, 0)
+
+    def new_inputs(seed):
+        r = np.random.default_rng(seed)
+        q.copy_(dev(synth.outlier_normal(r, (4, 32, 1, 128), 2)))
+        kn.copy_(dev(synth.outlier_normal(r, (4, 8, 1, 128), 2)))
+        vn.copy_(dev(synth.outlier_normal(r, (4, 8, 1, 128), 2)))
+
+    def step():
+        vq_encode_kv(kn, vn, kb, 8, vb, 4, smooth=sm, k_codes=kc, v_codes=vc, row_offsets=offs)
+        vq_attend(q, kc, kb, vc, vb, scale=c["scale"], smooth=sm, kv_lens=kl, causal=True,
+                  sliding_window=0, out=out, workspace=ws)
+
+    new_inputs(0)
+    step()                                   # eager warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        new_inputs(10 + rep)
+        g.replay()
+        torch.cuda.synchronize()
+        got, gk, gv = out.clone(), kc.clone(), vc.clone()
+        step()                               # eager, same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(gk, kc) and torch.equal(gv, vc), f"replay {rep}: codes differ from eager"
+        # the streaming kernel's waves claim blocks dynamically, so sums may
+        # round differently between runs
+        assert (got.float() - out.float()).abs().max().item() <= 2e-3, f"replay {rep}"
+        p = dict(c, q=q.cpu().numpy())
+        check_attn(got.cpu().numpy(), oracle_attend(p, kc.cpu().numpy(), vc.cpu().numpy()),
+                   f"graph replay {rep}")
