@@ -49,6 +49,7 @@
 #include "vq_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace vq {
@@ -882,16 +883,18 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(const int* __restrict
       __floats2half2_rn(acc.x * inv, acc.y * inv);
 }
 
+// CUs of the current device, cached per device (any thread may launch:
+// relaxed atomics, and racing threads store the same value).
 int cached_cu_count() {
-  static int cus[64];
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] <= 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 }  // namespace
