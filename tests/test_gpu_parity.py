@@ -713,3 +713,20 @@ def test_graph_capture_decode_step():
         p = dict(c, q=q.cpu().numpy())
         check_attn(got.cpu().numpy(), oracle_attend(p, kc.cpu().numpy(), vc.cpu().numpy()),
                    f"graph replay {rep}")
+
+
+@pytest.mark.parametrize("S_cap,lens,window", [
+    (8255, [8255, 8254, 4097, 63], 0),     # buffer length not a multiple of the 64-key block
+    (8255, [8255, 8192, 8191, 1] + [2100 + 300 * i for i in range(12)], 2100),  # B = 16, a window
+])
+def test_stream_kernel_ragged_buffer(S_cap, lens, window):
+    """The streaming kernel's blocks read past S_cap through range-checked
+    loads (zeros there, always masked): a buffer whose length is not a
+    multiple of 64, rows filling it, every output row against the oracle."""
+    B = len(lens)
+    c = small_case(700 + B + window, B=B, Hq=32, Hkv=8, Sq=1, D=128, dk=8, dv=4, S_cap=S_cap)
+    c["kv_lens"] = np.array(lens, np.int32)
+    c["window"] = window
+    assert path_of(c) == "stream"
+    out = run_attend(c)
+    check_attn(out, oracle_attend(c, c["k_codes"], c["v_codes"]), f"stream S_cap {S_cap} W{window}")
