@@ -730,3 +730,30 @@ def test_stream_kernel_ragged_buffer(S_cap, lens, window):
     assert path_of(c) == "stream"
     out = run_attend(c)
     check_attn(out, oracle_attend(c, c["k_codes"], c["v_codes"]), f"stream S_cap {S_cap} W{window}")
+
+
+@pytest.mark.parametrize("family", ["tile", "lut_mfma"])
+@pytest.mark.parametrize("transform,smooth,n_c", [
+    (False, "none", 256),     # no rotation, no smoothing
+    (True, "shared", 100),    # one smooth row for every kv head; fewer centroids
+    (False, "per_head", 7),
+])
+def test_tile_and_unit_kernel_options(family, transform, smooth, n_c):
+    """The many-query (prefill) and per-unit kernels with the query-transform
+    and codebook options, against the oracle on every output row."""
+    rng = np.random.default_rng(80 + n_c + 2 * int(transform) + len(family))
+    if family == "tile":
+        c = small_case(81 + n_c, B=3, Hq=4, Hkv=2, Sq=100, D=128, dk=8, dv=4, n_c=n_c, S_cap=400)
+        c["kv_lens"] = np.array([400, 130, 100], np.int32)
+    else:
+        c = small_case(82 + n_c, B=3, Hq=8, Hkv=2, Sq=2, D=128, dk=8, dv=4, n_c=n_c, S_cap=600)
+        c["kv_lens"] = np.array([600, 257, 0], np.int32)
+    c["transform"] = transform
+    assert path_of(c) == family
+    if smooth == "none":
+        c["smooth"] = None
+    elif smooth == "shared":
+        c["smooth"] = rng.uniform(0.5, 5, size=128).astype(np.float32)
+    out = run_attend(c)
+    check_attn(out, oracle_attend(c, c["k_codes"], c["v_codes"]),
+               f"{family} transform{transform} smooth {smooth} n_c {n_c}")
