@@ -213,3 +213,56 @@ def test_attend_path_rejects_what_attend_rejects(lib):
     with pytest.raises(api.VQError):
         api.vq_attend_path(1, 8, 1, 128, 8, 4, 257, 8, 100)      # more than 256 centroids
     assert lib.vq_attend_path(0, 8, 1, 128, 8, 4, 256, 8, 100, 0) == 0
+
+
+def test_binding_rejects_wrong_shapes(lib):
+    """The C ABI receives bare pointers and sizes, so the binding checks every
+    buffer's shape against the others before any call (host tensors here:
+    the shape checks come before the device check)."""
+    f16, f32, u8, i32 = torch.float16, torch.float32, torch.uint8, torch.int32
+    k = torch.zeros(2, 3, 8, 64, dtype=f16)
+    cb = torch.zeros(256, 4)
+    cases = [
+        (lambda: api.vq_encode(k, cb, 4, codes=torch.zeros(2, 3, 8, 8, dtype=u8)), "codes"),
+        (lambda: api.vq_encode(k, cb, 4, codes=torch.zeros(1, 3, 8, 16, dtype=u8)), "codes"),
+        (lambda: api.vq_encode(k, cb, 4, codes=torch.zeros(2, 3, 8, 16, dtype=u8), S_cap=9), "codes"),
+        (lambda: api.vq_encode(k, torch.zeros(256, 8), 4), "codebook"),
+        (lambda: api.vq_encode(k, cb, 3), "divide"),
+        (lambda: api.vq_encode(k, cb, 4, smooth=torch.zeros(3, 32)), "smooth"),
+        (lambda: api.vq_encode(k, cb, 4, smooth=torch.zeros(2, 64)), "smooth"),
+        (lambda: api.vq_encode(k, cb, 4, row_offsets=[0]), "row_offsets"),
+        (lambda: api.vq_encode_decode(k, cb, 4, recon=torch.zeros(2, 3, 7, 64, dtype=f16)), "recon"),
+        (lambda: api.vq_encode_decode(k, cb, 4, recon=torch.zeros(2, 3, 8, 64, dtype=torch.float64)),
+         "recon"),
+        (lambda: api.vq_decode(torch.zeros(2, 3, 8, 16, dtype=u8), cb, S=4,
+                               out=torch.zeros(2, 3, 5, 64)), "out"),
+        (lambda: api.vq_decode(torch.zeros(2, 3, 8, 16, dtype=u8), cb,
+                               out=torch.zeros(2, 3, 64, 8).transpose(2, 3)), "out"),
+        (lambda: api.vq_encode_kv(k, torch.zeros(2, 3, 8, 32, dtype=f16), cb, 4, cb, 4), "values"),
+        (lambda: api.vq_encode_kv(k, k, cb, 4, cb, 4, k_codes=torch.zeros(2, 3, 8, 16, dtype=u8),
+                                  v_codes=torch.zeros(2, 3, 9, 16, dtype=u8)), "v_codes"),
+    ]
+    q = torch.zeros(2, 8, 1, 64, dtype=f16)
+    kc = torch.zeros(2, 4, 100, 16, dtype=u8)
+    att_kw = dict(scale=0.1)
+    cases += [
+        (lambda: api.vq_attend(q, torch.zeros(3, 4, 100, 16, dtype=u8), cb, kc, cb, **att_kw), "k_codes"),
+        (lambda: api.vq_attend(q, torch.zeros(2, 4, 100, 8, dtype=u8), cb, kc, cb, **att_kw), "k_codes"),
+        (lambda: api.vq_attend(q, kc, cb, torch.zeros(2, 4, 99, 16, dtype=u8), cb, **att_kw), "v_codes"),
+        (lambda: api.vq_attend(q, kc, cb, kc, cb, kv_lens=torch.zeros(3, dtype=i32), **att_kw),
+         "kv_lens"),
+        (lambda: api.vq_attend(q, kc, cb, kc, cb, out=torch.zeros(2, 8, 1, 32, dtype=f16), **att_kw),
+         "out"),
+        (lambda: api.vq_attend(q, kc, cb, kc, cb, smooth=torch.zeros(4, 65), **att_kw), "smooth"),
+        (lambda: api.vq_attend(q, kc, cb, kc, torch.zeros(100, 4), **att_kw), "n_centroids"),
+        (lambda: api.vq_attend(q, kc, cb, kc, cb, workspace=torch.zeros(4, 4, dtype=u8), **att_kw),
+         "workspace"),
+    ]
+    for i, (fn, what) in enumerate(cases):
+        with pytest.raises(ValueError, match=what):
+            fn()
+    # consistent shapes get as far as the device check
+    with pytest.raises(ValueError, match="device tensor"):
+        api.vq_attend(q, kc, cb, kc, cb, kv_lens=torch.zeros(2, dtype=i32),
+                      out=torch.zeros(2, 8, 1, 64, dtype=f16), workspace=torch.zeros(16, dtype=u8),
+                      smooth=torch.zeros(4, 64), **att_kw)

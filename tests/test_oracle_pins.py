@@ -80,6 +80,40 @@ def pin_encode_golden(o):
     assert np.array_equal(codes2, codes)
 
 
+def pin_distances_and_gap_golden(o):
+    """The squared-distance table and the near-tie gap against the hand-worked
+    example: every sub-vector's distance to each centroid, and (d2 - d1) / d2
+    from its two smallest distances (one exact tie, gaps of 0.8 and 8/13)."""
+    g, D, d, keys, s, C = _golden_encode_inputs()
+    xt = o.forward_transform(keys, s, True)
+    dist = o.pvq_distances(xt, C, d)                              # [1, 1, 4, 2, 4]
+    assert dist.shape == (1, 1, 4, 2, 4)
+    assert np.array_equal(dist.reshape(-1), g["distances"])
+    _, gap = o.encode(keys, C, d, s, True)
+    want = g["gap_num"] / g["gap_den"]
+    assert np.max(np.abs(gap.reshape(-1) - want)) < 1e-15
+
+
+def pin_gap_bruteforce(o):
+    """pvq_distances and the gap of pvq_encode against pure-Python loops on
+    tiny inputs: every squared distance written out term by term, the two
+    smallest found by a full sort, gap = (d2 - d1) / d2."""
+    rng = np.random.default_rng(17)
+    for D, d, nc in [(8, 2, 5), (12, 4, 7), (6, 3, 2)]:
+        x = rng.standard_normal((1, 2, 3, D))
+        C = rng.standard_normal((nc, d))
+        dist = o.pvq_distances(x, C, d)
+        _, gap = o.pvq_encode(x, C, d)
+        for h in range(2):
+            for t in range(3):
+                for j in range(D // d):
+                    ds = [sum((float(x[0, h, t, j * d + e]) - float(C[c, e])) ** 2 for e in range(d))
+                          for c in range(nc)]
+                    assert max(abs(a - b) for a, b in zip(ds, dist[0, h, t, j])) < 1e-12
+                    srt = sorted(ds)
+                    assert abs(gap[0, h, t, j] - (srt[1] - srt[0]) / srt[1]) < 1e-12
+
+
 def pin_bruteforce(o):
     """Exhaustive search over whole code tuples equals the per-sub-vector
     argmin (product-VQ separability), with the rotation and smoothing
@@ -334,7 +368,8 @@ def pin_randomized_hadamard(o):
 
 
 ALL_PINS = [pin_hadamard_closed_form, pin_hadamard_golden, pin_hadamard_orthonormal,
-            pin_storage, pin_encode_golden, pin_bruteforce, pin_ties, pin_identity_codebook,
+            pin_storage, pin_encode_golden, pin_distances_and_gap_golden, pin_gap_bruteforce,
+            pin_bruteforce, pin_ties, pin_identity_codebook,
             pin_idempotent_and_permutation, pin_attend_golden, pin_attend_sdpa,
             pin_attend_closed_forms, pin_gqa_and_window, pin_dual_transform,
             pin_dense_transform, pin_randomized_hadamard]
@@ -509,10 +544,47 @@ def _lut_with(rot, q, C, d, s, t):
     return qt.reshape(-1, d) @ np.asarray(C, dtype=np.float64).T
 
 
+def _mut_gap_relative_to_d1(mp):
+    # the near-tie gap taken relative to the smaller distance: (d2 - d1) / d1
+    orig = O.pvq_encode
+
+    def enc(x, C, d, chunk_rows=1 << 15):
+        c, g = orig(x, C, d, chunk_rows)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            return c, np.where(g < 1, g / (1 - g), np.inf)
+    mp.setattr(O, "pvq_encode", enc)
+
+
+def _mut_gap_third_smallest(mp):
+    # the gap from the smallest and the third-smallest distance
+    orig = O.pvq_encode
+
+    def enc(x, C, d, chunk_rows=1 << 15):
+        c, _ = orig(x, C, d, chunk_rows)
+        dist = O.pvq_distances(np.asarray(x, dtype=np.float64), C, d)
+        srt = np.sort(dist, -1)
+        k = min(2, srt.shape[-1] - 1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            return c, np.where(srt[..., k] > 0, (srt[..., k] - srt[..., 0]) / srt[..., k], 0.0)
+    mp.setattr(O, "pvq_encode", enc)
+
+
+def _mut_distances_transposed(mp):
+    # the distance table built from a transposed reshape of the sub-vectors
+    def dist(x, C, sub_dim):
+        x = np.asarray(x, dtype=np.float64)
+        C = np.asarray(C, dtype=np.float64)
+        n_sub = x.shape[-1] // sub_dim
+        r = np.swapaxes(x.reshape(*x.shape[:-1], sub_dim, n_sub), -1, -2)[..., None, :]
+        return np.sum((r - C) ** 2, axis=-1)
+    mp.setattr(O, "pvq_distances", dist)
+
+
 MUTATIONS = [_mut_matrix_involutory, _mut_dual_untransposed, _mut_smooth_direction, _mut_unnormalized_hadamard, _mut_no_inverse_rotation,
              _mut_ties_high, _mut_strided_split, _mut_head_aligned_causal,
              _mut_window_off_by_one, _mut_window_needs_causal, _mut_gqa_modulo,
-             _mut_lut_divides, _mut_missing_scale, _mut_value_transposed]
+             _mut_lut_divides, _mut_missing_scale, _mut_value_transposed,
+             _mut_gap_relative_to_d1, _mut_gap_third_smallest, _mut_distances_transposed]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda m: m.__name__)

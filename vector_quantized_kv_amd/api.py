@@ -1,9 +1,11 @@
 """Python binding of libvq: same names as the C ABI, torch tensors in and out.
 
-Argument marshalling only: shapes are read off the tensors, device pointers
-and the current HIP stream are passed to the C functions, and a nonzero
-status becomes a VQError.  Every step of the computation runs in the HIP
-kernels of libvq.so; there is no other implementation behind these calls.
+Argument marshalling only: shapes are read off the tensors and checked
+against each other (the C ABI receives bare pointers and sizes, so a buffer of
+the wrong shape would otherwise be read or written out of bounds), device
+pointers and the current HIP stream are passed to the C functions, and a
+nonzero status becomes a VQError.  Every step of the computation runs in the
+HIP kernels of libvq.so; there is no other implementation behind these calls.
 """
 from __future__ import annotations
 
@@ -51,29 +53,66 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _need(t, name, dtype, ndim):
+def _need(t, name, dtype, ndim=None, shape=None):
+    """dtype (one or a tuple), rank, exact shape (None entries are free) and
+    contiguity.  The device is checked afterwards by _on_device, so a wrong
+    shape is reported as such on any host."""
     if t is None:
         raise ValueError(f"{name} is required")
-    if t.dtype != dtype:
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.dim() != ndim:
+    if shape is not None:
+        ndim = len(shape)
+    if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    if shape is not None and any(w is not None and g != w for g, w in zip(t.shape, shape)):
+        want = tuple("*" if w is None else w for w in shape)
+        raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
-def _smooth(smooth):
+def _on_device(**tensors):
+    """Every tensor given (None entries skipped) lives on one and the same GPU."""
+    devs = set()
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"tensors are on different devices: {sorted(map(str, devs))}")
+
+
+def _smooth(smooth, D, n_heads):
+    """(tensor, rows) of the smooth factors: None, [D] (one row shared by
+    every head) or [1 or n_heads, D]."""
     if smooth is None:
         return None, 1
-    if smooth.dtype != torch.float32 or not smooth.is_cuda or not smooth.is_contiguous():
-        raise ValueError("smooth must be a contiguous fp32 device tensor")
-    if smooth.dim() == 1:
+    if smooth.dtype != torch.float32 or not smooth.is_contiguous():
+        raise ValueError("smooth must be a contiguous fp32 tensor")
+    if smooth.dim() == 1 and smooth.shape[0] == D:
         return smooth, 1
-    if smooth.dim() == 2:
+    if smooth.dim() == 2 and smooth.shape[1] == D and smooth.shape[0] in (1, n_heads):
         return smooth, smooth.shape[0]
-    raise ValueError("smooth must be [D] or [H, D]")
+    raise ValueError(f"smooth must be [{D}] or [1 or {n_heads}, {D}], got {tuple(smooth.shape)}")
+
+
+def _offsets(row_offsets, B):
+    """Host int32 array of the per-row write offsets (None: use S_off)."""
+    if row_offsets is None:
+        return None
+    offs = [int(x) for x in row_offsets]
+    if len(offs) != B:
+        raise ValueError(f"row_offsets must hold B = {B} entries, got {len(offs)}")
+    return (ctypes.c_int32 * B)(*offs)
+
+
+def _n_sub(D, sub_dim, name="sub_dim"):
+    if sub_dim <= 0 or D % sub_dim:
+        raise ValueError(f"{name} {sub_dim} does not divide the head dim {D}")
+    return D // sub_dim
 
 
 def vq_supports_shape(n_centroids: int, n_sub: int, head_dim: int) -> bool:
@@ -87,15 +126,15 @@ def vq_encode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=Non
     Codes of token t of row b land in slot off_b + t (off_b = row_offsets[b]
     or S_off).  Returns the code tensor (allocated when `codes` is None)."""
     _need(keys, "keys", torch.float16, 4)
-    _need(codebook, "codebook", torch.float32, 2)
     B, H, S, D = keys.shape
+    n_sub = _n_sub(D, sub_dim)
+    _need(codebook, "codebook", torch.float32, shape=(None, sub_dim))
     if codes is None:
-        codes = torch.zeros((B, H, S_cap or S, D // sub_dim), dtype=torch.uint8, device=keys.device)
-    _need(codes, "codes", torch.uint8, 4)
-    sm, rows = _smooth(smooth)
-    offs = None
-    if row_offsets is not None:
-        offs = (ctypes.c_int32 * B)(*[int(x) for x in row_offsets])
+        codes = torch.zeros((B, H, S_cap or S, n_sub), dtype=torch.uint8, device=keys.device)
+    _need(codes, "codes", torch.uint8, shape=(B, H, S_cap, n_sub))
+    sm, rows = _smooth(smooth, D, H)
+    offs = _offsets(row_offsets, B)
+    _on_device(keys=keys, codebook=codebook, codes=codes, smooth=sm)
     return _call("vq_encode", _ptr(keys), B, H, S, D, _ptr(codebook), codebook.shape[0], sub_dim,
                  _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off, offs,
                  _stream(stream), prepare=prepare, result=codes)
@@ -107,24 +146,21 @@ def vq_encode_kv(keys, values, k_codebook, k_sub_dim, v_codebook, v_sub_dim, *, 
     """Encode the keys (smoothed, rotated) and the values (neither) of one
     append into their code buffers; returns (k_codes, v_codes)."""
     _need(keys, "keys", torch.float16, 4)
-    _need(values, "values", torch.float16, 4)
-    _need(k_codebook, "k_codebook", torch.float32, 2)
-    _need(v_codebook, "v_codebook", torch.float32, 2)
     B, H, S, D = keys.shape
-    if tuple(values.shape) != (B, H, S, D):
-        raise ValueError("keys and values must have the same shape")
+    _need(values, "values", torch.float16, shape=(B, H, S, D))
+    nk, nv = _n_sub(D, k_sub_dim, "k_sub_dim"), _n_sub(D, v_sub_dim, "v_sub_dim")
+    _need(k_codebook, "k_codebook", torch.float32, shape=(None, k_sub_dim))
+    _need(v_codebook, "v_codebook", torch.float32, shape=(None, v_sub_dim))
     if k_codes is None:
-        k_codes = torch.zeros((B, H, S_cap or S, D // k_sub_dim), dtype=torch.uint8, device=keys.device)
+        k_codes = torch.zeros((B, H, S_cap or S, nk), dtype=torch.uint8, device=keys.device)
     if v_codes is None:
-        v_codes = torch.zeros((B, H, S_cap or S, D // v_sub_dim), dtype=torch.uint8, device=keys.device)
-    _need(k_codes, "k_codes", torch.uint8, 4)
-    _need(v_codes, "v_codes", torch.uint8, 4)
-    if k_codes.shape[2] != v_codes.shape[2]:
-        raise ValueError("k_codes and v_codes must have the same S_cap")
-    sm, rows = _smooth(smooth)
-    offs = None
-    if row_offsets is not None:
-        offs = (ctypes.c_int32 * B)(*[int(x) for x in row_offsets])
+        v_codes = torch.zeros((B, H, S_cap or S, nv), dtype=torch.uint8, device=keys.device)
+    _need(k_codes, "k_codes", torch.uint8, shape=(B, H, S_cap, nk))
+    _need(v_codes, "v_codes", torch.uint8, shape=(B, H, k_codes.shape[2], nv))
+    sm, rows = _smooth(smooth, D, H)
+    offs = _offsets(row_offsets, B)
+    _on_device(keys=keys, values=values, k_codebook=k_codebook, v_codebook=v_codebook,
+               k_codes=k_codes, v_codes=v_codes, smooth=sm)
     return _call("vq_encode_kv", _ptr(keys), _ptr(values), B, H, S, D, _ptr(k_codebook),
                  k_codebook.shape[0], k_sub_dim, _ptr(sm), rows, int(bool(transform)),
                  _ptr(v_codebook), v_codebook.shape[0], v_sub_dim, _ptr(k_codes), _ptr(v_codes),
@@ -137,19 +173,18 @@ def vq_encode_decode(keys, codebook, sub_dim, *, smooth=None, transform=True, co
                      out_dtype=torch.float16, stream=None, prepare=False):
     """Fused encode + reconstruction.  Returns (recon [B, H, S, D], codes)."""
     _need(keys, "keys", torch.float16, 4)
-    _need(codebook, "codebook", torch.float32, 2)
     B, H, S, D = keys.shape
+    n_sub = _n_sub(D, sub_dim)
+    _need(codebook, "codebook", torch.float32, shape=(None, sub_dim))
     if codes is None:
-        codes = torch.zeros((B, H, S_cap or S, D // sub_dim), dtype=torch.uint8, device=keys.device)
-    _need(codes, "codes", torch.uint8, 4)
+        codes = torch.zeros((B, H, S_cap or S, n_sub), dtype=torch.uint8, device=keys.device)
+    _need(codes, "codes", torch.uint8, shape=(B, H, S_cap, n_sub))
     if recon is None:
         recon = torch.empty((B, H, S, D), dtype=out_dtype, device=keys.device)
-    if recon.dtype not in (torch.float32, torch.float16):
-        raise ValueError("recon must be fp32 or fp16")
-    sm, rows = _smooth(smooth)
-    offs = None
-    if row_offsets is not None:
-        offs = (ctypes.c_int32 * B)(*[int(x) for x in row_offsets])
+    _need(recon, "recon", (torch.float32, torch.float16), shape=(B, H, S, D))
+    sm, rows = _smooth(smooth, D, H)
+    offs = _offsets(row_offsets, B)
+    _on_device(keys=keys, codebook=codebook, codes=codes, recon=recon, smooth=sm)
     return _call("vq_encode_decode", _ptr(keys), B, H, S, D, _ptr(codebook), codebook.shape[0],
                  sub_dim, _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off,
                  offs, _ptr(recon), 1 if recon.dtype == torch.float16 else 0, _stream(stream),
@@ -168,7 +203,9 @@ def vq_decode(codes, codebook, *, smooth=None, transform=True, S=None, S_off=0,
     S = S_cap - S_off if S is None else S
     if out is None:
         out = torch.empty((B, H, S, D), dtype=out_dtype, device=codes.device)
-    sm, rows = _smooth(smooth)
+    _need(out, "out", (torch.float32, torch.float16), shape=(B, H, S, D))
+    sm, rows = _smooth(smooth, D, H)
+    _on_device(codes=codes, codebook=codebook, out=out, smooth=sm)
     return _call("vq_decode", _ptr(codes), B, H, S, S_cap, S_off, _ptr(codebook), codebook.shape[0],
                  sub_dim, _ptr(sm), rows, int(bool(transform)), D, _ptr(out),
                  1 if out.dtype == torch.float16 else 0, _stream(stream), prepare=prepare,
@@ -202,35 +239,44 @@ def attend_workspace(q, k_codes, sliding_window=0):
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=q.device)
 
 
+def _attend_args(q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out):
+    """Shape checks shared by the attention entry points; returns the
+    marshalled sizes and the (allocated if None) output."""
+    _need(q, "q", torch.float16, 4)
+    B, Hq, Sq, D = q.shape
+    _need(k_codebook, "k_codebook", torch.float32, 2)
+    _need(v_codebook, "v_codebook", torch.float32, 2)
+    dk, dv = k_codebook.shape[1], v_codebook.shape[1]
+    nk, nv = _n_sub(D, dk, "key sub_dim"), _n_sub(D, dv, "value sub_dim")
+    if k_codebook.shape[0] != v_codebook.shape[0]:
+        raise ValueError("key and value codebooks disagree on n_centroids")
+    _need(k_codes, "k_codes", torch.uint8, shape=(B, None, None, nk))
+    Hkv, S_cap = k_codes.shape[1], k_codes.shape[2]
+    _need(v_codes, "v_codes", torch.uint8, shape=(B, Hkv, S_cap, nv))
+    if kv_lens is not None:
+        _need(kv_lens, "kv_lens", torch.int32, shape=(B,))
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float16, device=q.device)
+    _need(out, "out", torch.float16, shape=(B, Hq, Sq, D))
+    sm, rows = _smooth(smooth, D, Hkv)
+    return B, Hq, Sq, D, dk, dv, Hkv, S_cap, sm, rows, out
+
+
 def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None,
               transform=True, kv_lens=None, causal=True, sliding_window=0, out=None,
               workspace=None, stream=None, prepare=False):
     """Attention of raw fp16 queries [B, H_q, S_q, D] over key/value codes
     [B, H_kv, S_cap, n_sub]; returns fp16 [B, H_q, S_q, D]."""
-    _need(q, "q", torch.float16, 4)
-    _need(k_codes, "k_codes", torch.uint8, 4)
-    _need(v_codes, "v_codes", torch.uint8, 4)
-    _need(k_codebook, "k_codebook", torch.float32, 2)
-    _need(v_codebook, "v_codebook", torch.float32, 2)
-    B, Hq, Sq, D = q.shape
-    Hkv, S_cap = k_codes.shape[1], k_codes.shape[2]
-    if tuple(v_codes.shape[:3]) != (B, Hkv, S_cap) or k_codes.shape[0] != B:
-        raise ValueError("k_codes and v_codes must share [B, H_kv, S_cap]")
-    if k_codebook.shape[0] != v_codebook.shape[0]:
-        raise ValueError("key and value codebooks disagree on n_centroids")
-    if k_codes.shape[3] * k_codebook.shape[1] != D or v_codes.shape[3] * v_codebook.shape[1] != D:
-        raise ValueError("n_sub * sub_dim must equal D for keys and values")
-    if kv_lens is not None:
-        _need(kv_lens, "kv_lens", torch.int32, 1)
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.float16, device=q.device)
-    _need(out, "out", torch.float16, 4)
+    B, Hq, Sq, D, dk, dv, Hkv, S_cap, sm, rows, out = _attend_args(
+        q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out)
     if workspace is None:
         workspace = attend_workspace(q, k_codes, sliding_window)
-    sm, rows = _smooth(smooth)
+    _need(workspace, "workspace", None, 1)
+    _on_device(q=q, k_codes=k_codes, k_codebook=k_codebook, v_codes=v_codes,
+               v_codebook=v_codebook, kv_lens=kv_lens, out=out, workspace=workspace, smooth=sm)
     return _call("vq_attend", _ptr(q), B, Hq, Sq, D, _ptr(k_codes), _ptr(k_codebook),
-                 k_codebook.shape[1], _ptr(sm), rows, int(bool(transform)), _ptr(v_codes),
-                 _ptr(v_codebook), v_codebook.shape[1], k_codebook.shape[0], Hkv, S_cap,
+                 dk, _ptr(sm), rows, int(bool(transform)), _ptr(v_codes),
+                 _ptr(v_codebook), dv, k_codebook.shape[0], Hkv, S_cap,
                  _ptr(kv_lens), float(scale), int(bool(causal)), int(sliding_window), _ptr(out),
                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
                  prepare=prepare, result=out)
