@@ -41,21 +41,33 @@ def oracle_transform(keys, smooth):
 # comparison helpers
 # ----------------------------------------------------------------------------
 def check_codes(keys, codebook, sub_dim, smooth, transform, gpu_codes, tag=""):
-    """Compare GPU codes [B, H, S, n_sub] with the oracle under the near-tie rule."""
+    """Compare GPU codes [B, H, S, n_sub] with the oracle under the near-tie
+    rule; returns the number of (near-tie) mismatches, which is printed."""
     ref, gap = O.encode(keys, codebook, sub_dim, smooth, transform)
     gpu = np.asarray(gpu_codes).astype(np.int64)
     mism = gpu != ref
     n = int(mism.sum())
     if n:
         assert np.all(gap[mism] < NEAR_TIE), f"{tag}: {n} code mismatches, some not near-ties"
+        # distances of the mismatched sub-vectors only: [n, 1, n_c]
         xt = O.forward_transform(keys, smooth, transform)
-        dist = O.pvq_distances(xt, codebook, sub_dim)             # [..., n_sub, n_c]
-        d_gpu = np.take_along_axis(dist, gpu[..., None], -1)[..., 0]
+        sv = xt.reshape(*xt.shape[:-1], -1, sub_dim)[mism]
+        dist = O.pvq_distances(sv, codebook, sub_dim)[:, 0]
+        d_gpu = dist[np.arange(n), gpu[mism]]
         srt = np.sort(dist, -1)
-        d1, d2 = srt[..., 0], srt[..., 1]
-        assert np.all(d_gpu[mism] - d1[mism] <= NEAR_TIE * d2[mism]), f"{tag}: GPU code not near-optimal"
+        d1, d2 = srt[:, 0], srt[:, 1]
+        assert np.all(d_gpu - d1 <= NEAR_TIE * d2), f"{tag}: GPU code not near-optimal"
     print(f"[codes] {tag}: {gpu.size} codes, {n} near-tie mismatches")
     return n
+
+
+def fp16_ulp(x):
+    """The fp16 unit in the last place of the binade holding |x|: 2^(e - 10)
+    for 2^e <= |x| < 2^(e+1), and 2^-24 in the subnormal range.  (Not the
+    spacing of the rounded value: -8.0034 rounds to -8.0, whose spacing
+    toward zero is half the 2^-7 gap that -8.0034 sits in.)"""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -14)
+    return np.exp2(np.floor(np.log2(a)) - 10)
 
 
 def check_recon(gpu, ref64, dtype, tag=""):
@@ -63,11 +75,13 @@ def check_recon(gpu, ref64, dtype, tag=""):
     if dtype == "fp32":
         tol = 1e-3
     else:
-        r16 = ref64.astype(np.float16)
-        ulp = np.abs(np.spacing(r16).astype(np.float64))
-        tol = 1e-3 + 0.5 * ulp
+        tol = 1e-3 + 0.5 * fp16_ulp(ref64)
     err = np.abs(gpu - ref64)
-    assert np.all(err <= tol), f"{tag}: recon error {err.max():.3g}"
+    bad = err > tol
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"{tag}: {int(bad.sum())} reconstruction elements out of tolerance; "
+                             f"worst at {i}: gpu {gpu[i]!r} ref {ref64[i]!r} tol {tol[i] if np.ndim(tol) else tol:.3g}")
     print(f"[recon] {tag}: max abs err {err.max():.3g}")
 
 
@@ -135,25 +149,47 @@ def test_tiny_end_to_end():
 
 def test_identity_codebook_round_trip():
     """Codebook rows = transformed sub-vectors of 16 tokens: each sub-vector
-    encodes to its own row and the fp16 reconstruction returns the keys."""
+    encodes to its own row and the fp16 reconstruction returns the keys.
+
+    The reconstruction is computed in fp32: each element's rounding error is
+    at most (log2 D + 3) * 2^-24 * |s_c| * ||x~||_1 (the rotation's adds over
+    entries bounded by the transformed vector's 1-norm, the final scale and
+    the smooth multiply).  Every element whose half fp16 ulp exceeds that
+    bound must come back bit for bit; the others (keys within that bound of
+    an fp16 rounding boundary, i.e. tiny elements next to x20 outliers) are
+    held to the fp16 reconstruction bar."""
     c = synth.tiny()
     keys = np.ascontiguousarray(c["keys"][:, :1, :16])
     s = c["smooth"][:1]
-    C = O.forward_transform(keys, s, True).reshape(-1, c["dk"]).astype(np.float32)
+    D = keys.shape[-1]
+    xt = O.forward_transform(keys, s, True)
+    C = xt.reshape(-1, c["dk"]).astype(np.float32)
     rec, codes = vq_encode_decode(dev(keys), dev(C), c["dk"], smooth=dev(s))
     torch.cuda.synchronize()
     assert np.array_equal(codes.cpu().numpy().reshape(-1), np.arange(256))
     rec = rec.cpu().numpy()
-    same = np.mean(rec.view(np.uint16) == keys.view(np.uint16))
     check_recon(rec, keys.astype(np.float64), "fp16", "identity codebook")
-    print(f"[identity] bit-identical fp16 elements: {same:.4f}")
-    assert same > 0.98
+    bound = (math.log2(D) + 3) * 2.0 ** -24 * np.abs(s[0].astype(np.float64)) \
+        * np.abs(xt).sum(-1, keepdims=True)
+    k64 = keys.astype(np.float64)
+    up = np.nextafter(keys, np.float16(np.inf)).astype(np.float64) - k64
+    down = k64 - np.nextafter(keys, np.float16(-np.inf)).astype(np.float64)
+    must = np.minimum(up, down) / 2 > bound       # half the gap to either fp16 neighbour
+    same = rec.view(np.uint16) == keys.view(np.uint16)
+    print(f"[identity] bit-identical fp16 elements: {same.mean():.4f}; "
+          f"{int(must.sum())} of {must.size} must be, {int(same[must].sum())} are")
+    assert np.all(same[must]), "an element far from an fp16 rounding boundary did not round-trip"
 
 
 # ----------------------------------------------------------------------------
 # key encode throughput workload at full size (sampled oracle)
 # ----------------------------------------------------------------------------
-def test_encode_full_size_sampled():
+def test_encode_full_size():
+    """The key-encode workload [1, 8, 8192, 128] (d_k = 8, 256 centroids) in
+    the launch configuration the benchmark times: every token-head's codes
+    against the oracle (near-tie rule; the mismatch count is printed), and
+    every element of the fp16 reconstruction against the oracle's decode of
+    the GPU's codes."""
     c = synth.encode(oracle_transform)
     k, s, C = c["keys"], c["smooth"], c["k_codebook"]
     rec, codes = vq_encode_decode(dev(k), dev(C), c["dk"], smooth=dev(s))
@@ -161,15 +197,8 @@ def test_encode_full_size_sampled():
     torch.cuda.synchronize()
     codes, rec = codes.cpu().numpy(), rec.cpu().numpy()
     assert np.array_equal(codes_only.cpu().numpy(), codes)
-    rng = np.random.default_rng(0)
-    total = 0
-    for h in range(c["H"]):
-        ts = np.sort(rng.choice(c["S"], 256, replace=False))
-        kk = np.ascontiguousarray(k[:, h:h + 1, ts])
-        total += check_codes(kk, C, c["dk"], s[h:h + 1], True, codes[:, h:h + 1, ts], f"encode h{h}")
-        check_recon(rec[:, h:h + 1, ts], O.decode(codes[:, h:h + 1, ts], C, s[h:h + 1], True), "fp16",
-                    f"encode h{h}")
-    assert total <= 5
+    check_codes(k, C, c["dk"], s, True, codes, "encode workload")
+    check_recon(rec, O.decode(codes, C, s, True), "fp16", "encode workload")
 
 
 def test_decode_entry_point():
@@ -342,41 +371,81 @@ def test_decode_attend(S_kv):
 
 
 @pytest.mark.parametrize("window", [0, 4096])
-def test_gqa_long_sampled(window):
+def test_gqa_long_full(window):
+    """The batched long-context GQA decode (B = 16, H_q = 32, H_kv = 8,
+    32768-slot buffers, ragged lengths) on the streaming kernel the benchmark
+    times: all 512 output rows against the oracle."""
     enc = synth.encode(oracle_transform)
     c = synth.gqa_long(window, k_codebook=enc["k_codebook"], smooth=enc["smooth"])
+    assert path_of(c) == "stream"
     out = run_attend(c)
-    rng = np.random.default_rng(window + 1)
-    rows = [(b, int(h)) for b in range(c["B"]) for h in rng.choice(c["H_q"], 2, replace=False)]
-    rows = [rows[i] for i in rng.choice(len(rows), 12, replace=False)]
-    ref = oracle_attend(c, c["k_codes"], c["v_codes"], rows=rows)
-    for b, h in rows:
-        check_attn(out[b, h], ref[b, h], f"gqa W{window} b{b} h{h}")
+    check_attn(out, oracle_attend(c, c["k_codes"], c["v_codes"]), f"gqa_long W{window}")
 
 
-def test_prefill_append_and_attend_sampled():
+def test_prefill_append_and_attend_full():
+    """The prefill chunk: 512 new K/V tokens appended at slot 16384 of
+    32768-slot buffers with vq_encode_kv (as the benchmark does; vq_encode of
+    each half writes the same bytes), every appended code against the oracle,
+    untouched slots checked, then all 32 (b, h) x 512 query rows of the causal
+    attention over 16896 keys on the tile kernel against the oracle."""
+    from vector_quantized_kv_amd import vq_encode_kv
     c = synth.prefill(oracle_transform)
     kbuf, vbuf = dev(c["k_codes"]), dev(c["v_codes"])
-    vq_encode(dev(c["keys"]), dev(c["k_codebook"]), c["dk"], smooth=dev(c["smooth"]), codes=kbuf,
+    vq_encode_kv(dev(c["keys"]), dev(c["values"]), dev(c["k_codebook"]), c["dk"],
+                 dev(c["v_codebook"]), c["dv"], smooth=dev(c["smooth"]), k_codes=kbuf,
+                 v_codes=vbuf, S_off=c["S_off"])
+    kb2, vb2 = dev(c["k_codes"]), dev(c["v_codes"])
+    vq_encode(dev(c["keys"]), dev(c["k_codebook"]), c["dk"], smooth=dev(c["smooth"]), codes=kb2,
               S_off=c["S_off"])
-    vq_encode(dev(c["values"]), dev(c["v_codebook"]), c["dv"], transform=False, codes=vbuf,
+    vq_encode(dev(c["values"]), dev(c["v_codebook"]), c["dv"], transform=False, codes=vb2,
               S_off=c["S_off"])
     torch.cuda.synchronize()
     kc, vc = kbuf.cpu().numpy(), vbuf.cpu().numpy()
+    assert np.array_equal(kc, kb2.cpu().numpy()) and np.array_equal(vc, vb2.cpu().numpy())
     lo, hi = c["S_off"], c["S_off"] + c["S_q"]
     assert np.array_equal(kc[:, :, :lo], c["k_codes"][:, :, :lo])
+    assert np.array_equal(vc[:, :, :lo], c["v_codes"][:, :, :lo])
     assert np.all(kc[:, :, hi:] == 0) and np.all(vc[:, :, hi:] == 0)
-    rng = np.random.default_rng(5)
-    for b, h in [(0, 0), (3, 7)]:
-        check_codes(c["keys"][b:b + 1, h:h + 1], c["k_codebook"], c["dk"], c["smooth"][h:h + 1],
-                    True, kc[b:b + 1, h:h + 1, lo:hi], f"prefill keys b{b} h{h}")
-        check_codes(c["values"][b:b + 1, h:h + 1], c["v_codebook"], c["dv"], None, False,
-                    vc[b:b + 1, h:h + 1, lo:hi], f"prefill values b{b} h{h}")
+    check_codes(c["keys"], c["k_codebook"], c["dk"], c["smooth"], True, kc[:, :, lo:hi],
+                "prefill keys")
+    check_codes(c["values"], c["v_codebook"], c["dv"], None, False, vc[:, :, lo:hi],
+                "prefill values")
+    assert path_of(c) == "tile"
     out = run_attend(c, k_codes=kc, v_codes=vc)
-    rows = [(0, 0), (1, 3), (2, 5), (3, 7)]
-    ref = oracle_attend(c, kc, vc, rows=rows)
-    for b, h in rows:
-        check_attn(out[b, h], ref[b, h], f"prefill b{b} h{h}")
+    check_attn(out, oracle_attend(c, kc, vc), "prefill attend")
+
+
+@pytest.mark.parametrize("family", ["stream", "lut_mfma", "tile"])
+def test_outlier_value_codebooks(family):
+    """Value codebooks sampled from values with x20 outlier channels (entries
+    up to |v| ~ 80) and key codebooks from the transformed outlier keys, with
+    x20-outlier queries, so softmax rows are peaked and large value entries
+    partly cancel: each kernel family's value path (fp16 value rows, fp16
+    weights, fp32 accumulation) against the oracle on every output row."""
+    rng = np.random.default_rng(1200 + len(family))
+    D, dk, dv = 128, 8, 4
+    if family == "stream":
+        B, Hq, Hkv, Sq, S_cap, lens = 4, 32, 8, 1, 8192, [8192, 5000, 77, 8100]
+    elif family == "lut_mfma":
+        B, Hq, Hkv, Sq, S_cap, lens = 3, 8, 2, 2, 2000, [2000, 900, 33]
+    else:
+        B, Hq, Hkv, Sq, S_cap, lens = 2, 4, 2, 100, 600, [600, 250]
+    keys = synth.outlier_normal(rng, (1, Hkv, 4096, D), 4)
+    vals = synth.outlier_normal(rng, (1, Hkv, 4096, D), 4)
+    s = synth.smooth_factors(keys)
+    Ck = synth.sample_rows(rng, O.forward_transform(keys, s, True).reshape(-1, dk), 256)
+    Cv = synth.sample_rows(rng, vals.astype(np.float64).reshape(-1, dv), 256)
+    assert np.abs(Cv).max() > 20                # rows holding x20 outlier entries
+    c = dict(B=B, H_q=Hq, H_kv=Hkv, S_q=Sq, D=D, dk=dk, dv=dv,
+             q=synth.outlier_normal(rng, (B, Hq, Sq, D), 4),
+             k_codes=synth.uniform_codes(rng, (B, Hkv, S_cap, D // dk)),
+             v_codes=synth.uniform_codes(rng, (B, Hkv, S_cap, D // dv)),
+             k_codebook=Ck, v_codebook=Cv, smooth=s, kv_lens=np.array(lens, np.int32),
+             scale=1 / math.sqrt(D), causal=True, window=0)
+    assert path_of(c) == family
+    out = run_attend(c)
+    ref = oracle_attend(c, c["k_codes"], c["v_codes"])
+    check_attn(out, ref, f"outlier value codebooks ({family}), max |ref| {np.abs(ref).max():.1f}")
 
 
 # ----------------------------------------------------------------------------
