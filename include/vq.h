@@ -238,6 +238,37 @@ int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D,
               float scale, int causal, int sliding_window,
               void* out_f16, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the per-GPU device scratch array used by vq_attend_noalloc. */
+#define VQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * vq_attend for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, result and errors as vq_attend, without the workspace: the
+ * split partials live in a file-scope device array of
+ * VQ_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); its first call on a device looks
+ * up that device's array address once.  The stream must belong to the
+ * current device.
+ *
+ * Shapes whose vq_attend_workspace_bytes(...) exceeds
+ * VQ_NOALLOC_SCRATCH_BYTES are rejected with VQ_ERR_WORKSPACE (every decode
+ * shape with S_q * H_q / H_kv < 64 query rows per kv head fits; a prefill
+ * chunk such as 4 x 8 heads x 512 queries does not).  Every call on a GPU
+ * shares that GPU's array: calls that may overlap on one GPU (concurrent
+ * streams, or host threads) race and give undefined results; serialize them,
+ * or use vq_attend with distinct workspaces.  The array's contents on entry
+ * are ignored (nothing needs clearing).
+ */
+int vq_attend_noalloc(const void* q_f16, int B, int H_q, int S_q, int D,
+                      const uint8_t* k_codes, const float* k_codebook, int k_sub_dim,
+                      const float* smooth, int smooth_rows, int transform,
+                      const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
+                      int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens,
+                      float scale, int causal, int sliding_window,
+                      void* out_f16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

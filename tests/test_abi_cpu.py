@@ -266,3 +266,18 @@ def test_binding_rejects_wrong_shapes(lib):
         api.vq_attend(q, kc, cb, kc, cb, kv_lens=torch.zeros(2, dtype=i32),
                       out=torch.zeros(2, 8, 1, 64, dtype=f16), workspace=torch.zeros(16, dtype=u8),
                       smooth=torch.zeros(4, 64), **att_kw)
+
+
+def test_attend_noalloc_validation(lib):
+    """vq_attend_noalloc validates like vq_attend, and rejects shapes whose
+    partials exceed its device scratch array before touching a device."""
+    f = lib.vq_attend_noalloc
+    args = lambda B=2, Hq=8, Sq=1, q=P: (q, B, Hq, Sq, 128, P, P, 8, P, 2, 1, P, P, 4, 256, 2, 64,
+                                         None, 0.1, 1, 0, P, None)
+    assert f(*args(q=None)) == INVALID
+    assert f(*args(Hq=7)) == INVALID                     # H_q % H_kv
+    assert f(*args(B=0)) == OK
+    st = f(P, 4, 8, 512, 128, P, P, 8, P, 8, 1, P, P, 4, 256, 8, 32768, None, 0.1, 1, 0, P, None)
+    assert st == WORKSPACE and b"scratch" in lib.vq_last_error()
+    if not torch.cuda.is_available():
+        assert f(*args()) == NO_DEVICE

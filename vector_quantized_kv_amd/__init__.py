@@ -3,7 +3,7 @@
 The compute runs in libvq.so (hand-written HIP kernels for gfx950) behind the
 C ABI declared in include/vq.h; this package only marshals torch tensors to it.
 """
-from .api import (VQError, attend_workspace, vq_attend, vq_attend_path,  # noqa: F401
+from .api import (VQError, attend_workspace, vq_attend, vq_attend_noalloc, vq_attend_path,  # noqa: F401
                   vq_attend_workspace_bytes, vq_decode, vq_encode, vq_encode_decode,
                   vq_encode_kv,
                   vq_supports_shape)

@@ -280,3 +280,21 @@ def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None
                  _ptr(kv_lens), float(scale), int(bool(causal)), int(sliding_window), _ptr(out),
                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
                  prepare=prepare, result=out)
+
+
+def vq_attend_noalloc(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None,
+                      transform=True, kv_lens=None, causal=True, sliding_window=0, out=None,
+                      stream=None, prepare=False):
+    """vq_attend with the split partials in the library's per-GPU device
+    scratch array instead of a workspace (no device allocation when `out` is
+    given).  Calls that overlap on one GPU race; shapes needing more than
+    VQ_NOALLOC_SCRATCH_BYTES of partials raise VQError."""
+    B, Hq, Sq, D, dk, dv, Hkv, S_cap, sm, rows, out = _attend_args(
+        q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out)
+    _on_device(q=q, k_codes=k_codes, k_codebook=k_codebook, v_codes=v_codes,
+               v_codebook=v_codebook, kv_lens=kv_lens, out=out, smooth=sm)
+    return _call("vq_attend_noalloc", _ptr(q), B, Hq, Sq, D, _ptr(k_codes), _ptr(k_codebook),
+                 dk, _ptr(sm), rows, int(bool(transform)), _ptr(v_codes),
+                 _ptr(v_codebook), dv, k_codebook.shape[0], Hkv, S_cap,
+                 _ptr(kv_lens), float(scale), int(bool(causal)), int(sliding_window), _ptr(out),
+                 _stream(stream), prepare=prepare, result=out)

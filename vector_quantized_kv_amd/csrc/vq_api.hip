@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -137,6 +138,104 @@ int run_encode(const char* what, const void* keys, const uint8_t* codes_in, int 
     for (int b = 0; b < B; ++b) offs.v[b] = row_offsets[b];
   return hip_status(what, launch_encode(a, row_offsets ? &offs : nullptr, mode,
                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
+// Device scratch of vq_attend_noalloc: the split partials of the attention
+// kernels live here instead of in a caller's workspace.  Every GPU the
+// library runs on holds its own copy until the process ends.
+static __device__ __align__(256) unsigned char scratch[VQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device.  In host code the
+// array's name is only a stand-in; the address is looked up once per device
+// (with that device current) and kept.
+int scratch_address(const char* what, void** out) {
+  static std::once_flag once[kMaxDevices];
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::atomic<int> err[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(what, e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VQ_ERR_UNSUPPORTED, "%s: device index %d is beyond %d", what, dev, kMaxDevices);
+  std::call_once(once[dev], [dev] {
+    void* ptr = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    err[dev].store((int)r, std::memory_order_relaxed);
+    addr[dev].store(r == hipSuccess ? ptr : nullptr, std::memory_order_release);
+  });
+  void* ptr = addr[dev].load(std::memory_order_acquire);
+  if (!ptr)
+    return fail(VQ_ERR_HIP, "%s: the scratch array's device address is unavailable (HIP error %d)", what,
+                err[dev].load(std::memory_order_relaxed));
+  *out = ptr;
+  return VQ_OK;
+}
+
+// vq_attend and vq_attend_noalloc: the workspace is the caller's buffer, or
+// (workspace == nullptr and noalloc) the device's scratch array.
+int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, int D,
+                const uint8_t* k_codes, const float* k_codebook, int k_sub_dim, const float* smooth,
+                int smooth_rows, int transform, const uint8_t* v_codes, const float* v_codebook,
+                int v_sub_dim, int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens,
+                float scale, int causal, int sliding_window, void* out_f16, void* workspace,
+                size_t workspace_bytes, bool noalloc, void* stream) {
+  if (B < 0 || S_q < 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0 and S_q >= 0 (got %d, %d)", what, B, S_q);
+  if (H_q <= 0 || H_kv <= 0 || S_cap <= 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need H_q, H_kv, S_cap > 0 (got %d, %d, %d)", what, H_q, H_kv,
+                S_cap);
+  if (!q_f16 || !k_codes || !k_codebook || !v_codes || !v_codebook || !out_f16)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: q, codes, codebooks and out must be non-null", what);
+  if (H_q % H_kv != 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: H_q (%d) is not a multiple of H_kv (%d)", what, H_q, H_kv);
+  int st = check_quantizer(what, D, n_centroids, k_sub_dim);
+  if (st) return st;
+  if ((st = check_quantizer(what, D, n_centroids, v_sub_dim))) return st;
+  if ((D / k_sub_dim) % 4 != 0 || (D / v_sub_dim) % 4 != 0)
+    return fail(VQ_ERR_UNSUPPORTED, "%s: the number of key and value sub-vectors must be multiples of 4", what);
+  if ((st = check_smooth(what, smooth, smooth_rows, H_kv))) return st;
+  if ((st = check_transform(what, transform, D))) return st;
+  if (causal != 0 && causal != 1)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1 (got %d)", what, causal);
+  if (sliding_window < 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: sliding_window must be >= 0 (got %d)", what, sliding_window);
+  if (!std::isfinite(scale)) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: scale must be finite", what);
+  if ((st = check_aligned(what, {q_f16, k_codes, k_codebook, smooth, v_codes, v_codebook, kv_lens,
+                                 out_f16, workspace})))
+    return st;
+  if (B == 0 || S_q == 0) return VQ_OK;
+  AttendPlan plan;
+  if (!plan_attend(B, H_q, S_q, D, H_kv, S_cap, sliding_window, &plan))
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: no launch plan for this shape", what);
+  size_t lds = 0;
+  if (!attend_pick_rows(plan.rows, D / k_sub_dim, n_centroids, v_sub_dim, D / v_sub_dim, D, &lds))
+    return fail(VQ_ERR_UNSUPPORTED, "%s: the query LUT does not fit in LDS for this shape", what);
+  if (noalloc) {
+    if (plan.workspace_bytes > (size_t)VQ_NOALLOC_SCRATCH_BYTES)
+      return fail(VQ_ERR_WORKSPACE,
+                  "%s: this shape needs %zu bytes of scratch, above the %zu-byte device array; "
+                  "call vq_attend with a workspace instead",
+                  what, plan.workspace_bytes, (size_t)VQ_NOALLOC_SCRATCH_BYTES);
+  } else if (!workspace || workspace_bytes < plan.workspace_bytes) {
+    return fail(VQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", what, plan.workspace_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  }
+  if ((st = check_device(what))) return st;
+  if (noalloc && (st = scratch_address(what, &workspace))) return st;
+  AttendArgs a{};
+  a.q = reinterpret_cast<const __half*>(q_f16);
+  a.k_codes = k_codes; a.k_codebook = k_codebook; a.smooth = smooth;
+  a.v_codes = v_codes; a.v_codebook = v_codebook; a.kv_lens = kv_lens;
+  a.out = reinterpret_cast<__half*>(out_f16);
+  a.partials = reinterpret_cast<float*>(workspace);
+  a.B = B; a.Hq = H_q; a.Sq = S_q; a.D = D; a.Hkv = H_kv; a.S_cap = S_cap;
+  a.dk = k_sub_dim; a.dv = v_sub_dim; a.n_c = n_centroids;
+  a.smooth_rows = smooth_rows; a.transform = transform;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  a.causal = causal; a.window = sliding_window;
+  return hip_status(what, launch_attend(a, plan, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -309,54 +408,21 @@ int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* 
               int causal, int sliding_window, void* out_f16, void* workspace,
               size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
-  const char* what = "vq_attend";
-  if (B < 0 || S_q < 0)
-    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0 and S_q >= 0 (got %d, %d)", what, B, S_q);
-  if (H_q <= 0 || H_kv <= 0 || S_cap <= 0)
-    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need H_q, H_kv, S_cap > 0 (got %d, %d, %d)", what, H_q, H_kv,
-                S_cap);
-  if (!q_f16 || !k_codes || !k_codebook || !v_codes || !v_codebook || !out_f16)
-    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: q, codes, codebooks and out must be non-null", what);
-  if (H_q % H_kv != 0)
-    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: H_q (%d) is not a multiple of H_kv (%d)", what, H_q, H_kv);
-  int st = check_quantizer("vq_attend (keys)", D, n_centroids, k_sub_dim);
-  if (st) return st;
-  if ((st = check_quantizer("vq_attend (values)", D, n_centroids, v_sub_dim))) return st;
-  if ((D / k_sub_dim) % 4 != 0 || (D / v_sub_dim) % 4 != 0)
-    return fail(VQ_ERR_UNSUPPORTED, "%s: the number of key and value sub-vectors must be multiples of 4", what);
-  if ((st = check_smooth(what, smooth, smooth_rows, H_kv))) return st;
-  if ((st = check_transform(what, transform, D))) return st;
-  if (causal != 0 && causal != 1)
-    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1 (got %d)", what, causal);
-  if (sliding_window < 0)
-    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: sliding_window must be >= 0 (got %d)", what, sliding_window);
-  if (!std::isfinite(scale)) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: scale must be finite", what);
-  if ((st = check_aligned(what, {q_f16, k_codes, k_codebook, smooth, v_codes, v_codebook, kv_lens,
-                                 out_f16, workspace})))
-    return st;
-  if (B == 0 || S_q == 0) return VQ_OK;
-  AttendPlan plan;
-  if (!plan_attend(B, H_q, S_q, D, H_kv, S_cap, sliding_window, &plan))
-    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: no launch plan for this shape", what);
-  size_t lds = 0;
-  if (!attend_pick_rows(plan.rows, D / k_sub_dim, n_centroids, v_sub_dim, D / v_sub_dim, D, &lds))
-    return fail(VQ_ERR_UNSUPPORTED, "%s: the query LUT does not fit in LDS for this shape", what);
-  if (!workspace || workspace_bytes < plan.workspace_bytes)
-    return fail(VQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", what, plan.workspace_bytes,
-                workspace ? workspace_bytes : (size_t)0);
-  if ((st = check_device(what))) return st;
-  AttendArgs a{};
-  a.q = reinterpret_cast<const __half*>(q_f16);
-  a.k_codes = k_codes; a.k_codebook = k_codebook; a.smooth = smooth;
-  a.v_codes = v_codes; a.v_codebook = v_codebook; a.kv_lens = kv_lens;
-  a.out = reinterpret_cast<__half*>(out_f16);
-  a.partials = reinterpret_cast<float*>(workspace);
-  a.B = B; a.Hq = H_q; a.Sq = S_q; a.D = D; a.Hkv = H_kv; a.S_cap = S_cap;
-  a.dk = k_sub_dim; a.dv = v_sub_dim; a.n_c = n_centroids;
-  a.smooth_rows = smooth_rows; a.transform = transform;
-  a.scale_log2e = scale * 1.4426950408889634f;
-  a.causal = causal; a.window = sliding_window;
-  return hip_status(what, launch_attend(a, plan, reinterpret_cast<hipStream_t>(stream)));
+  return attend_impl("vq_attend", q_f16, B, H_q, S_q, D, k_codes, k_codebook, k_sub_dim, smooth,
+                     smooth_rows, transform, v_codes, v_codebook, v_sub_dim, n_centroids, H_kv, S_cap,
+                     kv_lens, scale, causal, sliding_window, out_f16, workspace, workspace_bytes,
+                     false, stream);
+}
+
+int vq_attend_noalloc(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* k_codes,
+                      const float* k_codebook, int k_sub_dim, const float* smooth, int smooth_rows,
+                      int transform, const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
+                      int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens, float scale,
+                      int causal, int sliding_window, void* out_f16, void* stream) {
+  g_last_error[0] = 0;
+  return attend_impl("vq_attend_noalloc", q_f16, B, H_q, S_q, D, k_codes, k_codebook, k_sub_dim,
+                     smooth, smooth_rows, transform, v_codes, v_codebook, v_sub_dim, n_centroids, H_kv,
+                     S_cap, kv_lens, scale, causal, sliding_window, out_f16, nullptr, 0, true, stream);
 }
 
 }  // extern "C"
