@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused PVQ decode-attn µs/step & HBM GB/s; key encode Mtokens/s"
 HBM_PEAK_GBS = 8000.0
-FP32_VALU_PEAK_TFLOPS = 157.3
+FP16_MFMA_PEAK_TFLOPS = 2500.0
 MIB = 1 << 20
 COPY_BYTES = 1 << 30
 ATTEND_SOURCES = ("vq_attend.hip", "vq_attend_mfma.hip", "vq_attend_stream.hip", "vq_attend_tile.hip",
@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--mode", choices=["full", "attend", "encode", "encode_workload", "copy"],
                     default="full",
                     help="attend/encode: only launch that entry point of the main workload "
@@ -120,6 +120,137 @@ def time_events(fn, reps, torch, warm=3):
     ev[1].record()
     torch.cuda.synchronize()
     return ev[0].elapsed_time(ev[1]) * 1e3 / reps          # microseconds
+
+
+def host_cpu_info():
+    """Core count, CPU model and the BLAS thread count of this process."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "model": model, "blas_threads": blas}
+
+
+def cpu_baseline(args, c, k_new, v_new, lens):
+    """The oracle (plain fp64 numpy, unchanged) timed on the host cores on a
+    bounded sample of each workload; every entry says what it timed and how
+    it was scaled.  numpy's elementwise work runs on one core and its BLAS
+    calls on blas_threads cores.  A reported baseline only."""
+    import numpy as np
+    import oracle.vq_oracle as O
+    from vector_quantized_kv_amd import synth
+
+    info = host_cpu_info()
+    budget = args.cpu_seconds
+    tr = lambda k, s: O.forward_transform(k, s, True)
+    ops = {}
+
+    def timed(fn, reps_budget):
+        """Run fn() until reps_budget seconds are spent (at least once);
+        return (seconds per call, calls)."""
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            fn()
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= reps_budget:
+                return dt / n, n
+
+    # c4, W = 0: the decode step of the main workload, batch rows cycled
+    B, Hkv, Hq, D = c["B"], c["H_kv"], c["H_q"], c["D"]
+    state = {"b": 0}
+
+    def step_row():
+        b = state["b"] % B
+        state["b"] += 1
+        O.encode(k_new[b:b + 1], c["k_codebook"], c["dk"], c["smooth"], True)
+        O.encode(v_new[b:b + 1], c["v_codebook"], c["dv"])
+        O.attend(c["q"][b:b + 1], c["k_codes"][b:b + 1], c["k_codebook"], c["v_codes"][b:b + 1],
+                 c["v_codebook"], scale=c["scale"], causal=True, smooth=c["smooth"], transform=True,
+                 kv_lens=lens[b:b + 1])
+        return int(lens[b]) * Hkv * 48 + Hq * D * 4 + 2 * Hkv * D * 2
+
+    t0 = time.perf_counter()
+    done, rows = 0, 0
+    while rows < 8 * B:
+        done += step_row()
+        rows += 1
+        if time.perf_counter() - t0 >= 0.4 * budget:
+            break
+    t_main = time.perf_counter() - t0
+    main_gbps = done / t_main / 1e9
+    ops["gqa_long_W0_step"] = {
+        "GBps": round(main_gbps, 4), "us_per_step": round(t_main / rows * B * 1e6, 0),
+        "sample": f"{rows} batch-row passes (rows cycled; encode of the row's new K/V token and "
+                  f"fp64 attention of its 32 query heads) in {t_main:.1f} s; per step = per row x {B}"}
+
+    # c4, W = 4096: one batch row, x B
+    cw = dict(c, window=4096)
+    sec, n = timed(lambda: O.attend(cw["q"][:1], cw["k_codes"][:1], cw["k_codebook"], cw["v_codes"][:1],
+                                    cw["v_codebook"], scale=cw["scale"], causal=True, sliding_window=4096,
+                                    smooth=cw["smooth"], transform=True, kv_lens=lens[:1]),
+                   0.1 * budget)
+    ops["gqa_long_W4096_attend"] = {
+        "us": round(sec * B * 1e6, 0), "GBps": round(B * Hkv * 4096 * 48 / (sec * B) / 1e9, 4),
+        "sample": f"batch row 0 attended {n} times, {sec * 1e3:.1f} ms each; per call = per row x {B}"}
+
+    # c3: single-query decode at each length, whole call
+    for S in (512, 2048, 8192):
+        d = synth.decode(S)
+        sec, n = timed(lambda: O.attend(d["q"], d["k_codes"], d["k_codebook"], d["v_codes"],
+                                        d["v_codebook"], scale=d["scale"], causal=True,
+                                        smooth=d["smooth"], transform=True), 0.05 * budget)
+        ops[f"decode_S{S}_attend"] = {"us": round(sec * 1e6, 0),
+                                      "GBps": round(8 * S * 48 / sec / 1e9, 4),
+                                      "sample": f"whole call, {n} runs"}
+
+    # c2: key encode + reconstruction, on 512 tokens of every head, scaled to the 8192
+    e = synth.encode(tr)
+    sub = np.ascontiguousarray(e["keys"][:, :, :512])
+    sec, n = timed(lambda: O.encode_decode(sub, e["k_codebook"], e["dk"], e["smooth"], True),
+                   0.15 * budget)
+    ops["encode_decode_1x8x8192x128"] = {
+        "us": round(sec * 16 * 1e6, 0), "Mtok_s": round(512 / sec / 1e6, 6),
+        "sample": f"tokens 0..511 of the 8 heads, {n} runs of {sec:.2f} s; per call = x 16"}
+
+    # c5: encode of the 512 new K and V tokens plus the S_q = 512 attention, batch row 0, x B
+    pf = synth.prefill(tr)
+    b0 = lambda a: np.ascontiguousarray(a[:1])
+
+    def prefill_row():
+        kc, _ = O.encode(b0(pf["keys"]), pf["k_codebook"], pf["dk"], pf["smooth"], True)
+        vc, _ = O.encode(b0(pf["values"]), pf["v_codebook"], pf["dv"])
+        K, V = b0(pf["k_codes"]), b0(pf["v_codes"])
+        K[:, :, pf["S_off"]:pf["S_off"] + 512] = kc
+        V[:, :, pf["S_off"]:pf["S_off"] + 512] = vc
+        O.attend(b0(pf["q"]), K, pf["k_codebook"], V, pf["v_codebook"], scale=pf["scale"],
+                 causal=True, smooth=pf["smooth"], transform=True, kv_lens=pf["kv_lens"][:1])
+
+    sec, n = timed(prefill_row, 0.2 * budget)
+    ops["prefill_append_attend"] = {
+        "us": round(sec * pf["B"] * 1e6, 0),
+        "sample": f"batch row 0 of 4 (encode of its 512 new K and V tokens, then the 512-query "
+                  f"attention over 16896 keys), {n} runs of {sec:.2f} s; per call = per row x 4"}
+
+    return {
+        "value": round(main_gbps, 4), "unit": "GB/s", "cores": info["blas_threads"] or 1,
+        "kind": "oracle",
+        "sample": ops["gqa_long_W0_step"]["sample"],
+        "threads": f"1 core elementwise / {info['blas_threads']} cores BLAS",
+        "host": info,
+        "ops": ops,
+    }
 
 
 def main():
@@ -291,7 +422,12 @@ def main():
         f_e = vq_encode(ke, Ce, 8, smooth=se, codes=codes_e, prepare=True)
         us_ed = time_events(lambda i: f_ed(), 50, torch)
         us_e = time_events(lambda i: f_e(), 50, torch)
-        flops = 65536 * 16 * 256 * 8 * 2
+        flops = 65536 * 16 * 256 * 8 * 2          # distance products, 2 per multiply-add
+        # the argmin floor on the vector ALUs: one compare and two selects per
+        # (sub-vector, centroid) candidate, 64 candidates per wave instruction,
+        # one wave instruction per 4 clocks on each of 1024 SIMDs at 2.4 GHz
+        cands = 65536 * 16 * 256
+        argmin_floor_us = cands * 3 / 64 * 4 / (1024 * 2.4e9) * 1e6
         extra["key_encode"] = {
             "shape": "[1,8,8192,128] fp16, d_k=8, 256 centroids, smooth+WHT",
             "encode_decode_us": round(us_ed, 2), "encode_only_us": round(us_e, 2),
@@ -299,7 +435,12 @@ def main():
             "encode_only_Mtok_s": round(8192 / us_e, 3),
             "encode_decode_GBps": round(34603008 / us_ed / 1e3, 1),
             "distance_TFLOPs": round(flops / us_e / 1e6, 2),
-            "alu_frac_of_157TF": round(flops / us_e / 1e6 / FP32_VALU_PEAK_TFLOPS, 4),
+            # the distance products run on fp16 matrix cores (three split passes)
+            "mfma_frac_algorithmic": round(flops / us_e / 1e6 / FP16_MFMA_PEAK_TFLOPS, 4),
+            "mfma_frac_executed": round(3 * flops / us_e / 1e6 / FP16_MFMA_PEAK_TFLOPS, 4),
+            "hbm_frac_encode_only": round(17825792 / us_e / 1e3 / HBM_PEAK_GBS, 4),
+            "argmin_floor_us": round(argmin_floor_us, 2),
+            "frac_of_argmin_floor": round(argmin_floor_us / us_e, 4),
         }
         log(f"[bench] encode: {us_ed:.1f} us (enc+dec), {us_e:.1f} us (enc)")
 
@@ -361,40 +502,11 @@ def main():
         result["extra"] = extra
 
     # ------------------------------------------------------------------
-    # CPU baseline: the oracle on a bounded sample of the main workload
+    # CPU baseline: the oracle, timed on bounded samples of every workload
     # ------------------------------------------------------------------
     if not args.no_cpu_baseline:
-        import oracle.vq_oracle as O
-        try:
-            from threadpoolctl import threadpool_info
-            blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:
-            blas = os.cpu_count()
-        kcodes, vcodes = c["k_codes"], c["v_codes"]
-        done_bytes, t_cpu, rows = 0, 0.0, 0
-        t0 = time.perf_counter()
-        # cycle over the batch rows (at most 8 passes) until the time budget is spent
-        for b in [b for _ in range(8) for b in range(B)]:
-            qb = c["q"][b:b + 1]
-            O.encode(k_new[b:b + 1], c["k_codebook"], dk, c["smooth"], True)
-            O.encode(v_new[b:b + 1], c["v_codebook"], dv)
-            O.attend(qb, kcodes[b:b + 1], c["k_codebook"], vcodes[b:b + 1], c["v_codebook"],
-                     scale=c["scale"], causal=True, smooth=c["smooth"], transform=True,
-                     kv_lens=lens[b:b + 1])
-            rows += 1
-            done_bytes += int(lens[b]) * Hkv * 48 + Hq * D * 4 + 2 * Hkv * D * 2
-            t_cpu = time.perf_counter() - t0
-            if t_cpu >= args.cpu_seconds:
-                break
-        cpu_gbps = done_bytes / t_cpu / 1e9
-        result["cpu_baseline"] = {
-            "value": round(cpu_gbps, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"{rows} batch-row passes (of {B} rows, cycled) of the decode step (encode of the new K/V token "
-                      f"and fp64 attention over all 32 query heads), {t_cpu:.1f} s; numpy "
-                      f"elementwise work on 1 core, BLAS on {blas} threads",
-            "us_per_step_extrapolated": round(t_cpu / rows * B * 1e6, 0),
-        }
-        log(f"[bench] cpu oracle: {cpu_gbps:.4f} GB/s over {rows} rows in {t_cpu:.1f} s")
+        result["cpu_baseline"] = cpu_baseline(args, c, k_new, v_new, lens)
+        log(f"[bench] cpu oracle: {result['cpu_baseline']['value']:.4f} GB/s on the decode step")
 
     print(json.dumps(result), flush=True)
 

@@ -15,7 +15,7 @@
 // end to end into one token space of T = sum of unit lengths, and each
 // persistent workgroup takes one equal chunk of it (at least 512 keys), so
 // ragged lengths and masks cost no imbalance.  The unit prefix is computed
-// on the device from kv_lens by every workgroup.  The workgroup walks its
+// on the device from kv_lens by wave 0 of every workgroup, with wave scans.  The workgroup walks its
 // chunk one unit segment at a time: it builds the unit's score table in
 // LDS, its 8 waves claim the segment's 64-key blocks from an LDS counter,
 // and the waves' partials (m, l, acc) are combined in LDS into slot c + u
@@ -72,18 +72,14 @@ constexpr int kMaxUnits = 1791;        // units whose prefix fits in LDS (and B 
 constexpr uint32_t kLens = kScan + 64;  // int lens[B], clamped to [0, S_cap]
 constexpr uint32_t kPrefix = kLens + 4 * (kMaxUnits + 1);  // int prefix[U + 1]
 constexpr float kLazyMargin = 8.f;
-constexpr int kUnitsPerThread = (kMaxUnits + kThreads) / kThreads;
 constexpr int kMaxChunks = 4096;       // partial slots reserved for chunks (>= workgroups)
-constexpr int kQExp = kW + 4;          // int slots: exponents of the two query buffers
-static_assert(kUnitsPerThread * kThreads >= kMaxUnits + 1, "prefix coverage");
+// int slots of the scan area: 0..3 the chunk plan, kW the block-claim
+// counter, kQExp and kQExp + 1 the exponents of the two query buffers
+constexpr int kQExp = kW + 4;
 constexpr int kMaxGrid = 256;          // persistent workgroups (one per CU)
-constexpr uint32_t kInside = kPrefix + 4 * (kMaxUnits + 1);  // int [kMaxGrid]
-constexpr uint32_t kWaveMax = kInside + 4 * kMaxGrid;          // float [kW]
+constexpr uint32_t kWaveMax = kPrefix + 4 * (kMaxUnits + 1);  // float [kW]
 constexpr uint32_t kLdsBytes = kWaveMax + 4 * kW;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-// Keys charged for a unit starting inside a chunk (its table build and
-// partial combine, about 2 us of a workgroup's streaming time).
-constexpr int kSegCost = 768;
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -308,21 +304,76 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   };
   auto make_query = [&](int uq, int qbuf) { query_finish(query_load(uq), uq, qbuf); };
 
-  // ---- global reads first: codebooks and kv lengths, then LDS tables -----
+  // ---- kernel entry --------------------------------------------------------
+  // Every thread loads its share of the two codebooks.  Wave 0 alone plans
+  // the chunk, with no barrier and no LDS atomics on the way: the kv lengths
+  // (clamped) go to LDS, the unit prefix is a DPP scan over rounds of 64
+  // units, the chunk is the equal share [c C0, (c + 1) C0) of the T keys,
+  // and the unit holding its first key is found by a ballot.  That unit's
+  // query rows are requested at once, so they arrive while the tables are
+  // written.  (A wave's LDS accesses execute in issue order, so its reads of
+  // lens and pre see its own writes.)
+  float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), vq = kq;
+  if ((tid >> 1) < p.n_c) {
+    kq = reinterpret_cast<const float4*>(k_codebook)[tid];
+    vq = reinterpret_cast<const float4*>(v_codebook)[tid >> 1];
+  }
+  int* const lens_w = reinterpret_cast<int*>(lds + kLens);
+  int* const pre = reinterpret_cast<int*>(lds + kPrefix);
+  int* const plan = scan;  // T, start, end, first unit (ints 0..3 of the scan area)
+  const int c = blockIdx.x;
+  const int G = gridDim.x;
+  QueryRaw qraw;
+  if (wave == 0) {
+    for (int b = lane; b < p.B; b += 64) {
+      const int lv = kv_lens ? kv_lens[b] : p.S_cap;
+      lens_w[b] = lv < 0 ? 0 : (lv > p.S_cap ? p.S_cap : lv);
+    }
+    lds_order();
+    int carry = 0;
+    for (int base = 0; base < p.U; base += 64) {
+      const int uu = base + lane;
+      const int n = uu < p.U ? unit_len(p, lens_w, uu) : 0;
+      const int incl = wave_scan_int(n);
+      if (uu < p.U) pre[uu] = carry + incl - n;
+      if (c == 0 && uu < p.U && n == 0) {
+        header[2 * uu] = 0;       // an empty unit has no partials
+        header[2 * uu + 1] = -1;
+      }
+      carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+    const int Tw = carry;         // T <= U * S_cap < 2^30 is checked on the host
+    const int C0 = max(p.cmin, (Tw + G - 1) / G);
+    const int st = c * C0 < Tw ? c * C0 : Tw;
+    const int en = min(Tw, st + C0);
+    if (lane == 0) pre[p.U] = Tw;
+    lds_order();
+    // the nonempty unit holding position st
+    int uf = 0;
+    if (st < Tw) {
+      for (int base = 0; base < p.U; base += 64) {
+        const int uu = base + lane;
+        bool hit = false;
+        if (uu < p.U) {
+          const int a0 = pre[uu], a1 = pre[uu + 1];
+          hit = a0 < a1 && a0 <= st && st < a1;
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+        if (m) {
+          uf = base + (int)__builtin_ctzll(m);
+          break;
+        }
+      }
+      qraw = query_load(uf);
+    }
+    if (lane == 0) {
+      plan[0] = Tw;
+      plan[1] = st;
+      plan[2] = en;
+      plan[3] = uf;
+    }
+  }
   {
-    // key codebook: one float4 per thread; value codebook: two threads per
-    // code, each writing 16 of its 32 replicas
-    float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), vq = kq;
-    if ((tid >> 1) < p.n_c) {
-      kq = reinterpret_cast<const float4*>(k_codebook)[tid];
-      vq = reinterpret_cast<const float4*>(v_codebook)[tid >> 1];
-    }
-    int lv[kUnitsPerThread];
-#pragma unroll
-    for (int k = 0; k < kUnitsPerThread; ++k) {
-      const int b = tid + kThreads * k;
-      lv[k] = b < p.B ? (kv_lens ? kv_lens[b] : p.S_cap) : 0;
-    }
     *reinterpret_cast<float4*>(lds + kCbk + 16 * tid) = kq;
     // per-wave maximum magnitude of the key codebook
     const float kmx = wave_max_u(fmaxf(fmaxf(fabsf(kq.x), fabsf(kq.y)), fmaxf(fabsf(kq.z), fabsf(kq.w))));
@@ -334,15 +385,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       *reinterpret_cast<uint4*>(lds + kValTab + code * 256 + (tid & 1) * 128 + 16 * ((i + code) & 7)) = two;
-    int* lens = reinterpret_cast<int*>(lds + kLens);
-#pragma unroll
-    for (int k = 0; k < kUnitsPerThread; ++k) {
-      const int b = tid + kThreads * k;
-      if (b < p.B) lens[b] = lv[k] < 0 ? 0 : (lv[k] > p.S_cap ? p.S_cap : lv[k]);
-    }
   }
   __syncthreads();
-  const int* const lens = reinterpret_cast<const int*>(lds + kLens);
+  const int* const lens = lens_w;
   // magnitude exponent of the key codebook
   int ecb;
   {
@@ -352,101 +397,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     for (int w = 0; w < kW; ++w) mx = fmaxf(mx, wm[w]);
     ecb = mag_exp(mx);
   }
-
-  // ---- unit prefix (exclusive) over the U <= kMaxUnits units, the chunk
-  // boundaries, and the unit holding the chunk's first key -----------------
-  // Chunks start as equal shares C0 of T.  A unit that starts strictly
-  // inside a chunk costs that chunk an extra table build and combine, so
-  // each such start moves kSegCost keys of the chunk to the others:
-  //   B_k = k C0 - kSegCost E_k + floor(kSegCost N k / G),
-  // E_k = the (capped) number of inside starts in chunks < k, N = E_G, so
-  // B_0 = 0, B_G = G C0 >= T, and B is increasing.
-  int* const pre = reinterpret_cast<int*>(lds + kPrefix);
-  int* const spec_unit = scan + kW + 2;
-  int* const inside = reinterpret_cast<int*>(lds + kInside);  // [G]
-  const int c = blockIdx.x;
-  const int G = gridDim.x;
-  for (int i = tid; i < G; i += kThreads) inside[i] = 0;
-  if (tid == 0) *spec_unit = 0;  // stays 0 when the chunk starts past the end
-  int T, C0, start, end;
-  QueryRaw qraw;
-  {
-    int n[kUnitsPerThread], sum = 0;
-#pragma unroll
-    for (int k = 0; k < kUnitsPerThread; ++k) {
-      const int u = kUnitsPerThread * tid + k;
-      n[k] = u < p.U ? unit_len(p, lens, u) : 0;
-      sum += n[k];
-    }
-    const int incl = wave_scan_int(sum);
-    if (lane == 63) scan[wave] = incl;
-    __syncthreads();
-    int off = 0;
-    T = 0;
-#pragma unroll
-    for (int w = 0; w < kW; ++w) {
-      const int s = scan[w];
-      off += w < wave ? s : 0;
-      T += s;
-    }
-    C0 = max(p.cmin, (T + G - 1) / G);  // T <= U * S_cap < 2^30 is checked on the host
-    const int pu0 = off + incl - sum;
-    int pu = pu0;
-#pragma unroll
-    for (int k = 0; k < kUnitsPerThread; ++k) {
-      const int u = kUnitsPerThread * tid + k;
-      if (u < p.U) pre[u] = pu;
-      if (n[k] > 0 && pu % C0 != 0) atomicAdd(&inside[pu / C0], 1);
-      // the unit holding the first key of the chunk before the correction
-      // below (which moves bounds by at most C0 / 2): wave 0 starts loading
-      // its query rows right after the barrier
-      if (n[k] > 0 && pu <= c * C0 && c * C0 < pu + n[k]) *spec_unit = u;
-      if (blockIdx.x == 0 && u < p.U && n[k] == 0) {
-        header[2 * u] = 0;       // an empty unit has no partials
-        header[2 * u + 1] = -1;
-      }
-      pu += n[k];
-    }
-    if (tid == 0) pre[p.U] = T;
-    __syncthreads();
-    if (wave == 0) qraw = query_load(min(max(*spec_unit, 0), p.U - 1));
-    // every wave derives the chunk's bounds from the inside-start counts
-    // at most C0 / 2 keys move out of a chunk (none when C0 < 2 kSegCost)
-    const int cap = C0 / (2 * kSegCost);
-    int e_lo = 0, e_hi = 0, e_all = 0;
-    for (int i = lane; i < G; i += 64) {
-      const int v = min(inside[i], cap);
-      e_lo += i < c ? v : 0;
-      e_hi += i <= c ? v : 0;
-      e_all += v;
-    }
-    // full-wave sums, read from one lane: wave-uniform values for the
-    // compiler too (the code buffer descriptors derived from them must stay
-    // in scalar registers)
-    e_lo = wave_total_int(e_lo);
-    e_hi = wave_total_int(e_hi);
-    e_all = wave_total_int(e_all);
-    // kSegCost * e_all * (c + 1) <= kSegCost * U * G < 2^31
-    start = c * C0 - kSegCost * e_lo + (int)fast_div((uint32_t)(kSegCost * e_all * c), p.div_grid);
-    end = min(T, (c + 1) * C0 - kSegCost * e_hi +
-                     (int)fast_div((uint32_t)(kSegCost * e_all * (c + 1)), p.div_grid));
-  }
+  const int T = __builtin_amdgcn_readfirstlane(plan[0]);
+  const int start = __builtin_amdgcn_readfirstlane(plan[1]);
+  const int end = __builtin_amdgcn_readfirstlane(plan[2]);
+  int u = __builtin_amdgcn_readfirstlane(plan[3]);
   if (start >= T) return;
-  // the nonempty unit holding position `start`, by a ballot over the prefix
-  int u = 0;
-  for (int base = 0; base < p.U; base += 64) {
-    const int uu = base + lane;
-    bool hit = false;
-    if (uu < p.U) {
-      const int a0 = pre[uu], a1 = pre[uu + 1];
-      hit = a0 < a1 && a0 <= start && start < a1;
-    }
-    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
-    if (m) {
-      u = base + (int)__builtin_ctzll(m);
-      break;
-    }
-  }
 
   // ---- lane constants ------------------------------------------------------
   // Score gathers: at step k = 4 a + b the lane reads sub-vector
@@ -568,12 +523,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       load_codes(blk(nB), kcB, vrB);
     }
 
-    if (!q_ready && wave == 0) {
-      // first segment: use the rows loaded during the setup if they are the
-      // right unit's (the usual case)
-      const int su = __builtin_amdgcn_readfirstlane(*spec_unit);
-      if (su == u) query_finish(qraw, u, qbuf); else make_query(u, qbuf);
-    }
+    // first segment: the rows wave 0 requested during the plan
+    if (!q_ready && wave == 0) query_finish(qraw, u, qbuf);
     if (tid == 0) *claim_ctr = 2 * kW;
     __syncthreads();  // query rows ready; the previous combine has read the table area
     {
@@ -934,7 +885,6 @@ hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds
   const int cus = cached_cu_count();
   if (cus <= 0) return hipErrorInvalidDevice;
   const int grid = cus < kMaxGrid ? cus : kMaxGrid;
-  sp.div_grid = make_fastdiv((uint32_t)grid);
   sp.smooth_rows = a.smooth_rows;
   sp.transform = a.transform;
   sp.causal = a.causal;
