@@ -482,6 +482,28 @@ def main():
         log(f"[bench] gqa W=4096: {us_w:.1f} us")
         del kw, vw, fw
 
+        # the same decode step's attention with 4-bit codes (16-centroid
+        # codebooks, two codes per byte): 24 B per token and kv head
+        c4b = synth.gqa_long(0, code_bits=4)
+        l4 = c4b["kv_lens"].astype(np.int64)
+        b4 = int(l4.sum()) * Hkv * 24
+        n4 = max(2, math.ceil(600 * MIB / b4))
+        k4s = [t(c4b["k_codes"]) for _ in range(n4)]
+        v4s = [t(c4b["v_codes"]) for _ in range(n4)]
+        q4, kl4 = t(c4b["q"]), t(c4b["kv_lens"])
+        Ck4, Cv4, sm4 = t(c4b["k_codebook"]), t(c4b["v_codebook"]), t(c4b["smooth"])
+        ws4 = attend_workspace(q4, k4s[0], 0)
+        f4 = [vq_attend(q4, k4s[j], Ck4, v4s[j], Cv4, scale=c4b["scale"], smooth=sm4, kv_lens=kl4,
+                        out=out, workspace=ws4, code_bits=4, prepare=True) for j in range(n4)]
+        us4 = time_events(lambda i: f4[i % n4](), 200, torch)
+        byt4 = b4 + attn_fixed
+        extra["gqa_long_W0_4bit"] = {"us": round(us4, 2), "bytes": byt4,
+                                     "GBps": round(byt4 / us4 / 1e3, 1), "sets": n4,
+                                     "workload": "as the main decode step's attention, 16 centroids, "
+                                                 "4-bit codes (24 B per token and kv head)"}
+        log(f"[bench] gqa W=0 4-bit codes: {us4:.1f} us")
+        del k4s, v4s, f4
+
         # prefill chunk: append 512 new tokens (K and V) after 16384, attend S_q = 512
         p = synth.prefill()
         kb, vb = t(p["k_codes"]), t(p["v_codes"])

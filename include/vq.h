@@ -12,9 +12,16 @@
  * Conventions shared by every entry point
  *   - All tensors are dense, row-major (last index fastest), device
  *     pointers, unless stated otherwise.  fp16 means IEEE binary16.
- *   - Codes are uint8 (n_centroids <= 256).  A code buffer has shape
- *     [B, H, S_cap, D / sub_dim]: token slot t of (b, h) starts at byte
- *     ((b * H + h) * S_cap + t) * (D / sub_dim).
+ *   - Codes are code_bits = 8 bits wide (one uint8 per sub-vector,
+ *     n_centroids <= 256) or code_bits = 4 (two per byte, n_centroids <= 16:
+ *     sub-vector 2k in the low nibble and 2k + 1 in the high nibble of byte
+ *     k, the packing of rabitq_pack_values on the "Metal Kernels API" page;
+ *     per-token storage (D / sub_dim) * code_bits / 8 bytes, the storage
+ *     formula on the "veloxquant_mlx.cache.vecinfer_cache module" page).  A
+ *     code buffer has shape [B, H, S_cap, row_bytes], row_bytes =
+ *     (D / sub_dim) * code_bits / 8: token slot t of (b, h) starts at byte
+ *     ((b * H + h) * S_cap + t) * row_bytes.  4-bit codes need an even
+ *     number of sub-vectors (a multiple of 8 for vq_attend).
  *   - Sub-vector j of a D-vector covers dims [j * sub_dim, (j+1) * sub_dim).
  *     One codebook [n_centroids, sub_dim] (fp32) serves every sub-vector,
  *     head and batch row.
@@ -101,7 +108,8 @@ int vq_supports_shape(int n_centroids, int n_sub, int head_dim);
  *   codebook    [n_centroids, sub_dim] fp32
  *   smooth      NULL or [smooth_rows, D] fp32 (see conventions)
  *   transform   0 or 1
- *   codes       [B, H, S_cap, D / sub_dim] uint8; token t of row b is
+ *   code_bits   8 or 4 (see conventions)
+ *   codes       [B, H, S_cap, row_bytes] uint8; token t of row b is
  *               written to slot off_b + t, off_b = row_offsets[b] if
  *               row_offsets != NULL else S_off.  Other slots are untouched.
  *   row_offsets NULL or HOST array of B int32 (B <= VQ_MAX_ROW_OFFSETS),
@@ -109,11 +117,13 @@ int vq_supports_shape(int n_centroids, int n_sub, int head_dim);
  * The centroid index minimizes the fp32 squared distance summed over the
  * sub-vector; exact ties resolve to the lowest index.
  * Errors: INVALID_ARGUMENT for null pointers, nonpositive sizes, S_off or
- * offsets out of range, D % sub_dim != 0, smooth_rows not in {1, H};
- * UNSUPPORTED outside the caps.  S = 0 or B = 0 is a no-op returning VQ_OK.
+ * offsets out of range, D % sub_dim != 0, smooth_rows not in {1, H},
+ * code_bits not in {8, 4}, n_centroids > 16 or an odd number of
+ * sub-vectors with 4-bit codes; UNSUPPORTED outside the caps.  S = 0 or
+ * B = 0 is a no-op returning VQ_OK.
  */
 int vq_encode(const void* keys_f16, int B, int H, int S, int D,
-              const float* codebook, int n_centroids, int sub_dim,
+              const float* codebook, int n_centroids, int sub_dim, int code_bits,
               const float* smooth, int smooth_rows, int transform,
               uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets,
               void* stream);
@@ -130,14 +140,16 @@ int vq_encode(const void* keys_f16, int B, int H, int S, int D,
  *   keys_f16, values_f16   [B, H, S, D] fp16
  *   k_codebook [k_n_centroids, k_sub_dim], v_codebook [v_n_centroids,
  *   v_sub_dim] fp32; smooth, smooth_rows, transform as for vq_encode (keys)
- *   k_codes [B, H, S_cap, D / k_sub_dim], v_codes [B, H, S_cap, D / v_sub_dim]
+ *   code_bits 8 or 4, for both halves
+ *   k_codes [B, H, S_cap, row bytes of k_sub_dim], v_codes [B, H, S_cap,
+ *   row bytes of v_sub_dim]
  * Errors: those of vq_encode for either half, checked before anything is
  * enqueued.
  */
 int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int S, int D,
                  const float* k_codebook, int k_n_centroids, int k_sub_dim,
                  const float* smooth, int smooth_rows, int transform,
-                 const float* v_codebook, int v_n_centroids, int v_sub_dim,
+                 const float* v_codebook, int v_n_centroids, int v_sub_dim, int code_bits,
                  uint8_t* k_codes, uint8_t* v_codes, int S_cap, int S_off,
                  const int32_t* row_offsets, void* stream);
 
@@ -146,14 +158,15 @@ int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int
  * Kernels API", "VecInfer kernels", vecinfer_dequant_metal and the last three
  * steps of vecinfer_encode_decode_metal).
  *
- *   codes       [B, H, S_cap, D / sub_dim] uint8; slots [S_off, S_off + S)
- *               are read.  Codes >= n_centroids are undefined behaviour.
+ *   codes       [B, H, S_cap, row_bytes] uint8 of code_bits-wide codes;
+ *               slots [S_off, S_off + S) are read.  Codes >= n_centroids
+ *               are undefined behaviour.
  *   out         [B, H, S, D]; out_dtype 0 = fp32, 1 = fp16 (round to
  *               nearest even).
  * Errors as vq_encode.
  */
 int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
-              const float* codebook, int n_centroids, int sub_dim,
+              const float* codebook, int n_centroids, int sub_dim, int code_bits,
               const float* smooth, int smooth_rows, int transform, int D,
               void* out, int out_dtype, void* stream);
 
@@ -167,7 +180,7 @@ int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
  * Other arguments and errors as vq_encode.
  */
 int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D,
-                     const float* codebook, int n_centroids, int sub_dim,
+                     const float* codebook, int n_centroids, int sub_dim, int code_bits,
                      const float* smooth, int smooth_rows, int transform,
                      uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets,
                      void* recon, int out_dtype, void* stream);
@@ -195,7 +208,7 @@ enum {
  * computes the same attention.  Host-only; needs no device.
  */
 int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
-                   int n_centroids, int H_kv, int S_cap, int sliding_window);
+                   int n_centroids, int code_bits, int H_kv, int S_cap, int sliding_window);
 
 /*
  * Fused attention read directly from key and value codes ("Metal Kernels
@@ -213,11 +226,15 @@ int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
  * A query row with no valid key gets zeros.
  *
  *   q_f16       [B, H_q, S_q, D] fp16 raw queries
- *   k_codes     [B, H_kv, S_cap, D / k_sub_dim] uint8
+ *   k_codes     [B, H_kv, S_cap, row bytes] uint8 (code_bits wide codes)
  *   k_codebook  [n_centroids, k_sub_dim] fp32
  *   smooth      NULL or [smooth_rows, D] fp32 smooth factors of the keys
  *               (smooth_rows 1 or H_kv); transform as for vq_encode
- *   v_codes     [B, H_kv, S_cap, D / v_sub_dim] uint8 (no smooth, no rotation)
+ *   v_codes     [B, H_kv, S_cap, row bytes] uint8 (no smooth, no rotation)
+ *   code_bits   8 or 4, the width of both the key and the value codes; 4-bit
+ *               codes need n_centroids <= 16 and numbers of key and value
+ *               sub-vectors that are multiples of 8.  Codes >= n_centroids
+ *               are undefined behaviour.
  *   v_codebook  [n_centroids, v_sub_dim] fp32
  *   kv_lens     NULL (every row holds S_cap keys) or DEVICE int32 [B];
  *               values are clamped to [0, S_cap]
@@ -227,14 +244,15 @@ int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
  *               Calls that may run concurrently need distinct workspaces.
  * Errors: INVALID_ARGUMENT for null pointers, nonpositive sizes,
  * H_q % H_kv != 0, D % sub_dim != 0, smooth_rows not in {1, H_kv},
- * sliding_window < 0; UNSUPPORTED outside the caps; WORKSPACE when the
- * workspace is NULL or smaller than required.
+ * sliding_window < 0, code_bits not in {8, 4} or a 4-bit shape outside its
+ * limits; UNSUPPORTED outside the caps; WORKSPACE when the workspace is
+ * NULL or smaller than required.
  */
 int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D,
               const uint8_t* k_codes, const float* k_codebook, int k_sub_dim,
               const float* smooth, int smooth_rows, int transform,
               const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
-              int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens,
+              int n_centroids, int code_bits, int H_kv, int S_cap, const int32_t* kv_lens,
               float scale, int causal, int sliding_window,
               void* out_f16, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -265,7 +283,7 @@ int vq_attend_noalloc(const void* q_f16, int B, int H_q, int S_q, int D,
                       const uint8_t* k_codes, const float* k_codebook, int k_sub_dim,
                       const float* smooth, int smooth_rows, int transform,
                       const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
-                      int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens,
+                      int n_centroids, int code_bits, int H_kv, int S_cap, const int32_t* kv_lens,
                       float scale, int causal, int sliding_window,
                       void* out_f16, void* stream);
 

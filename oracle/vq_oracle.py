@@ -354,6 +354,34 @@ def lut_scores(q_row, k_codes_rows, k_codebook, sub_dim, smooth_row=None,
 
 
 # ----------------------------------------------------------------------------
+# Sub-byte codes: two 4-bit indices per byte
+# ----------------------------------------------------------------------------
+def pack_nibbles(codes) -> np.ndarray:
+    """[..., n] indices (n even) -> [..., n / 2] uint8, two per byte.
+
+    "Metal Kernels API" page, rabitq_pack_values: 4-bit indices are packed
+    two per byte along the last axis, the even element in the low nibble,
+    each value masked to 4 bits.  Used here for product-VQ codes of
+    codebooks with at most 16 centroids (b = 4 in the storage formula).
+    """
+    c = np.asarray(codes).astype(np.int64)
+    if c.shape[-1] % 2:
+        raise ValueError("the last axis must have even length")
+    lo = c[..., 0::2] & 0xF
+    hi = c[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed) -> np.ndarray:
+    """Inverse of pack_nibbles: [..., m] uint8 -> [..., 2 m] indices (int64)."""
+    b = np.asarray(packed).astype(np.int64)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int64)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+# ----------------------------------------------------------------------------
 # Storage accounting
 # ----------------------------------------------------------------------------
 def code_bytes_per_token(D: int, sub_dim: int, bits: int) -> float:

@@ -64,8 +64,8 @@ def test_supports_shape(lib, n_c, n_sub, D, ok):
 
 
 def enc(lib, B=1, H=2, S=8, D=64, n_c=256, dsub=4, smooth=P, srows=2, transform=1, S_cap=8,
-        S_off=0, offs=None, keys=P, cb=P, codes=P):
-    return lib.vq_encode(keys, B, H, S, D, cb, n_c, dsub, smooth, srows, transform, codes, S_cap,
+        S_off=0, offs=None, keys=P, cb=P, codes=P, bits=8):
+    return lib.vq_encode(keys, B, H, S, D, cb, n_c, dsub, bits, smooth, srows, transform, codes, S_cap,
                          S_off, offs, None)
 
 
@@ -88,25 +88,32 @@ def test_encode_validation(lib):
     assert enc(lib, B=257, offs=(ctypes.c_int32 * 257)()) == INVALID   # too many rows
     assert enc(lib, B=0) in (OK,)                       # empty: no-op
     assert enc(lib, S=0) in (OK,)
+    # 4-bit codes: at most 16 centroids, an even number of sub-vectors
+    assert enc(lib, bits=5) == INVALID
+    assert enc(lib, bits=4, n_c=17) == INVALID
+    assert b"16 centroids" in lib.vq_last_error()
+    assert enc(lib, bits=4, n_c=16, D=32, dsub=16, S=0) == OK   # valid, empty: no launch
 
 
 def test_decode_and_encode_decode_validation(lib):
-    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, P, 2, 1, P, 8, 0, None, None, 1, None)
+    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, 8, P, 2, 1, P, 8, 0, None, None, 1, None)
     assert st == INVALID                                # recon NULL
-    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, P, 2, 1, P, 8, 0, None, P, 7, None)
+    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, 8, P, 2, 1, P, 8, 0, None, P, 7, None)
     assert st == INVALID                                # out_dtype
-    st = lib.vq_decode(P, 1, 2, 8, 8, 1, P, 256, 4, None, 1, 1, 64, P, 0, None)
+    st = lib.vq_decode(P, 1, 2, 8, 8, 1, P, 256, 4, 8, None, 1, 1, 64, P, 0, None)
     assert st == INVALID                                # slots [1, 9) outside [0, 8)
-    st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 256, 4, None, 1, 1, 48, P, 0, None)
+    st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 256, 4, 8, None, 1, 1, 48, P, 0, None)
     assert st == UNSUPPORTED                            # D = 48
-    st = lib.vq_decode(None, 1, 2, 8, 8, 0, P, 256, 4, None, 1, 1, 64, P, 0, None)
+    st = lib.vq_decode(None, 1, 2, 8, 8, 0, P, 256, 4, 8, None, 1, 1, 64, P, 0, None)
     assert st == INVALID
+    st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 32, 4, 4, None, 1, 1, 64, P, 0, None)
+    assert st == INVALID                                # 4-bit codes, 32 centroids
 
 
 def enc_kv(lib, B=1, H=2, S=8, D=128, dk=8, dv=4, nk=256, nv=256, S_cap=8, S_off=0, offs=None,
-           keys=P, values=P, kcb=P, vcb=P, kc=P, vc=P, smooth=P, srows=2, transform=1):
+           keys=P, values=P, kcb=P, vcb=P, kc=P, vc=P, smooth=P, srows=2, transform=1, bits=8):
     return lib.vq_encode_kv(keys, values, B, H, S, D, kcb, nk, dk, smooth, srows, transform, vcb, nv,
-                            dv, kc, vc, S_cap, S_off, offs, None)
+                            dv, bits, kc, vc, S_cap, S_off, offs, None)
 
 
 def test_encode_kv_validation(lib):
@@ -121,13 +128,14 @@ def test_encode_kv_validation(lib):
     assert enc_kv(lib, B=2, S=4, offs=offs) == INVALID  # row 1 writes [6, 10)
     assert enc_kv(lib, S=0) == OK
     assert enc_kv(lib, B=0) == OK
+    assert enc_kv(lib, bits=4, nk=16, nv=17) == INVALID  # value codebook too large for 4 bits
     if not torch.cuda.is_available():
         assert enc_kv(lib) == NO_DEVICE
 
 
 def att(lib, B=2, Hq=8, Sq=1, D=128, dk=8, dv=4, n_c=256, Hkv=2, S_cap=64, W=0, causal=1,
-        ws=P, ws_bytes=1 << 30, smooth=P, srows=2, scale=0.1, q=P):
-    return lib.vq_attend(q, B, Hq, Sq, D, P, P, dk, smooth, srows, 1, P, P, dv, n_c, Hkv, S_cap,
+        ws=P, ws_bytes=1 << 30, smooth=P, srows=2, scale=0.1, q=P, bits=8):
+    return lib.vq_attend(q, B, Hq, Sq, D, P, P, dk, smooth, srows, 1, P, P, dv, n_c, bits, Hkv, S_cap,
                          None, scale, causal, W, P, ws, ws_bytes, None)
 
 
@@ -145,6 +153,8 @@ def test_attend_validation(lib):
     assert att(lib, ws_bytes=16) == WORKSPACE
     assert b"workspace needs" in lib.vq_last_error()
     assert att(lib, B=0) == OK
+    assert att(lib, bits=4) == INVALID                   # 256 centroids in 4 bits
+    assert att(lib, bits=4, n_c=16, D=64, dk=16) == INVALID   # 4 key sub-vectors: not a multiple of 8
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="a device is visible")
@@ -212,7 +222,9 @@ def test_attend_path_rejects_what_attend_rejects(lib):
         api.vq_attend_path(1, 8, 1, 128, 6, 4, 256, 8, 100)      # D % d_k != 0
     with pytest.raises(api.VQError):
         api.vq_attend_path(1, 8, 1, 128, 8, 4, 257, 8, 100)      # more than 256 centroids
-    assert lib.vq_attend_path(0, 8, 1, 128, 8, 4, 256, 8, 100, 0) == 0
+    assert lib.vq_attend_path(0, 8, 1, 128, 8, 4, 256, 8, 8, 100, 0) == 0
+    with pytest.raises(api.VQError):
+        api.vq_attend_path(1, 8, 1, 128, 8, 4, 17, 8, 100, code_bits=4)    # 17 centroids in 4 bits
 
 
 def test_binding_rejects_wrong_shapes(lib):
@@ -272,12 +284,12 @@ def test_attend_noalloc_validation(lib):
     """vq_attend_noalloc validates like vq_attend, and rejects shapes whose
     partials exceed its device scratch array before touching a device."""
     f = lib.vq_attend_noalloc
-    args = lambda B=2, Hq=8, Sq=1, q=P: (q, B, Hq, Sq, 128, P, P, 8, P, 2, 1, P, P, 4, 256, 2, 64,
+    args = lambda B=2, Hq=8, Sq=1, q=P: (q, B, Hq, Sq, 128, P, P, 8, P, 2, 1, P, P, 4, 256, 8, 2, 64,
                                          None, 0.1, 1, 0, P, None)
     assert f(*args(q=None)) == INVALID
     assert f(*args(Hq=7)) == INVALID                     # H_q % H_kv
     assert f(*args(B=0)) == OK
-    st = f(P, 4, 8, 512, 128, P, P, 8, P, 8, 1, P, P, 4, 256, 8, 32768, None, 0.1, 1, 0, P, None)
+    st = f(P, 4, 8, 512, 128, P, P, 8, P, 8, 1, P, P, 4, 256, 8, 8, 32768, None, 0.1, 1, 0, P, None)
     assert st == WORKSPACE and b"scratch" in lib.vq_last_error()
     if not torch.cuda.is_available():
         assert f(*args()) == NO_DEVICE

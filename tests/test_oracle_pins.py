@@ -114,6 +114,22 @@ def pin_gap_bruteforce(o):
                     assert abs(gap[0, h, t, j] - (srt[1] - srt[0]) / srt[1]) < 1e-12
 
 
+def pin_nibbles(o):
+    """Nibble packing against the hand-worked bytes (low nibble = even
+    element, masked to 4 bits), its inverse, and the storage formula at
+    b = 4: D = 128, d = 8 gives 16 codes in 8 bytes per token and head."""
+    g = read_golden("nibble_pack.txt")
+    codes = g["codes"].astype(np.int64)
+    packed = o.pack_nibbles(codes)
+    assert packed.dtype == np.uint8 and packed.tolist() == g["packed"].astype(int).tolist()
+    assert o.unpack_nibbles(packed).tolist() == g["unpacked"].astype(int).tolist()
+    rng = np.random.default_rng(23)
+    c = rng.integers(0, 16, size=(2, 3, 5, 16))
+    p2 = o.pack_nibbles(c)
+    assert p2.shape == (2, 3, 5, 8) and np.array_equal(o.unpack_nibbles(p2), c)
+    assert p2.shape[-1] == o.code_bytes_per_token(128, 8, 4)
+
+
 def pin_bruteforce(o):
     """Exhaustive search over whole code tuples equals the per-sub-vector
     argmin (product-VQ separability), with the rotation and smoothing
@@ -369,7 +385,7 @@ def pin_randomized_hadamard(o):
 
 ALL_PINS = [pin_hadamard_closed_form, pin_hadamard_golden, pin_hadamard_orthonormal,
             pin_storage, pin_encode_golden, pin_distances_and_gap_golden, pin_gap_bruteforce,
-            pin_bruteforce, pin_ties, pin_identity_codebook,
+            pin_bruteforce, pin_nibbles, pin_ties, pin_identity_codebook,
             pin_idempotent_and_permutation, pin_attend_golden, pin_attend_sdpa,
             pin_attend_closed_forms, pin_gqa_and_window, pin_dual_transform,
             pin_dense_transform, pin_randomized_hadamard]
@@ -580,11 +596,27 @@ def _mut_distances_transposed(mp):
     mp.setattr(O, "pvq_distances", dist)
 
 
+def _mut_nibble_order(mp):
+    # the even element in the high nibble
+    def pack(codes):
+        c = np.asarray(codes).astype(np.int64)
+        return (((c[..., 0::2] & 0xF) << 4) | (c[..., 1::2] & 0xF)).astype(np.uint8)
+
+    def unpack(packed):
+        b = np.asarray(packed).astype(np.int64)
+        out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int64)
+        out[..., 0::2], out[..., 1::2] = b >> 4, b & 0xF
+        return out
+    mp.setattr(O, "pack_nibbles", pack)
+    mp.setattr(O, "unpack_nibbles", unpack)
+
+
 MUTATIONS = [_mut_matrix_involutory, _mut_dual_untransposed, _mut_smooth_direction, _mut_unnormalized_hadamard, _mut_no_inverse_rotation,
              _mut_ties_high, _mut_strided_split, _mut_head_aligned_causal,
              _mut_window_off_by_one, _mut_window_needs_causal, _mut_gqa_modulo,
              _mut_lut_divides, _mut_missing_scale, _mut_value_transposed,
-             _mut_gap_relative_to_d1, _mut_gap_third_smallest, _mut_distances_transposed]
+             _mut_gap_relative_to_d1, _mut_gap_third_smallest, _mut_distances_transposed,
+             _mut_nibble_order]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda m: m.__name__)

@@ -115,40 +115,54 @@ def _n_sub(D, sub_dim, name="sub_dim"):
     return D // sub_dim
 
 
+def _row_bytes(n_sub, code_bits):
+    """Bytes of one token's code row: one code per byte, or two (4-bit)."""
+    if code_bits == 8:
+        return n_sub
+    if code_bits == 4:
+        if n_sub % 2:
+            raise ValueError("4-bit codes need an even number of sub-vectors")
+        return n_sub // 2
+    raise ValueError(f"code_bits must be 8 or 4, got {code_bits}")
+
+
 def vq_supports_shape(n_centroids: int, n_sub: int, head_dim: int) -> bool:
     return bool(_lib.load().vq_supports_shape(n_centroids, n_sub, head_dim))
 
 
 def vq_encode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=None,
-              S_cap=None, S_off=0, row_offsets=None, stream=None, prepare=False):
-    """Encode fp16 keys [B, H, S, D] into uint8 codes [B, H, S_cap, D // sub_dim].
+              S_cap=None, S_off=0, row_offsets=None, code_bits=8, stream=None, prepare=False):
+    """Encode fp16 keys [B, H, S, D] into uint8 codes [B, H, S_cap, row_bytes]
+    (row_bytes = D // sub_dim, or half that with code_bits=4: two codes per
+    byte, the even sub-vector in the low nibble).
 
     Codes of token t of row b land in slot off_b + t (off_b = row_offsets[b]
     or S_off).  Returns the code tensor (allocated when `codes` is None)."""
     _need(keys, "keys", torch.float16, 4)
     B, H, S, D = keys.shape
-    n_sub = _n_sub(D, sub_dim)
+    nb = _row_bytes(_n_sub(D, sub_dim), code_bits)
     _need(codebook, "codebook", torch.float32, shape=(None, sub_dim))
     if codes is None:
-        codes = torch.zeros((B, H, S_cap or S, n_sub), dtype=torch.uint8, device=keys.device)
-    _need(codes, "codes", torch.uint8, shape=(B, H, S_cap, n_sub))
+        codes = torch.zeros((B, H, S_cap or S, nb), dtype=torch.uint8, device=keys.device)
+    _need(codes, "codes", torch.uint8, shape=(B, H, S_cap, nb))
     sm, rows = _smooth(smooth, D, H)
     offs = _offsets(row_offsets, B)
     _on_device(keys=keys, codebook=codebook, codes=codes, smooth=sm)
     return _call("vq_encode", _ptr(keys), B, H, S, D, _ptr(codebook), codebook.shape[0], sub_dim,
-                 _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off, offs,
+                 code_bits, _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off, offs,
                  _stream(stream), prepare=prepare, result=codes)
 
 
 def vq_encode_kv(keys, values, k_codebook, k_sub_dim, v_codebook, v_sub_dim, *, smooth=None,
                  transform=True, k_codes=None, v_codes=None, S_cap=None, S_off=0,
-                 row_offsets=None, stream=None, prepare=False):
+                 row_offsets=None, code_bits=8, stream=None, prepare=False):
     """Encode the keys (smoothed, rotated) and the values (neither) of one
     append into their code buffers; returns (k_codes, v_codes)."""
     _need(keys, "keys", torch.float16, 4)
     B, H, S, D = keys.shape
     _need(values, "values", torch.float16, shape=(B, H, S, D))
-    nk, nv = _n_sub(D, k_sub_dim, "k_sub_dim"), _n_sub(D, v_sub_dim, "v_sub_dim")
+    nk = _row_bytes(_n_sub(D, k_sub_dim, "k_sub_dim"), code_bits)
+    nv = _row_bytes(_n_sub(D, v_sub_dim, "v_sub_dim"), code_bits)
     _need(k_codebook, "k_codebook", torch.float32, shape=(None, k_sub_dim))
     _need(v_codebook, "v_codebook", torch.float32, shape=(None, v_sub_dim))
     if k_codes is None:
@@ -163,22 +177,22 @@ def vq_encode_kv(keys, values, k_codebook, k_sub_dim, v_codebook, v_sub_dim, *, 
                k_codes=k_codes, v_codes=v_codes, smooth=sm)
     return _call("vq_encode_kv", _ptr(keys), _ptr(values), B, H, S, D, _ptr(k_codebook),
                  k_codebook.shape[0], k_sub_dim, _ptr(sm), rows, int(bool(transform)),
-                 _ptr(v_codebook), v_codebook.shape[0], v_sub_dim, _ptr(k_codes), _ptr(v_codes),
+                 _ptr(v_codebook), v_codebook.shape[0], v_sub_dim, code_bits, _ptr(k_codes), _ptr(v_codes),
                  k_codes.shape[2], S_off, offs, _stream(stream), prepare=prepare,
                  result=(k_codes, v_codes))
 
 
 def vq_encode_decode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=None,
                      S_cap=None, S_off=0, row_offsets=None, recon=None,
-                     out_dtype=torch.float16, stream=None, prepare=False):
+                     out_dtype=torch.float16, code_bits=8, stream=None, prepare=False):
     """Fused encode + reconstruction.  Returns (recon [B, H, S, D], codes)."""
     _need(keys, "keys", torch.float16, 4)
     B, H, S, D = keys.shape
-    n_sub = _n_sub(D, sub_dim)
+    nb = _row_bytes(_n_sub(D, sub_dim), code_bits)
     _need(codebook, "codebook", torch.float32, shape=(None, sub_dim))
     if codes is None:
-        codes = torch.zeros((B, H, S_cap or S, n_sub), dtype=torch.uint8, device=keys.device)
-    _need(codes, "codes", torch.uint8, shape=(B, H, S_cap, n_sub))
+        codes = torch.zeros((B, H, S_cap or S, nb), dtype=torch.uint8, device=keys.device)
+    _need(codes, "codes", torch.uint8, shape=(B, H, S_cap, nb))
     if recon is None:
         recon = torch.empty((B, H, S, D), dtype=out_dtype, device=keys.device)
     _need(recon, "recon", (torch.float32, torch.float16), shape=(B, H, S, D))
@@ -186,18 +200,22 @@ def vq_encode_decode(keys, codebook, sub_dim, *, smooth=None, transform=True, co
     offs = _offsets(row_offsets, B)
     _on_device(keys=keys, codebook=codebook, codes=codes, recon=recon, smooth=sm)
     return _call("vq_encode_decode", _ptr(keys), B, H, S, D, _ptr(codebook), codebook.shape[0],
-                 sub_dim, _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off,
+                 sub_dim, code_bits, _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off,
                  offs, _ptr(recon), 1 if recon.dtype == torch.float16 else 0, _stream(stream),
                  prepare=prepare, result=(recon, codes))
 
 
 def vq_decode(codes, codebook, *, smooth=None, transform=True, S=None, S_off=0,
-              out=None, out_dtype=torch.float32, stream=None, prepare=False):
-    """Decode slots [S_off, S_off + S) of codes [B, H, S_cap, n_sub] into
-    [B, H, S, n_sub * sub_dim] (fp32 by default)."""
+              out=None, out_dtype=torch.float32, code_bits=8, stream=None, prepare=False):
+    """Decode slots [S_off, S_off + S) of codes [B, H, S_cap, row_bytes] into
+    [B, H, S, n_sub * sub_dim] (fp32 by default); n_sub = row_bytes, or twice
+    that with code_bits=4."""
     _need(codes, "codes", torch.uint8, 4)
     _need(codebook, "codebook", torch.float32, 2)
-    B, H, S_cap, n_sub = codes.shape
+    B, H, S_cap, nb = codes.shape
+    if code_bits not in (8, 4):
+        raise ValueError(f"code_bits must be 8 or 4, got {code_bits}")
+    n_sub = nb * 8 // code_bits
     sub_dim = codebook.shape[1]
     D = n_sub * sub_dim
     S = S_cap - S_off if S is None else S
@@ -207,7 +225,7 @@ def vq_decode(codes, codebook, *, smooth=None, transform=True, S=None, S_off=0,
     sm, rows = _smooth(smooth, D, H)
     _on_device(codes=codes, codebook=codebook, out=out, smooth=sm)
     return _call("vq_decode", _ptr(codes), B, H, S, S_cap, S_off, _ptr(codebook), codebook.shape[0],
-                 sub_dim, _ptr(sm), rows, int(bool(transform)), D, _ptr(out),
+                 sub_dim, code_bits, _ptr(sm), rows, int(bool(transform)), D, _ptr(out),
                  1 if out.dtype == torch.float16 else 0, _stream(stream), prepare=prepare,
                  result=out)
 
@@ -220,13 +238,13 @@ PATH_NAMES = {1: "stream", 2: "tile", 3: "lut_mfma", 4: "lut_valu"}
 
 
 def vq_attend_path(B, H_q, S_q, D, k_sub_dim, v_sub_dim, n_centroids, H_kv, S_cap,
-                   sliding_window=0) -> str:
+                   sliding_window=0, code_bits=8) -> str:
     """Name of the kernel family vq_attend runs for this shape ("stream",
     "tile", "lut_mfma", "lut_valu"); raises VQError when vq_attend would
     reject the shape. Host-only."""
     lib = _lib.load()
-    p = int(lib.vq_attend_path(B, H_q, S_q, D, k_sub_dim, v_sub_dim, n_centroids, H_kv, S_cap,
-                               sliding_window))
+    p = int(lib.vq_attend_path(B, H_q, S_q, D, k_sub_dim, v_sub_dim, n_centroids, code_bits, H_kv,
+                               S_cap, sliding_window))
     if p not in PATH_NAMES:
         raise VQError(VQ_ERR_UNSUPPORTED, lib.vq_last_error().decode())
     return PATH_NAMES[p]
@@ -239,7 +257,7 @@ def attend_workspace(q, k_codes, sliding_window=0):
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=q.device)
 
 
-def _attend_args(q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out):
+def _attend_args(q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out, code_bits):
     """Shape checks shared by the attention entry points; returns the
     marshalled sizes and the (allocated if None) output."""
     _need(q, "q", torch.float16, 4)
@@ -247,7 +265,8 @@ def _attend_args(q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, o
     _need(k_codebook, "k_codebook", torch.float32, 2)
     _need(v_codebook, "v_codebook", torch.float32, 2)
     dk, dv = k_codebook.shape[1], v_codebook.shape[1]
-    nk, nv = _n_sub(D, dk, "key sub_dim"), _n_sub(D, dv, "value sub_dim")
+    nk = _row_bytes(_n_sub(D, dk, "key sub_dim"), code_bits)
+    nv = _row_bytes(_n_sub(D, dv, "value sub_dim"), code_bits)
     if k_codebook.shape[0] != v_codebook.shape[0]:
         raise ValueError("key and value codebooks disagree on n_centroids")
     _need(k_codes, "k_codes", torch.uint8, shape=(B, None, None, nk))
@@ -264,11 +283,11 @@ def _attend_args(q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, o
 
 def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None,
               transform=True, kv_lens=None, causal=True, sliding_window=0, out=None,
-              workspace=None, stream=None, prepare=False):
+              workspace=None, code_bits=8, stream=None, prepare=False):
     """Attention of raw fp16 queries [B, H_q, S_q, D] over key/value codes
-    [B, H_kv, S_cap, n_sub]; returns fp16 [B, H_q, S_q, D]."""
+    [B, H_kv, S_cap, row_bytes] (code_bits wide); returns fp16 [B, H_q, S_q, D]."""
     B, Hq, Sq, D, dk, dv, Hkv, S_cap, sm, rows, out = _attend_args(
-        q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out)
+        q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out, code_bits)
     if workspace is None:
         workspace = attend_workspace(q, k_codes, sliding_window)
     _need(workspace, "workspace", None, 1)
@@ -276,7 +295,7 @@ def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None
                v_codebook=v_codebook, kv_lens=kv_lens, out=out, workspace=workspace, smooth=sm)
     return _call("vq_attend", _ptr(q), B, Hq, Sq, D, _ptr(k_codes), _ptr(k_codebook),
                  dk, _ptr(sm), rows, int(bool(transform)), _ptr(v_codes),
-                 _ptr(v_codebook), dv, k_codebook.shape[0], Hkv, S_cap,
+                 _ptr(v_codebook), dv, k_codebook.shape[0], code_bits, Hkv, S_cap,
                  _ptr(kv_lens), float(scale), int(bool(causal)), int(sliding_window), _ptr(out),
                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
                  prepare=prepare, result=out)
@@ -284,17 +303,17 @@ def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None
 
 def vq_attend_noalloc(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None,
                       transform=True, kv_lens=None, causal=True, sliding_window=0, out=None,
-                      stream=None, prepare=False):
+                      code_bits=8, stream=None, prepare=False):
     """vq_attend with the split partials in the library's per-GPU device
     scratch array instead of a workspace (no device allocation when `out` is
     given).  Calls that overlap on one GPU race; shapes needing more than
     VQ_NOALLOC_SCRATCH_BYTES of partials raise VQError."""
     B, Hq, Sq, D, dk, dv, Hkv, S_cap, sm, rows, out = _attend_args(
-        q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out)
+        q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out, code_bits)
     _on_device(q=q, k_codes=k_codes, k_codebook=k_codebook, v_codes=v_codes,
                v_codebook=v_codebook, kv_lens=kv_lens, out=out, smooth=sm)
     return _call("vq_attend_noalloc", _ptr(q), B, Hq, Sq, D, _ptr(k_codes), _ptr(k_codebook),
                  dk, _ptr(sm), rows, int(bool(transform)), _ptr(v_codes),
-                 _ptr(v_codebook), dv, k_codebook.shape[0], Hkv, S_cap,
+                 _ptr(v_codebook), dv, k_codebook.shape[0], code_bits, Hkv, S_cap,
                  _ptr(kv_lens), float(scale), int(bool(causal)), int(sliding_window), _ptr(out),
                  _stream(stream), prepare=prepare, result=out)

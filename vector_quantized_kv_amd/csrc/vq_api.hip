@@ -65,6 +65,20 @@ int check_transform(const char* what, int transform, int D) {
   return VQ_OK;
 }
 
+// 8-bit codes (one byte each) or 4-bit codes (two per byte: n_c <= 16 and an
+// even number of sub-vectors; `multiple` more for kernels that read whole words).
+int check_code_bits(const char* what, int code_bits, int n_c, int n_sub, int multiple) {
+  if (code_bits == 8) return VQ_OK;
+  if (code_bits != 4)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: code_bits must be 8 or 4 (got %d)", what, code_bits);
+  if (n_c > 16)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: 4-bit codes hold at most 16 centroids (got %d)", what, n_c);
+  if (n_sub % multiple != 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: 4-bit codes need a multiple of %d sub-vectors (got %d)", what,
+                multiple, n_sub);
+  return VQ_OK;
+}
+
 // Device buffers are read and written with 16-byte vector accesses.
 int check_aligned(const char* what, std::initializer_list<const void*> ptrs) {
   for (const void* ptr : ptrs)
@@ -85,7 +99,7 @@ int hip_status(const char* what, hipError_t e) {
 
 // Shared validation of vq_encode / vq_encode_decode.
 int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
-                 const float* codebook, int n_c, int sub_dim, const float* smooth,
+                 const float* codebook, int n_c, int sub_dim, int code_bits, const float* smooth,
                  int smooth_rows, int transform, const uint8_t* codes, int S_cap, int S_off,
                  const int32_t* row_offsets) {
   if (B < 0 || H <= 0 || S < 0)
@@ -94,6 +108,7 @@ int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: keys, codebook and codes must be non-null", what);
   int st = check_quantizer(what, D, n_c, sub_dim);
   if (st) return st;
+  if ((st = check_code_bits(what, code_bits, n_c, D / sub_dim, 2))) return st;
   if ((st = check_smooth(what, smooth, smooth_rows, H))) return st;
   if ((st = check_transform(what, transform, D))) return st;
   if ((st = check_aligned(what, {keys, codebook, smooth}))) return st;
@@ -116,7 +131,7 @@ int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
 }
 
 int run_encode(const char* what, const void* keys, const uint8_t* codes_in, int B, int H, int S,
-               int D, const float* codebook, int n_c, int sub_dim, const float* smooth,
+               int D, const float* codebook, int n_c, int sub_dim, int code_bits, const float* smooth,
                int smooth_rows, int transform, uint8_t* codes, int S_cap, int S_off,
                const int32_t* row_offsets, void* recon, int out_dtype, int mode, void* stream) {
   if (B == 0 || S == 0) return VQ_OK;
@@ -129,7 +144,7 @@ int run_encode(const char* what, const void* keys, const uint8_t* codes_in, int 
   a.smooth = smooth;
   a.codes = codes;
   a.recon = recon;
-  a.B = B; a.H = H; a.S = S; a.D = D; a.n_c = n_c; a.sub_dim = sub_dim;
+  a.B = B; a.H = H; a.S = S; a.D = D; a.n_c = n_c; a.sub_dim = sub_dim; a.code_bits = code_bits;
   a.smooth_rows = smooth_rows; a.transform = transform;
   a.S_cap = S_cap; a.S_off = S_off; a.use_row_offsets = row_offsets != nullptr;
   a.recon_dtype = out_dtype;
@@ -178,9 +193,9 @@ int scratch_address(const char* what, void** out) {
 int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, int D,
                 const uint8_t* k_codes, const float* k_codebook, int k_sub_dim, const float* smooth,
                 int smooth_rows, int transform, const uint8_t* v_codes, const float* v_codebook,
-                int v_sub_dim, int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens,
-                float scale, int causal, int sliding_window, void* out_f16, void* workspace,
-                size_t workspace_bytes, bool noalloc, void* stream) {
+                int v_sub_dim, int n_centroids, int code_bits, int H_kv, int S_cap,
+                const int32_t* kv_lens, float scale, int causal, int sliding_window, void* out_f16,
+                void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
   if (B < 0 || S_q < 0)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0 and S_q >= 0 (got %d, %d)", what, B, S_q);
   if (H_q <= 0 || H_kv <= 0 || S_cap <= 0)
@@ -195,6 +210,8 @@ int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, in
   if ((st = check_quantizer(what, D, n_centroids, v_sub_dim))) return st;
   if ((D / k_sub_dim) % 4 != 0 || (D / v_sub_dim) % 4 != 0)
     return fail(VQ_ERR_UNSUPPORTED, "%s: the number of key and value sub-vectors must be multiples of 4", what);
+  if ((st = check_code_bits(what, code_bits, n_centroids, D / k_sub_dim, 8))) return st;
+  if ((st = check_code_bits(what, code_bits, n_centroids, D / v_sub_dim, 8))) return st;
   if ((st = check_smooth(what, smooth, smooth_rows, H_kv))) return st;
   if ((st = check_transform(what, transform, D))) return st;
   if (causal != 0 && causal != 1)
@@ -231,7 +248,7 @@ int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, in
   a.out = reinterpret_cast<__half*>(out_f16);
   a.partials = reinterpret_cast<float*>(workspace);
   a.B = B; a.Hq = H_q; a.Sq = S_q; a.D = D; a.Hkv = H_kv; a.S_cap = S_cap;
-  a.dk = k_sub_dim; a.dv = v_sub_dim; a.n_c = n_centroids;
+  a.dk = k_sub_dim; a.dv = v_sub_dim; a.n_c = n_centroids; a.code_bits = code_bits;
   a.smooth_rows = smooth_rows; a.transform = transform;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.causal = causal; a.window = sliding_window;
@@ -278,29 +295,30 @@ int vq_supports_shape(int n_centroids, int n_sub, int head_dim) {
 }
 
 int vq_encode(const void* keys_f16, int B, int H, int S, int D, const float* codebook,
-              int n_centroids, int sub_dim, const float* smooth, int smooth_rows, int transform,
-              uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets, void* stream) {
+              int n_centroids, int sub_dim, int code_bits, const float* smooth, int smooth_rows,
+              int transform, uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets,
+              void* stream) {
   g_last_error[0] = 0;
-  int st = check_encode("vq_encode", keys_f16, B, H, S, D, codebook, n_centroids, sub_dim, smooth,
-                        smooth_rows, transform, codes, S_cap, S_off, row_offsets);
+  int st = check_encode("vq_encode", keys_f16, B, H, S, D, codebook, n_centroids, sub_dim, code_bits,
+                        smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets);
   if (st) return st;
   return run_encode("vq_encode", keys_f16, nullptr, B, H, S, D, codebook, n_centroids, sub_dim,
-                    smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets, nullptr, 0,
-                    0, stream);
+                    code_bits, smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets,
+                    nullptr, 0, 0, stream);
 }
 
 int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int S, int D,
                  const float* k_codebook, int k_n_centroids, int k_sub_dim, const float* smooth,
                  int smooth_rows, int transform, const float* v_codebook, int v_n_centroids,
-                 int v_sub_dim, uint8_t* k_codes, uint8_t* v_codes, int S_cap, int S_off,
-                 const int32_t* row_offsets, void* stream) {
+                 int v_sub_dim, int code_bits, uint8_t* k_codes, uint8_t* v_codes, int S_cap,
+                 int S_off, const int32_t* row_offsets, void* stream) {
   g_last_error[0] = 0;
   const char* what = "vq_encode_kv";
-  int st = check_encode(what, keys_f16, B, H, S, D, k_codebook, k_n_centroids, k_sub_dim, smooth,
-                        smooth_rows, transform, k_codes, S_cap, S_off, row_offsets);
+  int st = check_encode(what, keys_f16, B, H, S, D, k_codebook, k_n_centroids, k_sub_dim, code_bits,
+                        smooth, smooth_rows, transform, k_codes, S_cap, S_off, row_offsets);
   if (st) return st;
-  if ((st = check_encode(what, values_f16, B, H, S, D, v_codebook, v_n_centroids, v_sub_dim, nullptr, 1,
-                         0, v_codes, S_cap, S_off, row_offsets)))
+  if ((st = check_encode(what, values_f16, B, H, S, D, v_codebook, v_n_centroids, v_sub_dim, code_bits,
+                         nullptr, 1, 0, v_codes, S_cap, S_off, row_offsets)))
     return st;
   if (B == 0 || S == 0) return VQ_OK;
   if ((st = check_device(what))) return st;
@@ -310,6 +328,7 @@ int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int
   k.smooth = smooth;
   k.codes = k_codes;
   k.B = B; k.H = H; k.S = S; k.D = D; k.n_c = k_n_centroids; k.sub_dim = k_sub_dim;
+  k.code_bits = code_bits;
   k.smooth_rows = smooth_rows; k.transform = transform;
   k.S_cap = S_cap; k.S_off = S_off; k.use_row_offsets = row_offsets != nullptr;
   v = k;
@@ -329,25 +348,26 @@ int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int
 }
 
 int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D, const float* codebook,
-                     int n_centroids, int sub_dim, const float* smooth, int smooth_rows,
-                     int transform, uint8_t* codes, int S_cap, int S_off,
+                     int n_centroids, int sub_dim, int code_bits, const float* smooth,
+                     int smooth_rows, int transform, uint8_t* codes, int S_cap, int S_off,
                      const int32_t* row_offsets, void* recon, int out_dtype, void* stream) {
   g_last_error[0] = 0;
   int st = check_encode("vq_encode_decode", keys_f16, B, H, S, D, codebook, n_centroids, sub_dim,
-                        smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets);
+                        code_bits, smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets);
   if (st) return st;
   if (!recon) return fail(VQ_ERR_INVALID_ARGUMENT, "vq_encode_decode: recon must be non-null");
   if ((st = check_aligned("vq_encode_decode", {recon}))) return st;
   if (out_dtype != 0 && out_dtype != 1)
     return fail(VQ_ERR_INVALID_ARGUMENT, "vq_encode_decode: out_dtype must be 0 (fp32) or 1 (fp16)");
   return run_encode("vq_encode_decode", keys_f16, nullptr, B, H, S, D, codebook, n_centroids,
-                    sub_dim, smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets,
-                    recon, out_dtype, 1, stream);
+                    sub_dim, code_bits, smooth, smooth_rows, transform, codes, S_cap, S_off,
+                    row_offsets, recon, out_dtype, 1, stream);
 }
 
 int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
-              const float* codebook, int n_centroids, int sub_dim, const float* smooth,
-              int smooth_rows, int transform, int D, void* out, int out_dtype, void* stream) {
+              const float* codebook, int n_centroids, int sub_dim, int code_bits,
+              const float* smooth, int smooth_rows, int transform, int D, void* out, int out_dtype,
+              void* stream) {
   g_last_error[0] = 0;
   const char* what = "vq_decode";
   if (B < 0 || H <= 0 || S < 0)
@@ -356,6 +376,7 @@ int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: codes, codebook and out must be non-null", what);
   int st = check_quantizer(what, D, n_centroids, sub_dim);
   if (st) return st;
+  if ((st = check_code_bits(what, code_bits, n_centroids, D / sub_dim, 2))) return st;
   if ((st = check_smooth(what, smooth, smooth_rows, H))) return st;
   if ((st = check_transform(what, transform, D))) return st;
   if (out_dtype != 0 && out_dtype != 1)
@@ -364,8 +385,8 @@ int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
   if (S_cap <= 0 || S_off < 0 || (long long)S_off + S > S_cap)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: slots [%d, %lld) fall outside [0, %d)", what, S_off,
                 (long long)S_off + S, S_cap);
-  return run_encode(what, nullptr, codes, B, H, S, D, codebook, n_centroids, sub_dim, smooth,
-                    smooth_rows, transform, nullptr, S_cap, S_off, nullptr, out, out_dtype, 2,
+  return run_encode(what, nullptr, codes, B, H, S, D, codebook, n_centroids, sub_dim, code_bits,
+                    smooth, smooth_rows, transform, nullptr, S_cap, S_off, nullptr, out, out_dtype, 2,
                     stream);
 }
 
@@ -377,7 +398,7 @@ size_t vq_attend_workspace_bytes(int B, int H_q, int S_q, int D, int H_kv, int S
 }
 
 int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
-                   int n_centroids, int H_kv, int S_cap, int sliding_window) {
+                   int n_centroids, int code_bits, int H_kv, int S_cap, int sliding_window) {
   g_last_error[0] = 0;
   const char* what = "vq_attend_path";
   if (B <= 0 || H_q <= 0 || S_q <= 0 || H_kv <= 0 || S_cap <= 0) {
@@ -395,8 +416,11 @@ int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
     fail(VQ_ERR_UNSUPPORTED, "%s: the numbers of key and value sub-vectors must be multiples of 4", what);
     return 0;
   }
+  if (check_code_bits(what, code_bits, n_centroids, D / k_sub_dim, 8) ||
+      check_code_bits(what, code_bits, n_centroids, D / v_sub_dim, 8))
+    return 0;
   const int path = attend_path(B, H_q, S_q, D, H_kv, S_cap, sliding_window, k_sub_dim, v_sub_dim,
-                               n_centroids);
+                               n_centroids, code_bits);
   if (!path) fail(VQ_ERR_UNSUPPORTED, "%s: no kernel fits this shape", what);
   return path;
 }
@@ -404,25 +428,26 @@ int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
 int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* k_codes,
               const float* k_codebook, int k_sub_dim, const float* smooth, int smooth_rows,
               int transform, const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
-              int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens, float scale,
-              int causal, int sliding_window, void* out_f16, void* workspace,
+              int n_centroids, int code_bits, int H_kv, int S_cap, const int32_t* kv_lens,
+              float scale, int causal, int sliding_window, void* out_f16, void* workspace,
               size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   return attend_impl("vq_attend", q_f16, B, H_q, S_q, D, k_codes, k_codebook, k_sub_dim, smooth,
-                     smooth_rows, transform, v_codes, v_codebook, v_sub_dim, n_centroids, H_kv, S_cap,
-                     kv_lens, scale, causal, sliding_window, out_f16, workspace, workspace_bytes,
-                     false, stream);
+                     smooth_rows, transform, v_codes, v_codebook, v_sub_dim, n_centroids, code_bits,
+                     H_kv, S_cap, kv_lens, scale, causal, sliding_window, out_f16, workspace,
+                     workspace_bytes, false, stream);
 }
 
 int vq_attend_noalloc(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* k_codes,
                       const float* k_codebook, int k_sub_dim, const float* smooth, int smooth_rows,
                       int transform, const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
-                      int n_centroids, int H_kv, int S_cap, const int32_t* kv_lens, float scale,
-                      int causal, int sliding_window, void* out_f16, void* stream) {
+                      int n_centroids, int code_bits, int H_kv, int S_cap, const int32_t* kv_lens,
+                      float scale, int causal, int sliding_window, void* out_f16, void* stream) {
   g_last_error[0] = 0;
   return attend_impl("vq_attend_noalloc", q_f16, B, H_q, S_q, D, k_codes, k_codebook, k_sub_dim,
-                     smooth, smooth_rows, transform, v_codes, v_codebook, v_sub_dim, n_centroids, H_kv,
-                     S_cap, kv_lens, scale, causal, sliding_window, out_f16, nullptr, 0, true, stream);
+                     smooth, smooth_rows, transform, v_codes, v_codebook, v_sub_dim, n_centroids,
+                     code_bits, H_kv, S_cap, kv_lens, scale, causal, sliding_window, out_f16, nullptr, 0,
+                     true, stream);
 }
 
 }  // extern "C"

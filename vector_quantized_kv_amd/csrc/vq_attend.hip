@@ -186,7 +186,10 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   const int n_chunks = (n_tok + 63) / 64;
   const int n_iter = (n_chunks + kWaves - 1) / kWaves;
   const size_t row0 = (size_t)unit * p.S_cap;
-  const int nskw = p.nsk / 4, nsvw = p.nsv / 4;
+  // bytes of a token's key / value code row; 32-bit words of codes
+  const int cps = p.code_bits == 4 ? 2 : 1;  // codes per byte
+  const int krow = p.nsk / cps, vrow = p.nsv / cps;
+  const int nskw = krow / 4, nsvw = vrow / 4;
   const int cmax = p.n_c - 1;  // codes beyond the codebook are clamped, never read out of bounds
 
   for (int it = 0; it < n_iter; ++it) {
@@ -198,17 +201,32 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) sc[r] = 0.f;
     if (tv) {
-      const uint32_t* kr = reinterpret_cast<const uint32_t*>(kcodes + (row0 + t) * p.nsk);
-      for (int jw = 0; jw < nskw; ++jw) {
-        const uint32_t w = kr[jw];
+      const uint32_t* kr = reinterpret_cast<const uint32_t*>(kcodes + (row0 + t) * krow);
+      if (p.code_bits == 4) {
+        for (int jw = 0; jw < nskw; ++jw) {
+          const uint32_t w = kr[jw];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int code = min((int)((w >> (8 * k)) & 0xff), cmax);
-          const float* e = lut + ((size_t)(jw * 4 + k) * p.n_c + code) * R;
-          float v[R];
-          lds_read_row<R>(e, v);
+          for (int k = 0; k < 8; ++k) {  // sub-vector 8 jw + k in nibble k
+            const int code = min((int)((w >> (4 * k)) & 0xf), cmax);
+            const float* e = lut + ((size_t)(jw * 8 + k) * p.n_c + code) * R;
+            float v[R];
+            lds_read_row<R>(e, v);
 #pragma unroll
-          for (int r = 0; r < R; ++r) sc[r] += v[r];
+            for (int r = 0; r < R; ++r) sc[r] += v[r];
+          }
+        }
+      } else {
+        for (int jw = 0; jw < nskw; ++jw) {
+          const uint32_t w = kr[jw];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int code = min((int)((w >> (8 * k)) & 0xff), cmax);
+            const float* e = lut + ((size_t)(jw * 4 + k) * p.n_c + code) * R;
+            float v[R];
+            lds_read_row<R>(e, v);
+#pragma unroll
+            for (int r = 0; r < R; ++r) sc[r] += v[r];
+          }
         }
       }
     }
@@ -229,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
       pst[lane * R + r] = pr;
     }
     {
-      const uint32_t* vr = reinterpret_cast<const uint32_t*>(vcodes + (row0 + (tv ? t : 0)) * p.nsv);
+      const uint32_t* vr = reinterpret_cast<const uint32_t*>(vcodes + (row0 + (tv ? t : 0)) * vrow);
       for (int jw = 0; jw < nsvw; ++jw) vst[lane * nsvw + jw] = tv ? vr[jw] : 0u;
     }
     __syncthreads();
@@ -238,20 +256,25 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
       const int tk = tt * TG + ts;
       float pr[R];
       lds_read_row<R>(pst + tk * R, pr);
-      const uint8_t* cr = vst_b + (size_t)tk * p.nsv;
+      const uint8_t* cr = vst_b + (size_t)tk * vrow;
+      // code of value sub-vector i of this token
+      auto vcode = [&](int i) {
+        const int c = p.code_bits == 4 ? (cr[i >> 1] >> (4 * (i & 1))) & 15 : cr[i];
+        return min(c, cmax);
+      };
       float c4[4];
       if (p.dv >= 4) {
         const int dim0 = 4 * dq;
-        const int code = min((int)cr[dim0 / p.dv], cmax);
+        const int code = vcode(dim0 / p.dv);
         const float4 v = *reinterpret_cast<const float4*>(cv + code * p.dv + dim0 % p.dv);
         c4[0] = v.x; c4[1] = v.y; c4[2] = v.z; c4[3] = v.w;
       } else if (p.dv == 2) {
-        const int c0 = min((int)cr[2 * dq], cmax), c1 = min((int)cr[2 * dq + 1], cmax);
+        const int c0 = vcode(2 * dq), c1 = vcode(2 * dq + 1);
         c4[0] = cv[c0 * 2]; c4[1] = cv[c0 * 2 + 1];
         c4[2] = cv[c1 * 2]; c4[3] = cv[c1 * 2 + 1];
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) c4[e] = cv[min((int)cr[4 * dq + e], cmax)];
+        for (int e = 0; e < 4; ++e) c4[e] = cv[vcode(4 * dq + e)];
       }
 #pragma unroll
       for (int r = 0; r < R; ++r)
@@ -461,21 +484,24 @@ int attend_pick_rows(int rows, int nsk, int n_c, int dv, int nsv, int D, size_t*
 }
 
 int attend_path(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, int dk, int dv,
-                int n_c) {
-  if (tile_plan(B, Hq, Sq, D, Hkv, S_cap, window, dk, dv, n_c, nullptr)) return VQ_PATH_TILE;
+                int n_c, int code_bits) {
+  // 4-bit codes run on the streaming kernel and the per-unit VALU kernel
+  if (code_bits == 8 && tile_plan(B, Hq, Sq, D, Hkv, S_cap, window, dk, dv, n_c, nullptr))
+    return VQ_PATH_TILE;
   if (stream_plan(B, Hq, Sq, D, Hkv, S_cap, window, dk, dv, n_c, nullptr, nullptr, nullptr))
     return VQ_PATH_STREAM;
   AttendPlan plan;
   if (!plan_attend(B, Hq, Sq, D, Hkv, S_cap, window, &plan)) return 0;
   int R = 0;
   size_t lds = 0;
-  if (attend_mfma_plan(D, dv, D / dk, plan.rows, &R, &lds)) return VQ_PATH_LUT_MFMA;
+  if (code_bits == 8 && attend_mfma_plan(D, dv, D / dk, plan.rows, &R, &lds)) return VQ_PATH_LUT_MFMA;
   if (attend_pick_rows(plan.rows, D / dk, n_c, dv, D / dv, D, &lds)) return VQ_PATH_LUT_VALU;
   return 0;
 }
 
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_t st) {
-  const int path = attend_path(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c);
+  const int path = attend_path(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c,
+                               a.code_bits);
   if (path == VQ_PATH_TILE) {
     TileParams tp;
     tile_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c, &tp);
@@ -490,11 +516,11 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_
   AttParams p;
   p.B = a.B; p.Hq = a.Hq; p.Sq = a.Sq; p.Hkv = a.Hkv; p.S_cap = a.S_cap;
   p.dk = a.dk; p.dv = a.dv; p.n_c = a.n_c; p.nsk = a.D / a.dk; p.nsv = a.D / a.dv;
-  p.smooth_rows = a.smooth_rows; p.transform = a.transform;
+  p.smooth_rows = a.smooth_rows; p.transform = a.transform; p.code_bits = a.code_bits;
   p.causal = a.causal; p.window = a.window;
   p.G = plan.G; p.rows = plan.rows; p.split_tokens = plan.split_tokens; p.n_split = plan.n_split;
   size_t lds = 0;
-  const bool mfma = attend_mfma_plan(a.D, a.dv, p.nsk, p.rows, &p.R, &lds);
+  const bool mfma = path == VQ_PATH_LUT_MFMA && attend_mfma_plan(a.D, a.dv, p.nsk, p.rows, &p.R, &lds);
   if (!mfma) p.R = attend_pick_rows(p.rows, p.nsk, p.n_c, p.dv, p.nsv, a.D, &lds);
   if (p.R == 0) return hipErrorInvalidValue;
   p.n_rgroups = (p.rows + p.R - 1) / p.R;

@@ -209,6 +209,9 @@ __device__ __forceinline__ int unit_len(const StreamParams& p, const int* lens, 
   return hi3 > lo0 ? hi3 - lo0 : 0;
 }
 
+// BITS: width of the key and value codes, 8 (one per byte) or 4 (two per
+// byte, the even sub-vector in the low nibble).
+template <int BITS>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_stream_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ k_codes,
     const float* __restrict__ k_codebook, const float* __restrict__ smooth,
@@ -216,6 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const int32_t* __restrict__ kv_lens, int* __restrict__ header, float* __restrict__ part,
     StreamParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
+  constexpr uint32_t kKRow = 16 * BITS / 8, kVRow = 32 * BITS / 8;  // code bytes per token
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -474,21 +478,30 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // keys at or past S_cap return zeros (those keys are always masked)
     const size_t row_tok = (size_t)bg * p.S_cap;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(k_codes + row_tok * 16), (short)0, p.S_cap * 16, kBufWord3);
+        const_cast<uint8_t*>(k_codes + row_tok * kKRow), (short)0, p.S_cap * kKRow, kBufWord3);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(v_codes + row_tok * 32), (short)0, p.S_cap * 32, kBufWord3);
+        const_cast<uint8_t*>(v_codes + row_tok * kVRow), (short)0, p.S_cap * kVRow, kBufWord3);
 
-    // codes of one block: the lane's key (16 bytes) and, for the value
-    // MFMA, the code pairs (2n, 2n+1) of keys 4 j + g, j = 0..15, kept as
-    // loaded (one per register) so that the prefetch of the next block is
-    // not waited for until that block is processed.  Load j of the wave
-    // reads keys 4 j .. 4 j + 3: one contiguous 128-byte span.
+    // codes of one block: the lane's key (16 bytes; 8 with 4-bit codes) and,
+    // for the value MFMA, the codes of sub-vectors (2n, 2n+1) of keys
+    // 4 j + g, j = 0..15 (two bytes; one with 4-bit codes), kept as loaded
+    // (one per register) so that the prefetch of the next block is not
+    // waited for until that block is processed.  Load j of the wave reads
+    // keys 4 j .. 4 j + 3: one contiguous span.
     auto load_codes = [&](int tb, uint4& kc, uint32_t (&vr)[16]) {
-      const u32x4_t k4 = __builtin_amdgcn_raw_buffer_load_b128(krs, (uint32_t)(tb + lane) * 16u, 0, 0);
-      kc = make_uint4(k4[0], k4[1], k4[2], k4[3]);
-      const uint32_t vo = (uint32_t)(tb + grp16) * 32u + 2u * (uint32_t)(lane & 15);
+      if constexpr (BITS == 8) {
+        const u32x4_t k4 = __builtin_amdgcn_raw_buffer_load_b128(krs, (uint32_t)(tb + lane) * 16u, 0, 0);
+        kc = make_uint4(k4[0], k4[1], k4[2], k4[3]);
+        const uint32_t vo = (uint32_t)(tb + grp16) * 32u + 2u * (uint32_t)(lane & 15);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) vr[k] = __builtin_amdgcn_raw_buffer_load_b16(vrs, vo + 128u * k, 0, 0);
+        for (int k = 0; k < 16; ++k) vr[k] = __builtin_amdgcn_raw_buffer_load_b16(vrs, vo + 128u * k, 0, 0);
+      } else {
+        const u32x2_t k2 = __builtin_amdgcn_raw_buffer_load_b64(krs, (uint32_t)(tb + lane) * 8u, 0, 0);
+        kc = make_uint4(k2[0], k2[1], 0u, 0u);
+        const uint32_t vo = (uint32_t)(tb + grp16) * 16u + (uint32_t)(lane & 15);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) vr[k] = __builtin_amdgcn_raw_buffer_load_b8(vrs, vo + 64u * k, 0, 0);
+      }
     };
 
     // Blocks of the segment are t0 + 64 n.  Wave w takes blocks w and
@@ -606,7 +619,19 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       {
         // dw[a] = kw[(a + rdw) mod 4]: rotate by rdw bit 0, then by bit 1,
         // with bit selects (no divergent branches)
-        const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+        uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+        if constexpr (BITS == 4) {
+          // nibbles to bytes: word d of the key holds sub-vectors 8 d .. 8 d + 7
+          // (the even one of each pair in the low nibble); kw[2 d + h] gets
+          // sub-vectors 8 d + 4 h .. 8 d + 4 h + 3, one per byte
+#pragma unroll
+          for (int d2 = 1; d2 >= 0; --d2) {
+            const uint32_t w = d2 ? kc.y : kc.x;
+            const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+            kw[2 * d2] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+            kw[2 * d2 + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+          }
+        }
         uint32_t r1[4], dw[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) r1[a] = (kw[(a + 1) & 3] & rot1) | (kw[a] & ~rot1);
@@ -697,7 +722,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         // [code(key 0, 2n), code(key 0, 2n+1), code(key 1, 2n), code(key 1, 2n+1)]
-        const uint32_t w = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x05040100u);
+        uint32_t w;
+        if constexpr (BITS == 8) {
+          w = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x05040100u);
+        } else {
+          // [key 0 byte, key 1 byte] -> [key 0 lo, key 0 hi, key 1 lo, key 1 hi]
+          const uint32_t x = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x0c0c0400u);
+          w = __builtin_amdgcn_perm((x >> 4) & 0x0f0fu, x & 0x0f0fu, 0x05010400u);
+        }
         vg[k][0] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020400u));
         vg[k][1] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020600u));
         vg[k][2] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020500u));
@@ -893,10 +925,11 @@ hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds
   const size_t header_bytes = ((size_t)sp.U * 8 + 255) / 256 * 256;
   int* header = reinterpret_cast<int*>(a.partials);
   float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.partials) + header_bytes);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attend_stream_kernel),
+  auto kern = a.code_bits == 4 ? attend_stream_kernel<4> : attend_stream_kernel<8>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_stream_kernel, dim3(grid), dim3(kThreads), lds, st, a.q, a.k_codes,
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, a.q, a.k_codes,
                      a.k_codebook, a.smooth, a.v_codes, a.v_codebook, a.kv_lens, header, part, sp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -173,6 +173,7 @@ __device__ __forceinline__ void wht(float (&x)[DS], int j) {
 struct Dims {
   int B, H, S, n_c, smooth_rows, transform, S_cap, S_off, use_row_offsets, recon_dtype;
   FastDiv div_S, div_H;  // by S and H (token-head indices below 2^31)
+  int code_bits;         // 8, or 4: two codes per byte, the even sub-vector in the low nibble
 };
 
 // MODE 0: encode; 1: encode + reconstruct; 2: decode (codes_in -> recon).
@@ -284,12 +285,29 @@ __device__ __forceinline__ void pvq_body(
         if (s_best[o] < best) { best = s_best[o]; idx = s_idx[o]; }
       }
     }
+    // 4-bit codes: the even sub-vector's lane packs its odd neighbour's
+    // code (lane + 1, the same token-head) into the high nibble
+    const int idx_next = __shfl_down(idx, 1);
     if (valid) {
       const int off = d.use_row_offsets ? offs.v[b] : d.S_off;
-      codes[(bh * d.S_cap + off + t) * NSUB + j] = (uint8_t)idx;
+      if (d.code_bits == 4) {
+        if (!(j & 1))
+          codes[(bh * d.S_cap + off + t) * (NSUB / 2) + j / 2] = (uint8_t)((idx & 15) | ((idx_next & 15) << 4));
+      } else {
+        codes[(bh * d.S_cap + off + t) * NSUB + j] = (uint8_t)idx;
+      }
     }
   } else {
-    if (valid) idx = min((int)codes_in[(bh * d.S_cap + d.S_off + t) * NSUB + j], d.n_c - 1);
+    if (valid) {
+      int c;
+      if (d.code_bits == 4) {
+        const int byte = codes_in[(bh * d.S_cap + d.S_off + t) * (NSUB / 2) + j / 2];
+        c = (j & 1) ? byte >> 4 : byte & 15;
+      } else {
+        c = codes_in[(bh * d.S_cap + d.S_off + t) * NSUB + j];
+      }
+      idx = min(c, d.n_c - 1);
+    }
   }
 
   if constexpr (MODE != 0) {
@@ -975,7 +993,8 @@ void launch_one(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStre
 
 Dims make_dims(const EncodeArgs& a) {
   return Dims{a.B, a.H, a.S, a.n_c, a.smooth_rows, a.transform, a.S_cap, a.S_off,
-              a.use_row_offsets, a.recon_dtype, make_fastdiv((uint32_t)a.S), make_fastdiv((uint32_t)a.H)};
+              a.use_row_offsets, a.recon_dtype, make_fastdiv((uint32_t)a.S), make_fastdiv((uint32_t)a.H),
+              a.code_bits};
 }
 
 // Fewer lanes than about four waves per CU (256 CUs): split the codebook
@@ -996,9 +1015,11 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
   RowOffsets o{};
   if (offs) o = *offs;
   const int split = codebook_split(a);
-  // Enough sub-vectors to fill the chip: nearest centroid on the matrix cores.
+  // Enough sub-vectors to fill the chip: nearest centroid on the matrix cores
+  // (8-bit codes; a 4-bit codebook has at most 16 centroids, a short search
+  // for the per-lane kernel).
   if constexpr (DS % 4 == 0) {
-    if (split == 1 && mode != 2 && n_th < (1LL << 31)) {
+    if (split == 1 && mode != 2 && a.code_bits == 8 && n_th < (1LL << 31)) {
       if (mode == 0) launch_mfma<D, DS, 0>(a, d, o, st);
       else launch_mfma<D, DS, 1>(a, d, o, st);
       return hipGetLastError();

@@ -32,6 +32,7 @@ struct EncodeArgs {
   void* recon;             // NULL or [B, H, S, D]
   int B, H, S, D, n_c, sub_dim, smooth_rows, transform;
   int S_cap, S_off, use_row_offsets, recon_dtype;  // recon_dtype 0 fp32, 1 fp16
+  int code_bits;           // 8: one code per byte; 4: two per byte (low nibble first)
 };
 
 // mode 0 = encode, 1 = encode + reconstruct, 2 = decode only.
@@ -54,6 +55,7 @@ struct AttendArgs {
   int B, Hq, Sq, D, Hkv, S_cap, dk, dv, n_c, smooth_rows, transform;
   float scale_log2e;
   int causal, window;
+  int code_bits;            // 8 or 4 (two codes per byte, low nibble first)
 };
 
 struct AttendPlan {
@@ -68,7 +70,7 @@ struct AttendPlan {
 
 // Kernel-side parameters of one attention launch (by value).
 struct AttParams {
-  int B, Hq, Sq, Hkv, S_cap, dk, dv, n_c, nsk, nsv, smooth_rows, transform;
+  int B, Hq, Sq, Hkv, S_cap, dk, dv, n_c, nsk, nsv, smooth_rows, transform, code_bits;
   float fold;  // WHT normalization (if any) * scale * log2(e)
   int causal, window;
   int G, rows, R, n_rgroups, split_tokens, n_split;
@@ -118,7 +120,7 @@ hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds
 
 // The VQ_PATH_* family launch_attend uses for a validated shape (0 if none).
 int attend_path(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, int dk, int dv,
-                int n_c);
+                int n_c, int code_bits);
 
 // Many-query kernel (prefill: at least 64 query rows per kv head; head dim
 // 128, key sub_dim 8, value sub_dim 4).

@@ -129,27 +129,31 @@ def decode(S_kv: int):
                 smooth=s, scale=1.0 / math.sqrt(D), causal=True, window=0)
 
 
-def gqa_long(window: int = 0, k_codebook=None, smooth=None, B: int = 16):
+def gqa_long(window: int = 0, k_codebook=None, smooth=None, B: int = 16, code_bits: int = 8):
     """Batched long-context GQA decode: H_q=32, H_kv=8, S_cap=32768, ragged.
 
     The key codebook and smooth factors are those of the encode workload
     when passed in; otherwise N(0, 1) rows and the encode recipe's smooth
-    factors drawn here.
+    factors drawn here.  code_bits=4 draws 16-centroid codebooks and code
+    rows of half the bytes: uniform random bytes, i.e. two independent
+    uniform 4-bit codes per byte.
     """
-    rng = np.random.default_rng(SEEDS["gqa_long"])
+    rng = np.random.default_rng(SEEDS["gqa_long"] + (0 if code_bits == 8 else 1000))
     Hq, Hkv, D, dk, dv, S_cap = 32, 8, 128, 8, 4, 32768
+    n_c = N_CENTROIDS if code_bits == 8 else 16
     lens = ragged_lengths(rng, 16, 16384, 32768)[:B]
     if smooth is None:
         smooth = smooth_factors(outlier_normal(rng, (1, Hkv, 8192, D), 4))
     if k_codebook is None:
-        k_codebook = normal_codebook(rng, N_CENTROIDS, dk)
-    return dict(name=f"gqa_long_W{window}", B=B, H_q=Hq, H_kv=Hkv, S_q=1, D=D, dk=dk, dv=dv,
-                S_cap=S_cap, kv_lens=lens,
+        k_codebook = normal_codebook(rng, n_c, dk)
+    rb = lambda n_sub: n_sub * code_bits // 8
+    return dict(name=f"gqa_long_W{window}" + ("" if code_bits == 8 else "_4bit"), B=B, H_q=Hq,
+                H_kv=Hkv, S_q=1, D=D, dk=dk, dv=dv, S_cap=S_cap, kv_lens=lens, code_bits=code_bits,
                 q=normal_fp16(rng, (B, Hq, 1, D)),
-                k_codes=uniform_codes(rng, (B, Hkv, S_cap, D // dk)),
-                v_codes=uniform_codes(rng, (B, Hkv, S_cap, D // dv)),
+                k_codes=uniform_codes(rng, (B, Hkv, S_cap, rb(D // dk))),
+                v_codes=uniform_codes(rng, (B, Hkv, S_cap, rb(D // dv))),
                 k_codebook=np.asarray(k_codebook, dtype=np.float32),
-                v_codebook=normal_codebook(rng, N_CENTROIDS, dv),
+                v_codebook=normal_codebook(rng, n_c, dv),
                 smooth=np.asarray(smooth, dtype=np.float32),
                 scale=1.0 / math.sqrt(D), causal=True, window=window)
 
