@@ -31,7 +31,17 @@
  *     Its entries must be finite and nonzero; they are not inspected.
  *   - transform = 1 applies the normalized Sylvester Walsh-Hadamard matrix
  *     H[i][k] = (-1)^popcount(i & k) / sqrt(D) (symmetric, its own inverse);
- *     transform = 0 applies none (the value path).
+ *     transform = 0 applies none (the value path); transform = 2 applies an
+ *     explicit invertible matrix M (the H_mat [D, D] argument of
+ *     vecinfer_encode_decode_metal, "Metal Kernels API", "VecInfer
+ *     kernels"), given by the arguments mat = M and mat_inv = M^-1, both
+ *     fp32 [D, D] row-major device arrays (head dims up to 128): encode
+ *     rotates a row vector as x . M, decode as x~ . M^-1, and the query's
+ *     dual transform is (q * s) . (M^-1)^T.  An entry point reads only the
+ *     matrices its steps use (encode: mat; decode: mat_inv; attention:
+ *     mat_inv); the others may be NULL, and both are ignored unless
+ *     transform = 2.  The matrices are not inspected: mat_inv must be the
+ *     inverse of mat.
  *   - A randomized Hadamard rotation M = diag(sigma) . H, sigma in {-1, +1}^D
  *     (an orthonormal choice of the fused encode-decode kernel's H_mat,
  *     "Metal Kernels API", "VecInfer kernels"), is given as transform = 1
@@ -107,7 +117,7 @@ int vq_supports_shape(int n_centroids, int n_sub, int head_dim);
  *   keys_f16    [B, H, S, D] fp16
  *   codebook    [n_centroids, sub_dim] fp32
  *   smooth      NULL or [smooth_rows, D] fp32 (see conventions)
- *   transform   0 or 1
+ *   transform   0, 1 or 2; mat, mat_inv as in the conventions
  *   code_bits   8 or 4 (see conventions)
  *   codes       [B, H, S_cap, row_bytes] uint8; token t of row b is
  *               written to slot off_b + t, off_b = row_offsets[b] if
@@ -125,6 +135,7 @@ int vq_supports_shape(int n_centroids, int n_sub, int head_dim);
 int vq_encode(const void* keys_f16, int B, int H, int S, int D,
               const float* codebook, int n_centroids, int sub_dim, int code_bits,
               const float* smooth, int smooth_rows, int transform,
+              const float* mat, const float* mat_inv,
               uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets,
               void* stream);
 
@@ -149,6 +160,7 @@ int vq_encode(const void* keys_f16, int B, int H, int S, int D,
 int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int S, int D,
                  const float* k_codebook, int k_n_centroids, int k_sub_dim,
                  const float* smooth, int smooth_rows, int transform,
+                 const float* mat, const float* mat_inv,
                  const float* v_codebook, int v_n_centroids, int v_sub_dim, int code_bits,
                  uint8_t* k_codes, uint8_t* v_codes, int S_cap, int S_off,
                  const int32_t* row_offsets, void* stream);
@@ -167,7 +179,8 @@ int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int
  */
 int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
               const float* codebook, int n_centroids, int sub_dim, int code_bits,
-              const float* smooth, int smooth_rows, int transform, int D,
+              const float* smooth, int smooth_rows, int transform,
+              const float* mat, const float* mat_inv, int D,
               void* out, int out_dtype, void* stream);
 
 /*
@@ -182,6 +195,7 @@ int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
 int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D,
                      const float* codebook, int n_centroids, int sub_dim, int code_bits,
                      const float* smooth, int smooth_rows, int transform,
+                     const float* mat, const float* mat_inv,
                      uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets,
                      void* recon, int out_dtype, void* stream);
 
@@ -208,7 +222,8 @@ enum {
  * computes the same attention.  Host-only; needs no device.
  */
 int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
-                   int n_centroids, int code_bits, int H_kv, int S_cap, int sliding_window);
+                   int n_centroids, int code_bits, int transform, int H_kv, int S_cap,
+                   int sliding_window);
 
 /*
  * Fused attention read directly from key and value codes ("Metal Kernels
@@ -229,7 +244,9 @@ int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
  *   k_codes     [B, H_kv, S_cap, row bytes] uint8 (code_bits wide codes)
  *   k_codebook  [n_centroids, k_sub_dim] fp32
  *   smooth      NULL or [smooth_rows, D] fp32 smooth factors of the keys
- *               (smooth_rows 1 or H_kv); transform as for vq_encode
+ *               (smooth_rows 1 or H_kv); transform (and mat_inv) as for
+ *               vq_encode; with transform = 2 the dual transform of the
+ *               query rows is computed first into the workspace
  *   v_codes     [B, H_kv, S_cap, row bytes] uint8 (no smooth, no rotation)
  *   code_bits   8 or 4, the width of both the key and the value codes; 4-bit
  *               codes need n_centroids <= 16 and numbers of key and value
@@ -251,6 +268,7 @@ int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
 int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D,
               const uint8_t* k_codes, const float* k_codebook, int k_sub_dim,
               const float* smooth, int smooth_rows, int transform,
+              const float* mat, const float* mat_inv,
               const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
               int n_centroids, int code_bits, int H_kv, int S_cap, const int32_t* kv_lens,
               float scale, int causal, int sliding_window,
@@ -282,6 +300,7 @@ int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D,
 int vq_attend_noalloc(const void* q_f16, int B, int H_q, int S_q, int D,
                       const uint8_t* k_codes, const float* k_codebook, int k_sub_dim,
                       const float* smooth, int smooth_rows, int transform,
+                      const float* mat, const float* mat_inv,
                       const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
                       int n_centroids, int code_bits, int H_kv, int S_cap, const int32_t* kv_lens,
                       float scale, int causal, int sliding_window,

@@ -64,9 +64,9 @@ def test_supports_shape(lib, n_c, n_sub, D, ok):
 
 
 def enc(lib, B=1, H=2, S=8, D=64, n_c=256, dsub=4, smooth=P, srows=2, transform=1, S_cap=8,
-        S_off=0, offs=None, keys=P, cb=P, codes=P, bits=8):
-    return lib.vq_encode(keys, B, H, S, D, cb, n_c, dsub, bits, smooth, srows, transform, codes, S_cap,
-                         S_off, offs, None)
+        S_off=0, offs=None, keys=P, cb=P, codes=P, bits=8, mat=None, mat_inv=None):
+    return lib.vq_encode(keys, B, H, S, D, cb, n_c, dsub, bits, smooth, srows, transform, mat, mat_inv,
+                         codes, S_cap, S_off, offs, None)
 
 
 def test_encode_validation(lib):
@@ -76,7 +76,11 @@ def test_encode_validation(lib):
     assert enc(lib, n_c=300) == INVALID                 # does not fit uint8
     assert enc(lib, n_c=0) == INVALID
     assert enc(lib, srows=3) == INVALID                 # smooth rows not 1 or H
-    assert enc(lib, transform=2) == INVALID
+    assert enc(lib, transform=3) == INVALID
+    assert enc(lib, transform=2) == INVALID            # the matrix is missing
+    assert b"mat" in lib.vq_last_error()
+    assert enc(lib, transform=2, mat=P, D=256, dsub=8, S=0) == UNSUPPORTED   # head dim above 128
+    assert enc(lib, transform=2, mat=P, S=0) == OK
     assert enc(lib, S_off=4) == INVALID                 # 4 + 8 > 8
     assert enc(lib, S_off=-1) == INVALID
     assert enc(lib, H=0) == INVALID
@@ -96,24 +100,29 @@ def test_encode_validation(lib):
 
 
 def test_decode_and_encode_decode_validation(lib):
-    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, 8, P, 2, 1, P, 8, 0, None, None, 1, None)
+    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, 8, P, 2, 1, None, None, P, 8, 0, None, None, 1,
+                              None)
     assert st == INVALID                                # recon NULL
-    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, 8, P, 2, 1, P, 8, 0, None, P, 7, None)
+    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, 8, P, 2, 1, None, None, P, 8, 0, None, P, 7, None)
     assert st == INVALID                                # out_dtype
-    st = lib.vq_decode(P, 1, 2, 8, 8, 1, P, 256, 4, 8, None, 1, 1, 64, P, 0, None)
+    st = lib.vq_encode_decode(P, 1, 2, 8, 64, P, 256, 4, 8, P, 2, 2, P, None, P, 8, 0, None, P, 1, None)
+    assert st == INVALID                                # transform 2 needs mat_inv for the recon
+    st = lib.vq_decode(P, 1, 2, 8, 8, 1, P, 256, 4, 8, None, 1, 1, None, None, 64, P, 0, None)
     assert st == INVALID                                # slots [1, 9) outside [0, 8)
-    st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 256, 4, 8, None, 1, 1, 48, P, 0, None)
+    st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 256, 4, 8, None, 1, 1, None, None, 48, P, 0, None)
     assert st == UNSUPPORTED                            # D = 48
-    st = lib.vq_decode(None, 1, 2, 8, 8, 0, P, 256, 4, 8, None, 1, 1, 64, P, 0, None)
+    st = lib.vq_decode(None, 1, 2, 8, 8, 0, P, 256, 4, 8, None, 1, 1, None, None, 64, P, 0, None)
     assert st == INVALID
-    st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 32, 4, 4, None, 1, 1, 64, P, 0, None)
+    st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 32, 4, 4, None, 1, 1, None, None, 64, P, 0, None)
     assert st == INVALID                                # 4-bit codes, 32 centroids
+    st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 256, 4, 8, None, 1, 2, P, None, 64, P, 0, None)
+    assert st == INVALID                                # decode reads mat_inv
 
 
 def enc_kv(lib, B=1, H=2, S=8, D=128, dk=8, dv=4, nk=256, nv=256, S_cap=8, S_off=0, offs=None,
            keys=P, values=P, kcb=P, vcb=P, kc=P, vc=P, smooth=P, srows=2, transform=1, bits=8):
-    return lib.vq_encode_kv(keys, values, B, H, S, D, kcb, nk, dk, smooth, srows, transform, vcb, nv,
-                            dv, bits, kc, vc, S_cap, S_off, offs, None)
+    return lib.vq_encode_kv(keys, values, B, H, S, D, kcb, nk, dk, smooth, srows, transform, None, None,
+                            vcb, nv, dv, bits, kc, vc, S_cap, S_off, offs, None)
 
 
 def test_encode_kv_validation(lib):
@@ -134,9 +143,10 @@ def test_encode_kv_validation(lib):
 
 
 def att(lib, B=2, Hq=8, Sq=1, D=128, dk=8, dv=4, n_c=256, Hkv=2, S_cap=64, W=0, causal=1,
-        ws=P, ws_bytes=1 << 30, smooth=P, srows=2, scale=0.1, q=P, bits=8):
-    return lib.vq_attend(q, B, Hq, Sq, D, P, P, dk, smooth, srows, 1, P, P, dv, n_c, bits, Hkv, S_cap,
-                         None, scale, causal, W, P, ws, ws_bytes, None)
+        ws=P, ws_bytes=1 << 30, smooth=P, srows=2, scale=0.1, q=P, bits=8, transform=1, mat=None,
+        mat_inv=None):
+    return lib.vq_attend(q, B, Hq, Sq, D, P, P, dk, smooth, srows, transform, mat, mat_inv, P, P, dv, n_c,
+                         bits, Hkv, S_cap, None, scale, causal, W, P, ws, ws_bytes, None)
 
 
 def test_attend_validation(lib):
@@ -155,6 +165,8 @@ def test_attend_validation(lib):
     assert att(lib, B=0) == OK
     assert att(lib, bits=4) == INVALID                   # 256 centroids in 4 bits
     assert att(lib, bits=4, n_c=16, D=64, dk=16) == INVALID   # 4 key sub-vectors: not a multiple of 8
+    assert att(lib, transform=2, mat=P) == INVALID       # the query needs mat_inv
+    assert att(lib, transform=2, mat_inv=P, B=0) == OK
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="a device is visible")
@@ -175,9 +187,12 @@ def test_workspace_bytes(lib):
     # (128 + 2) floats per (chunk, unit) pair, 4096 chunks + 128 units here
     assert a >= (4096 + 16 * 8) * 4 * (128 + 2) * 4
     assert a == f(16, 32, 1, 128, 8, 32768, 0)            # a pure function of the shape
-    # other head dims: (D + 2) floats per split partial, rows rounded up to 8
+    # other head dims: (D + 2) floats per split partial, rows rounded up to 8,
+    # then (256-byte aligned) the fp32 query rows an explicit transform matrix uses
     c = f(16, 32, 1, 64, 8, 32768, 0)
-    assert c > 0 and c % ((64 + 2) * 4 * 16 * 8 * 8) == 0
+    q_rows = 16 * 32 * 1 * 64 * 4
+    assert c > q_rows and (c - q_rows) % 256 == 0
+    assert (c - q_rows) >= (64 + 2) * 4 * 16 * 8 * 8
 
 
 def test_binding_rejects_host_tensors(lib):
@@ -222,7 +237,12 @@ def test_attend_path_rejects_what_attend_rejects(lib):
         api.vq_attend_path(1, 8, 1, 128, 6, 4, 256, 8, 100)      # D % d_k != 0
     with pytest.raises(api.VQError):
         api.vq_attend_path(1, 8, 1, 128, 8, 4, 257, 8, 100)      # more than 256 centroids
-    assert lib.vq_attend_path(0, 8, 1, 128, 8, 4, 256, 8, 8, 100, 0) == 0
+    assert lib.vq_attend_path(0, 8, 1, 128, 8, 4, 256, 8, 1, 8, 100, 0) == 0
+    # explicit transform matrices: the streaming and per-unit VALU kernels only
+    assert api.vq_attend_path(4, 8, 512, 128, 8, 4, 256, 8, 32768, transform=2) == "lut_valu"
+    assert api.vq_attend_path(16, 32, 1, 128, 8, 4, 256, 8, 32768, transform=2) == "stream"
+    with pytest.raises(api.VQError):
+        api.vq_attend_path(1, 8, 1, 256, 8, 4, 256, 8, 300, transform=2)
     with pytest.raises(api.VQError):
         api.vq_attend_path(1, 8, 1, 128, 8, 4, 17, 8, 100, code_bits=4)    # 17 centroids in 4 bits
 
@@ -284,12 +304,13 @@ def test_attend_noalloc_validation(lib):
     """vq_attend_noalloc validates like vq_attend, and rejects shapes whose
     partials exceed its device scratch array before touching a device."""
     f = lib.vq_attend_noalloc
-    args = lambda B=2, Hq=8, Sq=1, q=P: (q, B, Hq, Sq, 128, P, P, 8, P, 2, 1, P, P, 4, 256, 8, 2, 64,
-                                         None, 0.1, 1, 0, P, None)
+    args = lambda B=2, Hq=8, Sq=1, q=P: (q, B, Hq, Sq, 128, P, P, 8, P, 2, 1, None, None, P, P, 4, 256, 8,
+                                         2, 64, None, 0.1, 1, 0, P, None)
     assert f(*args(q=None)) == INVALID
     assert f(*args(Hq=7)) == INVALID                     # H_q % H_kv
     assert f(*args(B=0)) == OK
-    st = f(P, 4, 8, 512, 128, P, P, 8, P, 8, 1, P, P, 4, 256, 8, 8, 32768, None, 0.1, 1, 0, P, None)
+    st = f(P, 4, 8, 512, 128, P, P, 8, P, 8, 1, None, None, P, P, 4, 256, 8, 8, 32768, None, 0.1, 1, 0, P,
+           None)
     assert st == WORKSPACE and b"scratch" in lib.vq_last_error()
     if not torch.cuda.is_available():
         assert f(*args()) == NO_DEVICE

@@ -16,36 +16,36 @@ SIGNATURES = {
     "vq_supports_shape": (c_int, [c_int, c_int, c_int]),
     "vq_encode": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
                           c_void_p, c_int, c_int, c_int,
-                          c_void_p, c_int, c_int,
+                          c_void_p, c_int, c_int, c_void_p, c_void_p,
                           c_void_p, c_int, c_int, c_void_p,
                           c_void_p]),
     "vq_encode_kv": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                              c_void_p, c_int, c_int,
-                             c_void_p, c_int, c_int,
+                             c_void_p, c_int, c_int, c_void_p, c_void_p,
                              c_void_p, c_int, c_int, c_int,
                              c_void_p, c_void_p, c_int, c_int, c_void_p,
                              c_void_p]),
     "vq_decode": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int,
                           c_void_p, c_int, c_int, c_int,
-                          c_void_p, c_int, c_int, c_int,
+                          c_void_p, c_int, c_int, c_void_p, c_void_p, c_int,
                           c_void_p, c_int, c_void_p]),
     "vq_encode_decode": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
                                  c_void_p, c_int, c_int, c_int,
-                                 c_void_p, c_int, c_int,
+                                 c_void_p, c_int, c_int, c_void_p, c_void_p,
                                  c_void_p, c_int, c_int, c_void_p,
                                  c_void_p, c_int, c_void_p]),
     "vq_attend_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
-    "vq_attend_path": (c_int, [c_int] * 11),
+    "vq_attend_path": (c_int, [c_int] * 12),
     "vq_attend": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
                           c_void_p, c_void_p, c_int,
-                          c_void_p, c_int, c_int,
+                          c_void_p, c_int, c_int, c_void_p, c_void_p,
                           c_void_p, c_void_p, c_int,
                           c_int, c_int, c_int, c_int, c_void_p,
                           c_float, c_int, c_int,
                           c_void_p, c_void_p, c_size_t, c_void_p]),
     "vq_attend_noalloc": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
                                   c_void_p, c_void_p, c_int,
-                                  c_void_p, c_int, c_int,
+                                  c_void_p, c_int, c_int, c_void_p, c_void_p,
                                   c_void_p, c_void_p, c_int,
                                   c_int, c_int, c_int, c_int, c_void_p,
                                   c_float, c_int, c_int,

@@ -126,12 +126,27 @@ def _row_bytes(n_sub, code_bits):
     raise ValueError(f"code_bits must be 8 or 4, got {code_bits}")
 
 
+def _transform(transform, mat, mat_inv, D):
+    """(code, mat, mat_inv): transform False/0 -> none, True/1 -> the
+    normalized Sylvester Walsh-Hadamard matrix, 2 (or any matrix given) ->
+    the explicit [D, D] fp32 matrices mat = M and mat_inv = M^-1."""
+    if mat is None and mat_inv is None:
+        if transform == 2:
+            raise ValueError("transform 2 needs mat and/or mat_inv")
+        return int(bool(transform)), None, None
+    for name, m in (("mat", mat), ("mat_inv", mat_inv)):
+        if m is not None:
+            _need(m, name, torch.float32, shape=(D, D))
+    return 2, mat, mat_inv
+
+
 def vq_supports_shape(n_centroids: int, n_sub: int, head_dim: int) -> bool:
     return bool(_lib.load().vq_supports_shape(n_centroids, n_sub, head_dim))
 
 
 def vq_encode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=None,
-              S_cap=None, S_off=0, row_offsets=None, code_bits=8, stream=None, prepare=False):
+              S_cap=None, S_off=0, row_offsets=None, code_bits=8, mat=None, mat_inv=None,
+              stream=None, prepare=False):
     """Encode fp16 keys [B, H, S, D] into uint8 codes [B, H, S_cap, row_bytes]
     (row_bytes = D // sub_dim, or half that with code_bits=4: two codes per
     byte, the even sub-vector in the low nibble).
@@ -147,15 +162,17 @@ def vq_encode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=Non
     _need(codes, "codes", torch.uint8, shape=(B, H, S_cap, nb))
     sm, rows = _smooth(smooth, D, H)
     offs = _offsets(row_offsets, B)
-    _on_device(keys=keys, codebook=codebook, codes=codes, smooth=sm)
+    tr, m, mi = _transform(transform, mat, mat_inv, D)
+    _on_device(keys=keys, codebook=codebook, codes=codes, smooth=sm, mat=m, mat_inv=mi)
     return _call("vq_encode", _ptr(keys), B, H, S, D, _ptr(codebook), codebook.shape[0], sub_dim,
-                 code_bits, _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off, offs,
+                 code_bits, _ptr(sm), rows, tr, _ptr(m), _ptr(mi), _ptr(codes), codes.shape[2], S_off, offs,
                  _stream(stream), prepare=prepare, result=codes)
 
 
 def vq_encode_kv(keys, values, k_codebook, k_sub_dim, v_codebook, v_sub_dim, *, smooth=None,
                  transform=True, k_codes=None, v_codes=None, S_cap=None, S_off=0,
-                 row_offsets=None, code_bits=8, stream=None, prepare=False):
+                 row_offsets=None, code_bits=8, mat=None, mat_inv=None, stream=None,
+                 prepare=False):
     """Encode the keys (smoothed, rotated) and the values (neither) of one
     append into their code buffers; returns (k_codes, v_codes)."""
     _need(keys, "keys", torch.float16, 4)
@@ -173,10 +190,11 @@ def vq_encode_kv(keys, values, k_codebook, k_sub_dim, v_codebook, v_sub_dim, *, 
     _need(v_codes, "v_codes", torch.uint8, shape=(B, H, k_codes.shape[2], nv))
     sm, rows = _smooth(smooth, D, H)
     offs = _offsets(row_offsets, B)
+    tr, m, mi = _transform(transform, mat, mat_inv, D)
     _on_device(keys=keys, values=values, k_codebook=k_codebook, v_codebook=v_codebook,
-               k_codes=k_codes, v_codes=v_codes, smooth=sm)
+               k_codes=k_codes, v_codes=v_codes, smooth=sm, mat=m, mat_inv=mi)
     return _call("vq_encode_kv", _ptr(keys), _ptr(values), B, H, S, D, _ptr(k_codebook),
-                 k_codebook.shape[0], k_sub_dim, _ptr(sm), rows, int(bool(transform)),
+                 k_codebook.shape[0], k_sub_dim, _ptr(sm), rows, tr, _ptr(m), _ptr(mi),
                  _ptr(v_codebook), v_codebook.shape[0], v_sub_dim, code_bits, _ptr(k_codes), _ptr(v_codes),
                  k_codes.shape[2], S_off, offs, _stream(stream), prepare=prepare,
                  result=(k_codes, v_codes))
@@ -184,7 +202,8 @@ def vq_encode_kv(keys, values, k_codebook, k_sub_dim, v_codebook, v_sub_dim, *, 
 
 def vq_encode_decode(keys, codebook, sub_dim, *, smooth=None, transform=True, codes=None,
                      S_cap=None, S_off=0, row_offsets=None, recon=None,
-                     out_dtype=torch.float16, code_bits=8, stream=None, prepare=False):
+                     out_dtype=torch.float16, code_bits=8, mat=None, mat_inv=None, stream=None,
+                     prepare=False):
     """Fused encode + reconstruction.  Returns (recon [B, H, S, D], codes)."""
     _need(keys, "keys", torch.float16, 4)
     B, H, S, D = keys.shape
@@ -198,15 +217,18 @@ def vq_encode_decode(keys, codebook, sub_dim, *, smooth=None, transform=True, co
     _need(recon, "recon", (torch.float32, torch.float16), shape=(B, H, S, D))
     sm, rows = _smooth(smooth, D, H)
     offs = _offsets(row_offsets, B)
-    _on_device(keys=keys, codebook=codebook, codes=codes, recon=recon, smooth=sm)
+    tr, m, mi = _transform(transform, mat, mat_inv, D)
+    _on_device(keys=keys, codebook=codebook, codes=codes, recon=recon, smooth=sm, mat=m,
+               mat_inv=mi)
     return _call("vq_encode_decode", _ptr(keys), B, H, S, D, _ptr(codebook), codebook.shape[0],
-                 sub_dim, code_bits, _ptr(sm), rows, int(bool(transform)), _ptr(codes), codes.shape[2], S_off,
+                 sub_dim, code_bits, _ptr(sm), rows, tr, _ptr(m), _ptr(mi), _ptr(codes), codes.shape[2], S_off,
                  offs, _ptr(recon), 1 if recon.dtype == torch.float16 else 0, _stream(stream),
                  prepare=prepare, result=(recon, codes))
 
 
 def vq_decode(codes, codebook, *, smooth=None, transform=True, S=None, S_off=0,
-              out=None, out_dtype=torch.float32, code_bits=8, stream=None, prepare=False):
+              out=None, out_dtype=torch.float32, code_bits=8, mat=None, mat_inv=None,
+              stream=None, prepare=False):
     """Decode slots [S_off, S_off + S) of codes [B, H, S_cap, row_bytes] into
     [B, H, S, n_sub * sub_dim] (fp32 by default); n_sub = row_bytes, or twice
     that with code_bits=4."""
@@ -223,9 +245,10 @@ def vq_decode(codes, codebook, *, smooth=None, transform=True, S=None, S_off=0,
         out = torch.empty((B, H, S, D), dtype=out_dtype, device=codes.device)
     _need(out, "out", (torch.float32, torch.float16), shape=(B, H, S, D))
     sm, rows = _smooth(smooth, D, H)
-    _on_device(codes=codes, codebook=codebook, out=out, smooth=sm)
+    tr, m, mi = _transform(transform, mat, mat_inv, D)
+    _on_device(codes=codes, codebook=codebook, out=out, smooth=sm, mat=m, mat_inv=mi)
     return _call("vq_decode", _ptr(codes), B, H, S, S_cap, S_off, _ptr(codebook), codebook.shape[0],
-                 sub_dim, code_bits, _ptr(sm), rows, int(bool(transform)), D, _ptr(out),
+                 sub_dim, code_bits, _ptr(sm), rows, tr, _ptr(m), _ptr(mi), D, _ptr(out),
                  1 if out.dtype == torch.float16 else 0, _stream(stream), prepare=prepare,
                  result=out)
 
@@ -238,13 +261,13 @@ PATH_NAMES = {1: "stream", 2: "tile", 3: "lut_mfma", 4: "lut_valu"}
 
 
 def vq_attend_path(B, H_q, S_q, D, k_sub_dim, v_sub_dim, n_centroids, H_kv, S_cap,
-                   sliding_window=0, code_bits=8) -> str:
+                   sliding_window=0, code_bits=8, transform=1) -> str:
     """Name of the kernel family vq_attend runs for this shape ("stream",
     "tile", "lut_mfma", "lut_valu"); raises VQError when vq_attend would
     reject the shape. Host-only."""
     lib = _lib.load()
-    p = int(lib.vq_attend_path(B, H_q, S_q, D, k_sub_dim, v_sub_dim, n_centroids, code_bits, H_kv,
-                               S_cap, sliding_window))
+    p = int(lib.vq_attend_path(B, H_q, S_q, D, k_sub_dim, v_sub_dim, n_centroids, code_bits,
+                               int(transform), H_kv, S_cap, sliding_window))
     if p not in PATH_NAMES:
         raise VQError(VQ_ERR_UNSUPPORTED, lib.vq_last_error().decode())
     return PATH_NAMES[p]
@@ -283,7 +306,7 @@ def _attend_args(q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, o
 
 def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None,
               transform=True, kv_lens=None, causal=True, sliding_window=0, out=None,
-              workspace=None, code_bits=8, stream=None, prepare=False):
+              workspace=None, code_bits=8, mat=None, mat_inv=None, stream=None, prepare=False):
     """Attention of raw fp16 queries [B, H_q, S_q, D] over key/value codes
     [B, H_kv, S_cap, row_bytes] (code_bits wide); returns fp16 [B, H_q, S_q, D]."""
     B, Hq, Sq, D, dk, dv, Hkv, S_cap, sm, rows, out = _attend_args(
@@ -291,10 +314,12 @@ def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None
     if workspace is None:
         workspace = attend_workspace(q, k_codes, sliding_window)
     _need(workspace, "workspace", None, 1)
+    tr, m, mi = _transform(transform, mat, mat_inv, D)
     _on_device(q=q, k_codes=k_codes, k_codebook=k_codebook, v_codes=v_codes,
-               v_codebook=v_codebook, kv_lens=kv_lens, out=out, workspace=workspace, smooth=sm)
+               v_codebook=v_codebook, kv_lens=kv_lens, out=out, workspace=workspace, smooth=sm,
+               mat=m, mat_inv=mi)
     return _call("vq_attend", _ptr(q), B, Hq, Sq, D, _ptr(k_codes), _ptr(k_codebook),
-                 dk, _ptr(sm), rows, int(bool(transform)), _ptr(v_codes),
+                 dk, _ptr(sm), rows, tr, _ptr(m), _ptr(mi), _ptr(v_codes),
                  _ptr(v_codebook), dv, k_codebook.shape[0], code_bits, Hkv, S_cap,
                  _ptr(kv_lens), float(scale), int(bool(causal)), int(sliding_window), _ptr(out),
                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
@@ -303,17 +328,18 @@ def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None
 
 def vq_attend_noalloc(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None,
                       transform=True, kv_lens=None, causal=True, sliding_window=0, out=None,
-                      code_bits=8, stream=None, prepare=False):
+                      code_bits=8, mat=None, mat_inv=None, stream=None, prepare=False):
     """vq_attend with the split partials in the library's per-GPU device
     scratch array instead of a workspace (no device allocation when `out` is
     given).  Calls that overlap on one GPU race; shapes needing more than
     VQ_NOALLOC_SCRATCH_BYTES of partials raise VQError."""
     B, Hq, Sq, D, dk, dv, Hkv, S_cap, sm, rows, out = _attend_args(
         q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out, code_bits)
+    tr, m, mi = _transform(transform, mat, mat_inv, D)
     _on_device(q=q, k_codes=k_codes, k_codebook=k_codebook, v_codes=v_codes,
-               v_codebook=v_codebook, kv_lens=kv_lens, out=out, smooth=sm)
+               v_codebook=v_codebook, kv_lens=kv_lens, out=out, smooth=sm, mat=m, mat_inv=mi)
     return _call("vq_attend_noalloc", _ptr(q), B, Hq, Sq, D, _ptr(k_codes), _ptr(k_codebook),
-                 dk, _ptr(sm), rows, int(bool(transform)), _ptr(v_codes),
+                 dk, _ptr(sm), rows, tr, _ptr(m), _ptr(mi), _ptr(v_codes),
                  _ptr(v_codebook), dv, k_codebook.shape[0], code_bits, Hkv, S_cap,
                  _ptr(kv_lens), float(scale), int(bool(causal)), int(sliding_window), _ptr(out),
                  _stream(stream), prepare=prepare, result=out)

@@ -57,11 +57,21 @@ int check_smooth(const char* what, const float* smooth, int smooth_rows, int H) 
   return VQ_OK;
 }
 
-int check_transform(const char* what, int transform, int D) {
-  if (transform != 0 && transform != 1)
-    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: transform must be 0 or 1 (got %d)", what, transform);
+// transform 0 (none), 1 (Sylvester Walsh-Hadamard, power-of-two D) or 2
+// (the explicit matrices; `need` bit 1: mat, bit 2: mat_inv), head dims <= 128.
+int check_transform(const char* what, int transform, int D, const float* mat, const float* mat_inv,
+                    int need) {
+  if (transform < 0 || transform > 2)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: transform must be 0, 1 or 2 (got %d)", what, transform);
   if (transform == 1 && !is_pow2(D))
     return fail(VQ_ERR_UNSUPPORTED, "%s: the Walsh-Hadamard transform needs a power-of-two D (got %d)", what, D);
+  if (transform == 2) {
+    if (D > 128)
+      return fail(VQ_ERR_UNSUPPORTED, "%s: an explicit transform matrix needs D <= 128 (got %d)", what, D);
+    if (((need & 1) && !mat) || ((need & 2) && !mat_inv))
+      return fail(VQ_ERR_INVALID_ARGUMENT, "%s: transform 2 needs the %s matrix", what,
+                  (need & 1) && !mat ? "mat" : "mat_inv");
+  }
   return VQ_OK;
 }
 
@@ -100,8 +110,8 @@ int hip_status(const char* what, hipError_t e) {
 // Shared validation of vq_encode / vq_encode_decode.
 int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
                  const float* codebook, int n_c, int sub_dim, int code_bits, const float* smooth,
-                 int smooth_rows, int transform, const uint8_t* codes, int S_cap, int S_off,
-                 const int32_t* row_offsets) {
+                 int smooth_rows, int transform, const float* mat, const float* mat_inv, int need,
+                 const uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets) {
   if (B < 0 || H <= 0 || S < 0)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0, H > 0, S >= 0 (got %d, %d, %d)", what, B, H, S);
   if (!keys || !codebook || !codes)
@@ -110,8 +120,8 @@ int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
   if (st) return st;
   if ((st = check_code_bits(what, code_bits, n_c, D / sub_dim, 2))) return st;
   if ((st = check_smooth(what, smooth, smooth_rows, H))) return st;
-  if ((st = check_transform(what, transform, D))) return st;
-  if ((st = check_aligned(what, {keys, codebook, smooth}))) return st;
+  if ((st = check_transform(what, transform, D, mat, mat_inv, need))) return st;
+  if ((st = check_aligned(what, {keys, codebook, smooth, mat, mat_inv}))) return st;
   if (S_cap <= 0) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: S_cap must be positive (got %d)", what, S_cap);
   if (row_offsets) {
     if (B > VQ_MAX_ROW_OFFSETS)
@@ -132,7 +142,8 @@ int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
 
 int run_encode(const char* what, const void* keys, const uint8_t* codes_in, int B, int H, int S,
                int D, const float* codebook, int n_c, int sub_dim, int code_bits, const float* smooth,
-               int smooth_rows, int transform, uint8_t* codes, int S_cap, int S_off,
+               int smooth_rows, int transform, const float* mat, const float* mat_inv,
+               uint8_t* codes, int S_cap, int S_off,
                const int32_t* row_offsets, void* recon, int out_dtype, int mode, void* stream) {
   if (B == 0 || S == 0) return VQ_OK;
   int st = check_device(what);
@@ -146,6 +157,7 @@ int run_encode(const char* what, const void* keys, const uint8_t* codes_in, int 
   a.recon = recon;
   a.B = B; a.H = H; a.S = S; a.D = D; a.n_c = n_c; a.sub_dim = sub_dim; a.code_bits = code_bits;
   a.smooth_rows = smooth_rows; a.transform = transform;
+  a.rot = mat; a.rot_inv = mat_inv;
   a.S_cap = S_cap; a.S_off = S_off; a.use_row_offsets = row_offsets != nullptr;
   a.recon_dtype = out_dtype;
   RowOffsets offs{};
@@ -192,7 +204,8 @@ int scratch_address(const char* what, void** out) {
 // (workspace == nullptr and noalloc) the device's scratch array.
 int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, int D,
                 const uint8_t* k_codes, const float* k_codebook, int k_sub_dim, const float* smooth,
-                int smooth_rows, int transform, const uint8_t* v_codes, const float* v_codebook,
+                int smooth_rows, int transform, const float* mat, const float* mat_inv,
+                const uint8_t* v_codes, const float* v_codebook,
                 int v_sub_dim, int n_centroids, int code_bits, int H_kv, int S_cap,
                 const int32_t* kv_lens, float scale, int causal, int sliding_window, void* out_f16,
                 void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
@@ -213,14 +226,14 @@ int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, in
   if ((st = check_code_bits(what, code_bits, n_centroids, D / k_sub_dim, 8))) return st;
   if ((st = check_code_bits(what, code_bits, n_centroids, D / v_sub_dim, 8))) return st;
   if ((st = check_smooth(what, smooth, smooth_rows, H_kv))) return st;
-  if ((st = check_transform(what, transform, D))) return st;
+  if ((st = check_transform(what, transform, D, mat, mat_inv, 2))) return st;
   if (causal != 0 && causal != 1)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1 (got %d)", what, causal);
   if (sliding_window < 0)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: sliding_window must be >= 0 (got %d)", what, sliding_window);
   if (!std::isfinite(scale)) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: scale must be finite", what);
   if ((st = check_aligned(what, {q_f16, k_codes, k_codebook, smooth, v_codes, v_codebook, kv_lens,
-                                 out_f16, workspace})))
+                                 out_f16, workspace, mat_inv})))
     return st;
   if (B == 0 || S_q == 0) return VQ_OK;
   AttendPlan plan;
@@ -250,6 +263,7 @@ int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, in
   a.B = B; a.Hq = H_q; a.Sq = S_q; a.D = D; a.Hkv = H_kv; a.S_cap = S_cap;
   a.dk = k_sub_dim; a.dv = v_sub_dim; a.n_c = n_centroids; a.code_bits = code_bits;
   a.smooth_rows = smooth_rows; a.transform = transform;
+  a.rot_inv = transform == 2 ? mat_inv : nullptr;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.causal = causal; a.window = sliding_window;
   return hip_status(what, launch_attend(a, plan, reinterpret_cast<hipStream_t>(stream)));
@@ -296,29 +310,32 @@ int vq_supports_shape(int n_centroids, int n_sub, int head_dim) {
 
 int vq_encode(const void* keys_f16, int B, int H, int S, int D, const float* codebook,
               int n_centroids, int sub_dim, int code_bits, const float* smooth, int smooth_rows,
-              int transform, uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets,
-              void* stream) {
+              int transform, const float* mat, const float* mat_inv, uint8_t* codes, int S_cap,
+              int S_off, const int32_t* row_offsets, void* stream) {
   g_last_error[0] = 0;
   int st = check_encode("vq_encode", keys_f16, B, H, S, D, codebook, n_centroids, sub_dim, code_bits,
-                        smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets);
+                        smooth, smooth_rows, transform, mat, mat_inv, 1, codes, S_cap, S_off,
+                        row_offsets);
   if (st) return st;
   return run_encode("vq_encode", keys_f16, nullptr, B, H, S, D, codebook, n_centroids, sub_dim,
-                    code_bits, smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets,
-                    nullptr, 0, 0, stream);
+                    code_bits, smooth, smooth_rows, transform, mat, mat_inv, codes, S_cap, S_off,
+                    row_offsets, nullptr, 0, 0, stream);
 }
 
 int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int S, int D,
                  const float* k_codebook, int k_n_centroids, int k_sub_dim, const float* smooth,
-                 int smooth_rows, int transform, const float* v_codebook, int v_n_centroids,
-                 int v_sub_dim, int code_bits, uint8_t* k_codes, uint8_t* v_codes, int S_cap,
-                 int S_off, const int32_t* row_offsets, void* stream) {
+                 int smooth_rows, int transform, const float* mat, const float* mat_inv,
+                 const float* v_codebook, int v_n_centroids, int v_sub_dim, int code_bits,
+                 uint8_t* k_codes, uint8_t* v_codes, int S_cap, int S_off,
+                 const int32_t* row_offsets, void* stream) {
   g_last_error[0] = 0;
   const char* what = "vq_encode_kv";
   int st = check_encode(what, keys_f16, B, H, S, D, k_codebook, k_n_centroids, k_sub_dim, code_bits,
-                        smooth, smooth_rows, transform, k_codes, S_cap, S_off, row_offsets);
+                        smooth, smooth_rows, transform, mat, mat_inv, 1, k_codes, S_cap, S_off,
+                        row_offsets);
   if (st) return st;
   if ((st = check_encode(what, values_f16, B, H, S, D, v_codebook, v_n_centroids, v_sub_dim, code_bits,
-                         nullptr, 1, 0, v_codes, S_cap, S_off, row_offsets)))
+                         nullptr, 1, 0, nullptr, nullptr, 0, v_codes, S_cap, S_off, row_offsets)))
     return st;
   if (B == 0 || S == 0) return VQ_OK;
   if ((st = check_device(what))) return st;
@@ -330,6 +347,7 @@ int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int
   k.B = B; k.H = H; k.S = S; k.D = D; k.n_c = k_n_centroids; k.sub_dim = k_sub_dim;
   k.code_bits = code_bits;
   k.smooth_rows = smooth_rows; k.transform = transform;
+  k.rot = mat; k.rot_inv = mat_inv;
   k.S_cap = S_cap; k.S_off = S_off; k.use_row_offsets = row_offsets != nullptr;
   v = k;
   v.keys = reinterpret_cast<const __half*>(values_f16);
@@ -337,6 +355,7 @@ int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int
   v.smooth = nullptr;
   v.smooth_rows = 1;
   v.transform = 0;
+  v.rot = v.rot_inv = nullptr;
   v.codes = v_codes;
   v.n_c = v_n_centroids;
   v.sub_dim = v_sub_dim;
@@ -349,25 +368,27 @@ int vq_encode_kv(const void* keys_f16, const void* values_f16, int B, int H, int
 
 int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D, const float* codebook,
                      int n_centroids, int sub_dim, int code_bits, const float* smooth,
-                     int smooth_rows, int transform, uint8_t* codes, int S_cap, int S_off,
-                     const int32_t* row_offsets, void* recon, int out_dtype, void* stream) {
+                     int smooth_rows, int transform, const float* mat, const float* mat_inv,
+                     uint8_t* codes, int S_cap, int S_off, const int32_t* row_offsets, void* recon,
+                     int out_dtype, void* stream) {
   g_last_error[0] = 0;
   int st = check_encode("vq_encode_decode", keys_f16, B, H, S, D, codebook, n_centroids, sub_dim,
-                        code_bits, smooth, smooth_rows, transform, codes, S_cap, S_off, row_offsets);
+                        code_bits, smooth, smooth_rows, transform, mat, mat_inv, 3, codes, S_cap,
+                        S_off, row_offsets);
   if (st) return st;
   if (!recon) return fail(VQ_ERR_INVALID_ARGUMENT, "vq_encode_decode: recon must be non-null");
   if ((st = check_aligned("vq_encode_decode", {recon}))) return st;
   if (out_dtype != 0 && out_dtype != 1)
     return fail(VQ_ERR_INVALID_ARGUMENT, "vq_encode_decode: out_dtype must be 0 (fp32) or 1 (fp16)");
   return run_encode("vq_encode_decode", keys_f16, nullptr, B, H, S, D, codebook, n_centroids,
-                    sub_dim, code_bits, smooth, smooth_rows, transform, codes, S_cap, S_off,
-                    row_offsets, recon, out_dtype, 1, stream);
+                    sub_dim, code_bits, smooth, smooth_rows, transform, mat, mat_inv, codes, S_cap,
+                    S_off, row_offsets, recon, out_dtype, 1, stream);
 }
 
 int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
               const float* codebook, int n_centroids, int sub_dim, int code_bits,
-              const float* smooth, int smooth_rows, int transform, int D, void* out, int out_dtype,
-              void* stream) {
+              const float* smooth, int smooth_rows, int transform, const float* mat,
+              const float* mat_inv, int D, void* out, int out_dtype, void* stream) {
   g_last_error[0] = 0;
   const char* what = "vq_decode";
   if (B < 0 || H <= 0 || S < 0)
@@ -378,16 +399,16 @@ int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
   if (st) return st;
   if ((st = check_code_bits(what, code_bits, n_centroids, D / sub_dim, 2))) return st;
   if ((st = check_smooth(what, smooth, smooth_rows, H))) return st;
-  if ((st = check_transform(what, transform, D))) return st;
+  if ((st = check_transform(what, transform, D, mat, mat_inv, 2))) return st;
   if (out_dtype != 0 && out_dtype != 1)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: out_dtype must be 0 (fp32) or 1 (fp16)", what);
-  if ((st = check_aligned(what, {codebook, smooth, out}))) return st;
+  if ((st = check_aligned(what, {codebook, smooth, out, mat_inv}))) return st;
   if (S_cap <= 0 || S_off < 0 || (long long)S_off + S > S_cap)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: slots [%d, %lld) fall outside [0, %d)", what, S_off,
                 (long long)S_off + S, S_cap);
   return run_encode(what, nullptr, codes, B, H, S, D, codebook, n_centroids, sub_dim, code_bits,
-                    smooth, smooth_rows, transform, nullptr, S_cap, S_off, nullptr, out, out_dtype, 2,
-                    stream);
+                    smooth, smooth_rows, transform, mat, mat_inv, nullptr, S_cap, S_off, nullptr, out,
+                    out_dtype, 2, stream);
 }
 
 size_t vq_attend_workspace_bytes(int B, int H_q, int S_q, int D, int H_kv, int S_cap,
@@ -398,7 +419,8 @@ size_t vq_attend_workspace_bytes(int B, int H_q, int S_q, int D, int H_kv, int S
 }
 
 int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
-                   int n_centroids, int code_bits, int H_kv, int S_cap, int sliding_window) {
+                   int n_centroids, int code_bits, int transform, int H_kv, int S_cap,
+                   int sliding_window) {
   g_last_error[0] = 0;
   const char* what = "vq_attend_path";
   if (B <= 0 || H_q <= 0 || S_q <= 0 || H_kv <= 0 || S_cap <= 0) {
@@ -419,33 +441,38 @@ int vq_attend_path(int B, int H_q, int S_q, int D, int k_sub_dim, int v_sub_dim,
   if (check_code_bits(what, code_bits, n_centroids, D / k_sub_dim, 8) ||
       check_code_bits(what, code_bits, n_centroids, D / v_sub_dim, 8))
     return 0;
+  if (transform < 0 || transform > 2 || (transform == 2 && D > 128)) {
+    fail(VQ_ERR_UNSUPPORTED, "%s: transform %d with head dim %d", what, transform, D);
+    return 0;
+  }
   const int path = attend_path(B, H_q, S_q, D, H_kv, S_cap, sliding_window, k_sub_dim, v_sub_dim,
-                               n_centroids, code_bits);
+                               n_centroids, code_bits, transform);
   if (!path) fail(VQ_ERR_UNSUPPORTED, "%s: no kernel fits this shape", what);
   return path;
 }
 
 int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* k_codes,
               const float* k_codebook, int k_sub_dim, const float* smooth, int smooth_rows,
-              int transform, const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
-              int n_centroids, int code_bits, int H_kv, int S_cap, const int32_t* kv_lens,
-              float scale, int causal, int sliding_window, void* out_f16, void* workspace,
-              size_t workspace_bytes, void* stream) {
+              int transform, const float* mat, const float* mat_inv, const uint8_t* v_codes,
+              const float* v_codebook, int v_sub_dim, int n_centroids, int code_bits, int H_kv,
+              int S_cap, const int32_t* kv_lens, float scale, int causal, int sliding_window,
+              void* out_f16, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   return attend_impl("vq_attend", q_f16, B, H_q, S_q, D, k_codes, k_codebook, k_sub_dim, smooth,
-                     smooth_rows, transform, v_codes, v_codebook, v_sub_dim, n_centroids, code_bits,
+                     smooth_rows, transform, mat, mat_inv, v_codes, v_codebook, v_sub_dim, n_centroids, code_bits,
                      H_kv, S_cap, kv_lens, scale, causal, sliding_window, out_f16, workspace,
                      workspace_bytes, false, stream);
 }
 
 int vq_attend_noalloc(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* k_codes,
                       const float* k_codebook, int k_sub_dim, const float* smooth, int smooth_rows,
-                      int transform, const uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
-                      int n_centroids, int code_bits, int H_kv, int S_cap, const int32_t* kv_lens,
-                      float scale, int causal, int sliding_window, void* out_f16, void* stream) {
+                      int transform, const float* mat, const float* mat_inv, const uint8_t* v_codes,
+                      const float* v_codebook, int v_sub_dim, int n_centroids, int code_bits,
+                      int H_kv, int S_cap, const int32_t* kv_lens, float scale, int causal,
+                      int sliding_window, void* out_f16, void* stream) {
   g_last_error[0] = 0;
   return attend_impl("vq_attend_noalloc", q_f16, B, H_q, S_q, D, k_codes, k_codebook, k_sub_dim,
-                     smooth, smooth_rows, transform, v_codes, v_codebook, v_sub_dim, n_centroids,
+                     smooth, smooth_rows, transform, mat, mat_inv, v_codes, v_codebook, v_sub_dim, n_centroids,
                      code_bits, H_kv, S_cap, kv_lens, scale, causal, sliding_window, out_f16, nullptr, 0,
                      true, stream);
 }

@@ -84,7 +84,8 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     const __half* __restrict__ q, const uint8_t* __restrict__ kcodes,
     const float* __restrict__ kcb, const float* __restrict__ smooth,
     const uint8_t* __restrict__ vcodes, const float* __restrict__ vcb,
-    const int32_t* __restrict__ kv_lens, float* __restrict__ part, AttParams p) {
+    const int32_t* __restrict__ kv_lens, float* __restrict__ part, const float* __restrict__ qpre,
+    AttParams p) {
   extern __shared__ float smem[];
   const LdsLayout L = lds_layout(p.nsk, p.n_c, p.dv, p.nsv, R, D);
   float* lut = smem + L.lut;
@@ -128,13 +129,18 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     if (gr < p.rows) {
       const int hl = gr / p.Sq, i = gr % p.Sq;
       const int h = g * p.G + hl;
-      v = __half2float(q[(((size_t)b * p.Hq + h) * p.Sq + i) * D + c]);
-      if (srow) v *= srow[c];
+      const size_t qi = (((size_t)b * p.Hq + h) * p.Sq + i) * D + c;
+      if (qpre) {
+        v = qpre[qi];  // dual-transformed already (explicit matrix)
+      } else {
+        v = __half2float(q[qi]);
+        if (srow) v *= srow[c];
+      }
     }
     qt[idx] = v;
   }
   __syncthreads();
-  if (p.transform) {
+  if (p.transform == 1) {
     for (int hb = 1; hb < D; hb <<= 1) {
       for (int k = tid; k < R * D / 2; k += kThreads) {
         const int r = k / (D / 2), m = k % (D / 2);
@@ -384,6 +390,32 @@ __global__ __launch_bounds__(D) void attend_merge_kernel(const float* __restrict
   out[(size_t)row * D + threadIdx.x] = __float2half_rn(lsum > 0.f ? a / lsum : 0.f);
 }
 
+// Dual transform of every query row for an explicit matrix (transform 2):
+// q~ = (q * s[kv(h)]) . (M^-1)^T in fp32, one workgroup per query row (the
+// dual of the keys' x . M, "Metal Kernels API", "Fused SDPA": q~ . K~^T =
+// q . K_hat^T).  Column j of (M^-1)^T is row j of M^-1.
+__global__ __launch_bounds__(128) void dense_query_kernel(const __half* __restrict__ q,
+                                                          const float* __restrict__ smooth,
+                                                          const float* __restrict__ rot_inv,
+                                                          float* __restrict__ out, int Hq, int Sq,
+                                                          int D, int G, int smooth_rows) {
+  extern __shared__ float xrow[];  // [D]
+  const size_t row = blockIdx.x;   // (b, h, i)
+  const int g = (int)((row / Sq) % Hq) / G;
+  for (int i = threadIdx.x; i < D; i += blockDim.x) {
+    float v = __half2float(q[row * D + i]);
+    if (smooth) v *= smooth[(size_t)(smooth_rows == 1 ? 0 : g) * D + i];
+    xrow[i] = v;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < D; j += blockDim.x) {
+    const float* m = rot_inv + (size_t)j * D;
+    float acc = 0.f;
+    for (int i = 0; i < D; ++i) acc = fmaf(xrow[i], m[i], acc);
+    out[row * D + j] = acc;
+  }
+}
+
 template <int D, int R>
 hipError_t launch_dr(const AttendArgs& a, const AttParams& p, size_t lds_bytes, hipStream_t st) {
   auto k = attend_split_kernel<D, R>;
@@ -392,7 +424,7 @@ hipError_t launch_dr(const AttendArgs& a, const AttParams& p, size_t lds_bytes, 
   if (e != hipSuccess) return e;
   dim3 grid(a.B * a.Hkv, p.n_rgroups, p.n_split);
   hipLaunchKernelGGL(k, grid, dim3(kThreads), lds_bytes, st, a.q, a.k_codes, a.k_codebook,
-                     a.smooth, a.v_codes, a.v_codebook, a.kv_lens, a.partials, p);
+                     a.smooth, a.v_codes, a.v_codebook, a.kv_lens, a.partials, a.q_pre, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_attend_merge(a, p, st);
@@ -461,6 +493,9 @@ bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, A
   pl->workspace_bytes = std::max(pl->workspace_bytes, stream_workspace_bytes(B, Hq, Sq, D, Hkv));
   pl->workspace_bytes =
       std::max(pl->workspace_bytes, tile_workspace_bytes(B, Hq, Sq, D, Hkv, S_cap, window));
+  // after the partials: the fp32 query rows of an explicit transform matrix
+  pl->qpre_offset = (pl->workspace_bytes + 255) / 256 * 256;
+  pl->workspace_bytes = pl->qpre_offset + (size_t)B * Hq * Sq * D * sizeof(float);
   pl->R = 0;
   pl->n_rgroups = 0;
   return true;
@@ -484,9 +519,11 @@ int attend_pick_rows(int rows, int nsk, int n_c, int dv, int nsv, int D, size_t*
 }
 
 int attend_path(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, int dk, int dv,
-                int n_c, int code_bits) {
-  // 4-bit codes run on the streaming kernel and the per-unit VALU kernel
-  if (code_bits == 8 && tile_plan(B, Hq, Sq, D, Hkv, S_cap, window, dk, dv, n_c, nullptr))
+                int n_c, int code_bits, int transform) {
+  // 4-bit codes and explicit transform matrices run on the streaming kernel
+  // and the per-unit VALU kernel
+  const bool basic = code_bits == 8 && transform != 2;
+  if (basic && tile_plan(B, Hq, Sq, D, Hkv, S_cap, window, dk, dv, n_c, nullptr))
     return VQ_PATH_TILE;
   if (stream_plan(B, Hq, Sq, D, Hkv, S_cap, window, dk, dv, n_c, nullptr, nullptr, nullptr))
     return VQ_PATH_STREAM;
@@ -494,14 +531,26 @@ int attend_path(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, in
   if (!plan_attend(B, Hq, Sq, D, Hkv, S_cap, window, &plan)) return 0;
   int R = 0;
   size_t lds = 0;
-  if (code_bits == 8 && attend_mfma_plan(D, dv, D / dk, plan.rows, &R, &lds)) return VQ_PATH_LUT_MFMA;
+  if (basic && attend_mfma_plan(D, dv, D / dk, plan.rows, &R, &lds)) return VQ_PATH_LUT_MFMA;
   if (attend_pick_rows(plan.rows, D / dk, n_c, dv, D / dv, D, &lds)) return VQ_PATH_LUT_VALU;
   return 0;
 }
 
-hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_t st) {
+hipError_t launch_attend(const AttendArgs& a_in, const AttendPlan& plan, hipStream_t st) {
+  AttendArgs a = a_in;
+  if (a.transform == 2) {
+    // the query rows' dual transform, into the end of the workspace
+    a.q_pre = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.partials) +
+                                             plan.qpre_offset);
+    const unsigned rows = (unsigned)((long long)a.B * a.Hq * a.Sq);
+    hipLaunchKernelGGL(dense_query_kernel, dim3(rows), dim3(128), a.D * sizeof(float), st, a.q,
+                       a.smooth, a.rot_inv, const_cast<float*>(a.q_pre), a.Hq, a.Sq, a.D,
+                       a.Hq / a.Hkv, a.smooth_rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int path = attend_path(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c,
-                               a.code_bits);
+                               a.code_bits, a.transform);
   if (path == VQ_PATH_TILE) {
     TileParams tp;
     tile_plan(a.B, a.Hq, a.Sq, a.D, a.Hkv, a.S_cap, a.window, a.dk, a.dv, a.n_c, &tp);
@@ -526,7 +575,7 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& plan, hipStream_
   p.n_rgroups = (p.rows + p.R - 1) / p.R;
   if (p.n_rgroups > 65535 || p.n_split > 65535) return hipErrorInvalidValue;
   float norm = 1.f;
-  if (a.transform) {
+  if (a.transform == 1) {
     switch (a.D) {
       case 32: norm = WhtNorm<32>::value; break;
       case 64: norm = WhtNorm<64>::value; break;

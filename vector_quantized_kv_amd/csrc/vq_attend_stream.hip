@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const float* __restrict__ k_codebook, const float* __restrict__ smooth,
     const uint8_t* __restrict__ v_codes, const float* __restrict__ v_codebook,
     const int32_t* __restrict__ kv_lens, int* __restrict__ header, float* __restrict__ part,
-    StreamParams p) {
+    const float* __restrict__ qpre, StreamParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   constexpr uint32_t kKRow = 16 * BITS / 8, kVRow = 32 * BITS / 8;  // code bytes per token
   const int tid = threadIdx.x;
@@ -244,9 +244,15 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const int rc = rho < p.GS ? rho : p.GS - 1;
     const int ip = (int)fast_div((uint32_t)rc, p.div_g);
     const int h = gq * p.G + rc - ip * p.G;
-    const __half* qp = q + ((size_t)(bq_b * p.Hq + h) * p.Sq + ip) * kD;
+    const size_t qrow = ((size_t)(bq_b * p.Hq + h) * p.Sq + ip) * kD;
+    if (qpre) {
+      // rows already dual-transformed (explicit matrix): fp32, in the s slots
 #pragma unroll
-    for (int k = 0; k < 2; ++k) r.q[k] = *reinterpret_cast<const uint2*>(qp + 64 * k + 4 * bq);
+      for (int k = 0; k < 2; ++k) r.s[k] = *reinterpret_cast<const float4*>(qpre + qrow + 64 * k + 4 * bq);
+      return r;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) r.q[k] = *reinterpret_cast<const uint2*>(q + qrow + 64 * k + 4 * bq);
     if (smooth) {
       const float* sp = smooth + (p.smooth_rows == 1 ? 0 : gq) * kD;
 #pragma unroll
@@ -259,19 +265,26 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const int bq = lane >> 2, ir = lane & 3;
     const int rho = 4 * rgq + ir;
     float x[8];
+    if (qpre) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        x[4 * k] = r.s[k].x; x[4 * k + 1] = r.s[k].y; x[4 * k + 2] = r.s[k].z; x[4 * k + 3] = r.s[k].w;
+      }
+    } else {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const float2 f0 = __half22float2(*reinterpret_cast<const __half2*>(&r.q[k].x));
       const float2 f1 = __half22float2(*reinterpret_cast<const __half2*>(&r.q[k].y));
       x[4 * k] = f0.x; x[4 * k + 1] = f0.y; x[4 * k + 2] = f1.x; x[4 * k + 3] = f1.y;
     }
-    if (smooth) {
+    }
+    if (smooth && !qpre) {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         x[4 * k] *= r.s[k].x; x[4 * k + 1] *= r.s[k].y; x[4 * k + 2] *= r.s[k].z; x[4 * k + 3] *= r.s[k].w;
       }
     }
-    if (p.transform) {
+    if (p.transform == 1) {
       // in-register index bits 0, 1 (dims 0, 1) and 2 (dim bit 6)
 #pragma unroll
       for (int m = 1; m < 8; m <<= 1) {
@@ -921,7 +934,7 @@ hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds
   sp.transform = a.transform;
   sp.causal = a.causal;
   sp.window = a.window;
-  sp.fold = (a.transform ? WhtNorm<kD>::value : 1.f) * a.scale_log2e;
+  sp.fold = (a.transform == 1 ? WhtNorm<kD>::value : 1.f) * a.scale_log2e;
   const size_t header_bytes = ((size_t)sp.U * 8 + 255) / 256 * 256;
   int* header = reinterpret_cast<int*>(a.partials);
   float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.partials) + header_bytes);
@@ -930,7 +943,8 @@ hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, a.q, a.k_codes,
-                     a.k_codebook, a.smooth, a.v_codes, a.v_codebook, a.kv_lens, header, part, sp);
+                     a.k_codebook, a.smooth, a.v_codes, a.v_codebook, a.kv_lens, header, part, a.q_pre,
+                     sp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = (long long)a.B * a.Hq * a.Sq;

@@ -336,6 +336,143 @@ __global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kernel(
   pvq_body<D, DS, MODE, CSPLIT>(blockIdx.x, keys, codes_in, cb, smooth, codes, recon, d, offs);
 }
 
+// Dense rotation (transform == 2): an explicit invertible [D, D] matrix M,
+// the H_mat argument of vecinfer_encode_decode_metal ("Metal Kernels API",
+// "VecInfer kernels"): encode rotates x / s by M (x~ = (x / s) . M, a row
+// vector times M), decode by M^-1.  One lane per (token-head, sub-vector j)
+// as in pvq_body; the token-head's D values are staged in LDS and the lane
+// forms its sub_dim outputs y[e] = sum_i x[i] A[i][j d + e] with the
+// matrix A held in LDS for the whole (grid-stride) launch.  fp32 products
+// summed in index order; then the same nearest-centroid search.
+template <int D, int DS, int MODE>
+__global__ __launch_bounds__(kThreads) void pvq_dense_kernel(
+    const __half* __restrict__ keys, const uint8_t* __restrict__ codes_in,
+    const float* __restrict__ cb, const float* __restrict__ smooth,
+    const float* __restrict__ rot, const float* __restrict__ rot_inv,
+    uint8_t* __restrict__ codes, void* __restrict__ recon, Dims d, RowOffsets offs) {
+  constexpr int NSUB = D / DS;      // lanes per token-head
+  constexpr int TPW = 64 / NSUB;    // token-heads per wave step
+  constexpr int WPB = kThreads / 64;
+  constexpr int NMAT = MODE == 1 ? 2 : 1;  // M (encode), M^-1 (decode), or both
+  extern __shared__ __align__(16) float dl[];
+  float* const mat = dl;                          // [NMAT][D][D]
+  float* const xs = dl + NMAT * D * D;            // [WPB][TPW][D] staged vectors
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int j = lane % NSUB, tok = lane / NSUB;
+  {
+    const float* src0 = MODE == 2 ? rot_inv : rot;
+    for (int i = threadIdx.x; i < D * D / 4; i += kThreads)
+      reinterpret_cast<float4*>(mat)[i] = reinterpret_cast<const float4*>(src0)[i];
+    if constexpr (MODE == 1)
+      for (int i = threadIdx.x; i < D * D / 4; i += kThreads)
+        reinterpret_cast<float4*>(mat + D * D)[i] = reinterpret_cast<const float4*>(rot_inv)[i];
+  }
+  __syncthreads();
+  float* const xw = xs + (wave * TPW + tok) * D;  // this lane's token-head vector
+  // y = x . A for the lane's sub-vector: x staged in xw (the wave's own LDS
+  // accesses execute in issue order, so the reads see the writes)
+  auto rotate = [&](float (&x)[DS], const float* A) {
+#pragma unroll
+    for (int e = 0; e < DS; ++e) xw[j * DS + e] = x[e];
+    float y[DS];
+#pragma unroll
+    for (int e = 0; e < DS; ++e) y[e] = 0.f;
+    for (int i = 0; i < D; i += 4) {
+      const float4 xv = *reinterpret_cast<const float4*>(xw + i);
+      const float xi[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float* arow = A + (i + k) * D + j * DS;
+#pragma unroll
+        for (int e = 0; e < DS; ++e) y[e] = fmaf(xi[k], arow[e], y[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < DS; ++e) x[e] = y[e];
+  };
+
+  const long long n_th = (long long)d.B * d.H * d.S;
+  const long long n_steps = (n_th + TPW - 1) / TPW;
+  for (long long step = (long long)blockIdx.x * WPB + wave; step < n_steps;
+       step += (long long)gridDim.x * WPB) {
+    const long long th = step * TPW + tok;
+    const bool valid = th < n_th;
+    const long long thc = valid ? th : 0;
+    const int t = (int)(thc % d.S);
+    const long long bh = thc / d.S;
+    const int h = (int)(bh % d.H);
+    const int b = (int)(bh / d.H);
+    const float* srow =
+        smooth ? smooth + (long long)(d.smooth_rows == 1 ? 0 : h) * D + j * DS : nullptr;
+    float x[DS];
+    int idx = 0;
+    if constexpr (MODE != 2) {
+      RawHalves<DS> raw = load_raw_f16<DS>(keys + thc * D + j * DS);
+      cvt_raw_f16<DS>(raw, x);
+      if (!valid) {
+#pragma unroll
+        for (int e = 0; e < DS; ++e) x[e] = 0.f;
+      }
+      if (srow) {
+#pragma unroll
+        for (int e = 0; e < DS; ++e) x[e] = x[e] / srow[e];
+      }
+      rotate(x, mat);
+      // nearest centroid (fp32 squared distance over e in order, strict '<')
+      float best = INFINITY;
+#pragma unroll 8
+      for (int c = 0; c < d.n_c; ++c) {
+        const float* cc = cb + c * DS;
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < DS; ++e) {
+          const float df = x[e] - cc[e];
+          acc = fmaf(df, df, acc);
+        }
+        if (acc < best) { best = acc; idx = c; }
+      }
+      const int idx_next = __shfl_down(idx, 1);
+      if (valid) {
+        const int off = d.use_row_offsets ? offs.v[b] : d.S_off;
+        if (d.code_bits == 4) {
+          if (!(j & 1))
+            codes[(bh * d.S_cap + off + t) * (NSUB / 2) + j / 2] = (uint8_t)((idx & 15) | ((idx_next & 15) << 4));
+        } else {
+          codes[(bh * d.S_cap + off + t) * NSUB + j] = (uint8_t)idx;
+        }
+      }
+    } else {
+      if (valid) {
+        int c;
+        if (d.code_bits == 4) {
+          const int byte = codes_in[(bh * d.S_cap + d.S_off + t) * (NSUB / 2) + j / 2];
+          c = (j & 1) ? byte >> 4 : byte & 15;
+        } else {
+          c = codes_in[(bh * d.S_cap + d.S_off + t) * NSUB + j];
+        }
+        idx = min(c, d.n_c - 1);
+      }
+    }
+    if constexpr (MODE != 0) {
+      const float* cc = cb + idx * DS;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) x[e] = cc[e];
+      rotate(x, MODE == 1 ? mat + D * D : mat);  // by M^-1
+      if (srow) {
+#pragma unroll
+        for (int e = 0; e < DS; ++e) x[e] = x[e] * srow[e];
+      }
+      if (valid) {
+        if (d.recon_dtype == 1)
+          store_f16<DS>(reinterpret_cast<__half*>(recon) + thc * D + j * DS, x);
+        else
+          store_f32<DS>(reinterpret_cast<float*>(recon) + thc * D + j * DS, x);
+      }
+    }
+  }
+}
+
 // Encode of the keys and the values of one append in one launch (the cache
 // appends both, "veloxquant_mlx.cache.vecinfer_cache module",
 // update_and_fetch): workgroups [0, k_blocks) encode the keys with their
@@ -1014,6 +1151,35 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
   const Dims d = make_dims(a);
   RowOffsets o{};
   if (offs) o = *offs;
+  if (a.transform == 2) {
+    if constexpr (D <= 128) {
+      // one grid-stride pass: as many workgroups as are resident at once
+      const int nmat = mode == 1 ? 2 : 1;
+      const size_t lds = (size_t)(nmat * D * D + kThreads / 64 * 64 / (D / DS) * D) * sizeof(float);
+      void (*kern)(const __half*, const uint8_t*, const float*, const float*, const float*,
+                   const float*, uint8_t*, void*, Dims, RowOffsets);
+      kern = mode == 0 ? pvq_dense_kernel<D, DS, 0>
+                       : (mode == 1 ? pvq_dense_kernel<D, DS, 1> : pvq_dense_kernel<D, DS, 2>);
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      int per_cu = 0, cus = 0, dev = 0;
+      (void)hipGetDevice(&dev);
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds) != hipSuccess ||
+          per_cu <= 0)
+        per_cu = 1;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          cus <= 0)
+        cus = 256;
+      const long long steps = (n_th + 64 / (D / DS) - 1) / (64 / (D / DS));
+      const long long want = (steps + kThreads / 64 - 1) / (kThreads / 64);
+      const unsigned blocks = (unsigned)std::max(1LL, std::min(want, (long long)per_cu * cus));
+      hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, st, a.keys, a.codes_in, a.codebook,
+                         a.smooth, a.rot, a.rot_inv, a.codes, a.recon, d, o);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   const int split = codebook_split(a);
   // Enough sub-vectors to fill the chip: nearest centroid on the matrix cores
   // (8-bit codes; a 4-bit codebook has at most 16 centroids, a short search
@@ -1084,7 +1250,7 @@ hipError_t launch_encode_kv(const EncodeArgs& k, const EncodeArgs& v, const RowO
   // the same split and a compiled (head dim, key, value sub_dim) triple;
   // otherwise the two encodes run one after the other.
   const int split = codebook_split(k);
-  if (split > 1 && split == codebook_split(v)) {
+  if (k.transform != 2 && split > 1 && split == codebook_split(v)) {
     RowOffsets o{};
     if (offs) o = *offs;
     bool done = false;

@@ -33,6 +33,8 @@ struct EncodeArgs {
   int B, H, S, D, n_c, sub_dim, smooth_rows, transform;
   int S_cap, S_off, use_row_offsets, recon_dtype;  // recon_dtype 0 fp32, 1 fp16
   int code_bits;           // 8: one code per byte; 4: two per byte (low nibble first)
+  const float* rot;        // transform == 2: [D, D] M (encode)
+  const float* rot_inv;    // transform == 2: [D, D] M^-1 (decode)
 };
 
 // mode 0 = encode, 1 = encode + reconstruct, 2 = decode only.
@@ -56,6 +58,9 @@ struct AttendArgs {
   float scale_log2e;
   int causal, window;
   int code_bits;            // 8 or 4 (two codes per byte, low nibble first)
+  const float* rot_inv;     // transform == 2: [D, D] M^-1 (the query uses its transpose)
+  const float* q_pre;       // set by launch_attend for transform 2: [B, H_q, S_q, D] fp32
+                            // dual-transformed, scale-free query rows in the workspace
 };
 
 struct AttendPlan {
@@ -65,7 +70,8 @@ struct AttendPlan {
   int n_rgroups;    // ceil(rows / R)
   int split_tokens; // keys per split
   int n_split;      // splits per (b, kv head, row group)
-  size_t workspace_bytes; // split partials
+  size_t workspace_bytes; // split partials, then the transformed query rows
+  size_t qpre_offset;     // byte offset of the transformed query rows
 };
 
 // Kernel-side parameters of one attention launch (by value).
@@ -120,7 +126,7 @@ hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds
 
 // The VQ_PATH_* family launch_attend uses for a validated shape (0 if none).
 int attend_path(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, int dk, int dv,
-                int n_c, int code_bits);
+                int n_c, int code_bits, int transform);
 
 // Many-query kernel (prefill: at least 64 query rows per kv head; head dim
 // 128, key sub_dim 8, value sub_dim 4).
