@@ -7,3 +7,4 @@ from .api import (VQError, attend_workspace, vq_attend, vq_attend_noalloc, vq_at
                   vq_attend_workspace_bytes, vq_decode, vq_encode, vq_encode_decode,
                   vq_encode_kv,
                   vq_supports_shape)
+from .cache import CacheLayout, VQKVCache  # noqa: F401
