@@ -44,6 +44,13 @@ the design notes of the repository):
   R10 a query row with no valid key outputs zeros.
   R11 GQA: query head h reads kv head h // (H_q / H_kv).
   R12 the query uses the smooth row of its kv head.
+  R24 4-bit codes pack two indices per byte, the even sub-vector in the low
+      nibble (the pages' rabitq_pack_values layout).
+  R25 codebooks are trained by Lloyd's k-means over the pooled sub-vectors
+      (the keys' after smoothing and rotation, the values' raw): the pages
+      only say the keys are encoded against a pre-trained codebook.  The
+      initial centroids are an input; assignment follows R5; a centroid
+      with no member keeps its value; a fixed number of iterations.
 
 Every function computes in float64.  Precision notes for comparisons with
 the GPU live with the tests.
@@ -395,6 +402,63 @@ def code_bytes_per_token(D: int, sub_dim: int, bits: int) -> float:
 
 def codebook_bytes(bits: int, sub_dim: int, bytes_per_entry: int) -> int:
     """2**b * d entries of bytes_per_entry bytes (amortized codebook cost,
-    same page and formula; the page counts fp16 entries, this build stores
+    same page and formula; the page counts fp16 entries, the library stores
     fp32 codebooks)."""
     return (2 ** bits) * sub_dim * bytes_per_entry
+
+
+# ----------------------------------------------------------------------------
+# Codebook training (reading R25)
+# ----------------------------------------------------------------------------
+def lloyd_step(vectors, centroids):
+    """One iteration of Lloyd's algorithm (k-means) on vectors [N, d].
+
+    The codebooks the "veloxquant_mlx.cache.vecinfer_cache module" page
+    encodes against come pre-trained; this is the plain k-means reading of
+    that training (R25).  Assignment: every vector takes the index of its
+    nearest centroid by squared distance, lowest index on exact ties (R5).
+    Update: every centroid becomes the mean of the vectors assigned to it;
+    one with no member keeps its value.
+
+    Returns (new centroids float64 [k, d], labels int64 [N], inertia = the
+    sum over vectors of the smallest squared distance to the centroids
+    passed in, gap float64 [N] as in pvq_encode).
+    """
+    x = np.asarray(vectors, dtype=F64)
+    C = np.asarray(centroids, dtype=F64)
+    if x.ndim != 2 or C.ndim != 2 or x.shape[1] != C.shape[1]:
+        raise ValueError("vectors [N, d] and centroids [k, d] expected")
+    k, d = C.shape
+    labels, gap = pvq_encode(x, C, d)
+    labels, gap = labels[:, 0], gap[:, 0]
+    diff = x - C[labels]
+    inertia = float(np.sum(diff * diff))
+    sums = np.zeros((k, d), dtype=F64)
+    np.add.at(sums, labels, x)
+    counts = np.bincount(labels, minlength=k)
+    new = C.copy()
+    has = counts > 0
+    new[has] = sums[has] / counts[has, None]
+    return new, labels, inertia, gap
+
+
+def kmeans(vectors, init, iters: int):
+    """`iters` Lloyd steps from the centroids `init` [k, d].
+
+    Returns (centroids after the last update, labels of the last assignment,
+    inertia of every step (list), gap of the last assignment).
+    """
+    C = np.asarray(init, dtype=F64)
+    labels = np.zeros(np.asarray(vectors).shape[0], dtype=np.int64)
+    gap = np.full(labels.shape, np.inf)
+    inertia = []
+    for _ in range(iters):
+        C, labels, e, gap = lloyd_step(vectors, C)
+        inertia.append(e)
+    return C, labels, inertia, gap
+
+
+def training_vectors(x, sub_dim: int, smooth=None, transform=False) -> np.ndarray:
+    """The pooled sub-vectors [B * H * S * D / d, d] a codebook is trained
+    on: forward_transform of x [B, H, S, D] split as in R3."""
+    return forward_transform(x, smooth, transform).reshape(-1, sub_dim)

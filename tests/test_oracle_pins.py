@@ -383,12 +383,97 @@ def pin_randomized_hadamard(o):
     assert np.max(np.abs(a1 - a2)) < 1e-12
 
 
+def pin_kmeans_golden(o):
+    """Two Lloyd runs worked by hand (tests/golden/kmeans_worked.txt): a 1-D
+    one whose second step moves a point, a 2-D one with an exact tie and a
+    centroid that never gets a member."""
+    g = read_golden("kmeans_worked.txt")
+    for tag, d, steps in [("a", 1, 3), ("b", 2, 2)]:
+        x = g[f"{tag}_points"].reshape(-1, d)
+        C = g[f"{tag}_init"].reshape(-1, d)
+        for it in range(1, steps + 1):
+            C, labels, inertia, _ = o.lloyd_step(x, C)
+            if f"{tag}_labels_{it}" in g:
+                assert np.array_equal(labels, g[f"{tag}_labels_{it}"]), (tag, it)
+            assert abs(inertia - g[f"{tag}_inertia_{it}"][0]) < 1e-12, (tag, it, inertia)
+            assert np.max(np.abs(C.ravel() - g[f"{tag}_centroids_{it}"])) < 1e-12, (tag, it)
+        Ck, lk, ek, _ = o.kmeans(x, g[f"{tag}_init"].reshape(-1, d), steps)
+        assert np.allclose(ek, [g[f"{tag}_inertia_{i}"][0] for i in range(1, steps + 1)], rtol=0, atol=1e-12)
+        assert np.max(np.abs(Ck.ravel() - g[f"{tag}_centroids_{steps}"])) < 1e-12
+
+
+def pin_kmeans_single_cluster(o):
+    """k = 1 in closed form: one step moves the centroid to the mean; the
+    first inertia is N (sum of variances + |mean - init|^2) (parallel axis),
+    the second N * sum of variances."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((500, 6)) * rng.uniform(0.5, 4, size=6) + rng.uniform(-3, 3, size=6)
+    init = rng.standard_normal((1, 6)) * 5
+    C, labels, inertia, _ = o.kmeans(x, init, 2)
+    mean, var = x.mean(axis=0), x.var(axis=0)
+    assert np.max(np.abs(C[0] - mean)) < 1e-12 and not labels.any()
+    n = x.shape[0]
+    assert abs(inertia[0] - n * (var.sum() + np.sum((mean - init[0]) ** 2))) < 1e-8 * inertia[0]
+    assert abs(inertia[1] - n * var.sum()) < 1e-9 * inertia[1]
+
+
+def pin_kmeans_separated(o):
+    """Blobs far apart relative to their spread, each started from one of its
+    own points (in a shuffled order): every label is the blob's start index
+    and every centroid the blob's mean, from the first step on."""
+    rng = np.random.default_rng(32)
+    k, n, d = 12, 40, 8
+    centres = rng.standard_normal((k, d)) * 100
+    x = np.concatenate([c + rng.standard_normal((n, d)) for c in centres])
+    order = rng.permutation(k)                      # centroid i starts in blob order[i]
+    init = x[order * n]
+    C, labels, inertia, _ = o.kmeans(x, init, 3)
+    blob_of_centroid = np.empty(k, dtype=np.int64)
+    blob_of_centroid[order] = np.arange(k)          # blob b is centroid blob_of_centroid[b]
+    assert np.array_equal(labels, np.repeat(blob_of_centroid, n))
+    for b in range(k):
+        assert np.max(np.abs(C[blob_of_centroid[b]] - x[b * n:(b + 1) * n].mean(axis=0))) < 1e-9
+    assert inertia[1] == pytest.approx(inertia[2], rel=1e-12) and inertia[0] > inertia[1]
+
+
+def pin_kmeans_fixed_point_bruteforce(o):
+    """Run to convergence on a tiny random set; then, checked with plain
+    loops, every label is the nearest centroid (lowest index on ties), every
+    centroid the mean of its members, and the inertia never rose."""
+    rng = np.random.default_rng(33)
+    N, k, d = 60, 5, 3
+    x = rng.standard_normal((N, d)) * np.array([1.0, 3.0, 0.5])
+    C, labels, inertia, _ = o.kmeans(x, x[:k] + 0.01, 60)
+    for i in range(1, len(inertia)):
+        assert inertia[i] <= inertia[i - 1] * (1 + 1e-12)
+    for i in range(N):
+        best, arg = None, None
+        for c in range(k):
+            dist = sum((float(x[i][e]) - float(C[c][e])) ** 2 for e in range(d))
+            if best is None or dist < best:
+                best, arg = dist, c
+        assert labels[i] == arg
+    for c in range(k):
+        members = [i for i in range(N) if labels[i] == c]
+        if members:
+            for e in range(d):
+                assert abs(C[c][e] - sum(float(x[i][e]) for i in members) / len(members)) < 1e-12
+    # the training vectors are the transformed keys' sub-vectors, in order
+    keys = rng.standard_normal((1, 2, 3, 8))
+    tv = o.training_vectors(keys, 4)
+    for h in range(2):
+        for t in range(3):
+            for j in range(2):
+                assert np.array_equal(tv[(h * 3 + t) * 2 + j], keys[0, h, t, 4 * j:4 * j + 4])
+
+
 ALL_PINS = [pin_hadamard_closed_form, pin_hadamard_golden, pin_hadamard_orthonormal,
             pin_storage, pin_encode_golden, pin_distances_and_gap_golden, pin_gap_bruteforce,
             pin_bruteforce, pin_nibbles, pin_ties, pin_identity_codebook,
             pin_idempotent_and_permutation, pin_attend_golden, pin_attend_sdpa,
             pin_attend_closed_forms, pin_gqa_and_window, pin_dual_transform,
-            pin_dense_transform, pin_randomized_hadamard]
+            pin_dense_transform, pin_randomized_hadamard, pin_kmeans_golden,
+            pin_kmeans_single_cluster, pin_kmeans_separated, pin_kmeans_fixed_point_bruteforce]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -611,12 +696,58 @@ def _mut_nibble_order(mp):
     mp.setattr(O, "unpack_nibbles", unpack)
 
 
+def _mut_kmeans_sum_update(mp):
+    # the update keeps the members' sum instead of their mean
+    orig = O.lloyd_step
+
+    def step(x, C):
+        new, labels, e, gap = orig(x, C)
+        counts = np.bincount(labels, minlength=np.asarray(C).shape[0])
+        has = counts > 0
+        new[has] *= counts[has, None]
+        return new, labels, e, gap
+    mp.setattr(O, "lloyd_step", step)
+
+
+def _mut_kmeans_empty_to_zero(mp):
+    # a centroid with no member is reset to the origin
+    orig = O.lloyd_step
+
+    def step(x, C):
+        new, labels, e, gap = orig(x, C)
+        counts = np.bincount(labels, minlength=np.asarray(C).shape[0])
+        new[counts == 0] = 0.0
+        return new, labels, e, gap
+    mp.setattr(O, "lloyd_step", step)
+
+
+def _mut_kmeans_inertia_after_update(mp):
+    # the inertia measured against the updated centroids
+    orig = O.lloyd_step
+
+    def step(x, C):
+        new, labels, e, gap = orig(x, C)
+        diff = np.asarray(x, dtype=np.float64) - new[labels]
+        return new, labels, float(np.sum(diff * diff)), gap
+    mp.setattr(O, "lloyd_step", step)
+
+
+def _mut_kmeans_split_strided(mp):
+    # training vectors taken with a strided split of D
+    def tv(x, sub_dim, smooth=None, transform=False):
+        xt = O.forward_transform(x, smooth, transform)
+        D = xt.shape[-1]
+        return np.swapaxes(xt.reshape(*xt.shape[:-1], sub_dim, D // sub_dim), -1, -2).reshape(-1, sub_dim)
+    mp.setattr(O, "training_vectors", tv)
+
+
 MUTATIONS = [_mut_matrix_involutory, _mut_dual_untransposed, _mut_smooth_direction, _mut_unnormalized_hadamard, _mut_no_inverse_rotation,
              _mut_ties_high, _mut_strided_split, _mut_head_aligned_causal,
              _mut_window_off_by_one, _mut_window_needs_causal, _mut_gqa_modulo,
              _mut_lut_divides, _mut_missing_scale, _mut_value_transposed,
              _mut_gap_relative_to_d1, _mut_gap_third_smallest, _mut_distances_transposed,
-             _mut_nibble_order]
+             _mut_nibble_order, _mut_kmeans_sum_update, _mut_kmeans_empty_to_zero,
+             _mut_kmeans_inertia_after_update, _mut_kmeans_split_strided]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda m: m.__name__)
