@@ -200,6 +200,65 @@ int vq_encode_decode(const void* keys_f16, int B, int H, int S, int D,
                      void* recon, int out_dtype, void* stream);
 
 /*
+ * Forward transform only: out = (x / s) . M in fp32, the first two steps of
+ * vecinfer_encode_decode_metal ("Metal Kernels API", "VecInfer kernels"),
+ * i.e. the vectors the encode searches.  Viewed as [B * H * S * D / d, d],
+ * out holds the pooled sub-vectors a codebook of sub-vector width d is
+ * trained on (sub-vector j of a row covers dims [j * d, (j + 1) * d)).
+ *
+ *   keys_f16    [B, H, S, D] fp16
+ *   smooth, smooth_rows, transform, mat   as in vq_encode (mat_inv unused)
+ *   out         [B, H, S, D] fp32, written in full
+ * The arithmetic is that of the per-lane encode kernels (x / s in fp32,
+ * then the butterflies or the fp32 matrix product in index order).
+ * Errors: INVALID_ARGUMENT for null pointers, negative sizes, smooth_rows
+ * not in {1, H}, a bad transform or a missing mat; UNSUPPORTED for head
+ * dims other than 32, 64, 128, 256 (transform 2: up to 128).  B = 0 or
+ * S = 0 is a no-op.
+ */
+int vq_transform(const void* keys_f16, int B, int H, int S, int D, const float* smooth,
+                 int smooth_rows, int transform, const float* mat, float* out, void* stream);
+
+/*
+ * Bytes of device workspace vq_kmeans needs (0 on invalid arguments).
+ * Depends only on its arguments.
+ */
+size_t vq_kmeans_workspace_bytes(long long N, int sub_dim, int n_centroids);
+
+/*
+ * Codebook training: `iters` iterations of Lloyd's k-means over N vectors.
+ * The pages encode keys against a pre-trained codebook ("veloxquant_mlx.
+ * cache.vecinfer_cache module" page, module description) and say no more;
+ * this is the plain k-means reading of that training.  Each iteration
+ * assigns every vector to its nearest centroid (the encode's rule: fp32
+ * squared distance summed over the sub-vector in index order, lowest index
+ * on exact ties), then moves every centroid to the mean of its members
+ * (summed in fp64, rounded to fp32); a centroid with no member keeps its
+ * value.
+ *
+ *   vectors     [N, sub_dim] fp32 (e.g. vq_transform's output of the keys,
+ *               or raw values converted to fp32); NULL allowed when N = 0
+ *   centroids   [n_centroids, sub_dim] fp32: the initial centroids on
+ *               entry, the trained ones on return (updated in place)
+ *   labels      NULL or [N] uint8: the last iteration's assignment (made
+ *               against the centroids that iteration started from)
+ *   inertia     NULL or [iters] fp64: for each iteration, the sum over
+ *               vectors of the smallest squared distance to the centroids it
+ *               started from (non-increasing up to rounding)
+ *   workspace   DEVICE buffer of >= vq_kmeans_workspace_bytes(...) bytes;
+ *               calls that may run concurrently need distinct workspaces
+ * sub_dim in {1, 2, 4, 8, 16}; 1 <= n_centroids <= 256.  Two kernel launches
+ * per iteration, no host synchronization; vectors, centroids and workspace
+ * must be 16-byte aligned.
+ * Errors: INVALID_ARGUMENT for negative N or iters, n_centroids outside
+ * [1, 256], null pointers; UNSUPPORTED for other sub_dim; WORKSPACE when the
+ * workspace is missing or too small.  iters = 0 is a no-op.
+ */
+int vq_kmeans(const float* vectors, long long N, int sub_dim, float* centroids, int n_centroids,
+              int iters, uint8_t* labels, double* inertia, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/*
  * Bytes of device workspace vq_attend needs for this shape (0 on invalid
  * sizes).  Depends only on its arguments, not on the device.
  */

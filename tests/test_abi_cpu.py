@@ -314,3 +314,68 @@ def test_attend_noalloc_validation(lib):
     assert st == WORKSPACE and b"scratch" in lib.vq_last_error()
     if not torch.cuda.is_available():
         assert f(*args()) == NO_DEVICE
+
+
+def test_transform_validation(lib):
+    f = lib.vq_transform
+    args = lambda B=1, H=2, S=4, D=128, smooth=None, rows=1, tr=1, mat=None, keys=P, out=P: (
+        keys, B, H, S, D, smooth, rows, tr, mat, out, None)
+    assert f(*args(keys=None)) == INVALID
+    assert f(*args(out=None)) == INVALID
+    assert f(*args(H=0)) == INVALID
+    assert f(*args(S=-1)) == INVALID
+    assert f(*args(D=96)) == UNSUPPORTED
+    assert f(*args(smooth=P, rows=3)) == INVALID                     # smooth_rows not in {1, H}
+    assert f(*args(tr=2)) == INVALID and b"mat" in lib.vq_last_error()
+    assert f(*args(tr=2, D=256, mat=P)) == UNSUPPORTED
+    assert f(*args(tr=3)) == INVALID
+    assert f(*args(out=ctypes.c_void_p(0x10004))) == INVALID        # misaligned
+    assert f(*args(S=0)) == OK and f(*args(B=0)) == OK
+    if not torch.cuda.is_available():
+        assert f(*args()) == NO_DEVICE
+
+
+def test_kmeans_validation(lib):
+    f = lib.vq_kmeans
+    need = lib.vq_kmeans_workspace_bytes(1 << 20, 8, 256)
+    args = lambda v=P, N=1 << 20, d=8, C=P, n_c=256, it=4, ws=P, wsb=need: (
+        v, N, d, C, n_c, it, None, None, ws, wsb, None)
+    assert f(*args(N=-1)) == INVALID
+    assert f(*args(d=3)) == UNSUPPORTED and f(*args(d=32)) == UNSUPPORTED
+    assert f(*args(n_c=0)) == INVALID and f(*args(n_c=257)) == INVALID
+    assert f(*args(it=-1)) == INVALID
+    assert f(*args(C=None)) == INVALID and f(*args(v=None)) == INVALID
+    assert f(*args(ws=ctypes.c_void_p(0x10008))) == INVALID         # misaligned
+    assert f(*args(wsb=need - 1)) == WORKSPACE and b"workspace" in lib.vq_last_error()
+    assert f(*args(ws=None)) == WORKSPACE
+    assert f(*args(it=0)) == OK                                      # no-op
+    if not torch.cuda.is_available():
+        assert f(*args()) == NO_DEVICE
+        assert f(*args(v=None, N=0, wsb=lib.vq_kmeans_workspace_bytes(0, 8, 256))) == NO_DEVICE
+
+
+def test_kmeans_workspace_bytes(lib):
+    """One fp64 row of n_c * (d + 1) + 1 accumulators per assignment
+    workgroup: one workgroup per 4096 vectors, at most 256."""
+    f = lib.vq_kmeans_workspace_bytes
+    row = lambda d, n_c: (n_c * (d + 1) + 1) * 8
+    assert f(0, 8, 256) == row(8, 256)
+    assert f(4096, 8, 256) == row(8, 256)
+    assert f(4097, 8, 256) == 2 * row(8, 256)
+    assert f(1 << 20, 8, 256) == 256 * row(8, 256)
+    assert f(1 << 30, 16, 16) == 256 * row(16, 16)
+    assert f(-1, 8, 256) == 0 and f(10, 3, 256) == 0 and f(10, 8, 0) == 0 and f(10, 8, 257) == 0
+
+
+def test_kmeans_binding_checks_shapes(lib):
+    C = torch.zeros(16, 8)
+    with pytest.raises(ValueError, match="vectors must be"):
+        api.vq_kmeans(torch.zeros(100, 4), C, 1)
+    with pytest.raises(ValueError, match="centroids must be"):
+        api.vq_kmeans(torch.zeros(100, 8), torch.zeros(16, 8, dtype=torch.float64), 1)
+    with pytest.raises(ValueError, match="labels must have shape"):
+        api.vq_kmeans(torch.zeros(100, 8), C, 1, labels=torch.zeros(99, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="device tensor"):
+        api.vq_kmeans(torch.zeros(100, 8), C, 1)
+    with pytest.raises(ValueError, match="out must have shape"):
+        api.vq_transform(torch.zeros(1, 2, 3, 64, dtype=torch.float16), out=torch.zeros(1, 2, 3, 32))

@@ -34,6 +34,11 @@ SIGNATURES = {
                                  c_void_p, c_int, c_int, c_void_p, c_void_p,
                                  c_void_p, c_int, c_int, c_void_p,
                                  c_void_p, c_int, c_void_p]),
+    "vq_transform": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_void_p, c_int, c_int,
+                             c_void_p, c_void_p, c_void_p]),
+    "vq_kmeans_workspace_bytes": (c_size_t, [ctypes.c_longlong, c_int, c_int]),
+    "vq_kmeans": (c_int, [c_void_p, ctypes.c_longlong, c_int, c_void_p, c_int, c_int,
+                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "vq_attend_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int, c_int]),
     "vq_attend_path": (c_int, [c_int] * 12),
     "vq_attend": (c_int, [c_void_p, c_int, c_int, c_int, c_int,

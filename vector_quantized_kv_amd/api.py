@@ -253,6 +253,57 @@ def vq_decode(codes, codebook, *, smooth=None, transform=True, S=None, S_off=0,
                  result=out)
 
 
+def vq_transform(keys, *, smooth=None, transform=True, mat=None, out=None, stream=None,
+                 prepare=False):
+    """Forward transform (x / s) . M of keys [B, H, S, D] fp16 into fp32
+    [B, H, S, D]: the vectors the encode searches and a codebook is trained on
+    (view as [-1, sub_dim] for the pooled sub-vectors)."""
+    _need(keys, "keys", torch.float16, 4)
+    B, H, S, D = keys.shape
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=torch.float32, device=keys.device)
+    _need(out, "out", torch.float32, shape=(B, H, S, D))
+    sm, rows = _smooth(smooth, D, H)
+    tr, m, _ = _transform(transform, mat, None, D)
+    _on_device(keys=keys, out=out, smooth=sm, mat=m)
+    return _call("vq_transform", _ptr(keys), B, H, S, D, _ptr(sm), rows, tr, _ptr(m), _ptr(out),
+                 _stream(stream), prepare=prepare, result=out)
+
+
+def vq_kmeans_workspace_bytes(N, sub_dim, n_centroids) -> int:
+    return int(_lib.load().vq_kmeans_workspace_bytes(N, sub_dim, n_centroids))
+
+
+def vq_kmeans(vectors, centroids, iters, *, labels=None, with_labels=False, inertia=None,
+              workspace=None, stream=None, prepare=False):
+    """`iters` Lloyd iterations over vectors [N, d] fp32 (any contiguous
+    [..., d] is taken as [N, d]); centroids [n_c, d] fp32 are updated in
+    place.  Returns (centroids, labels [N] uint8 of the last assignment or
+    None, inertia [iters] fp64)."""
+    _need(centroids, "centroids", torch.float32, 2)
+    n_c, d = centroids.shape
+    _need(vectors, "vectors", torch.float32)
+    if vectors.dim() < 1 or vectors.shape[-1] != d:
+        raise ValueError(f"vectors must be [..., {d}], got {tuple(vectors.shape)}")
+    N = vectors.numel() // d
+    if labels is None and with_labels:
+        labels = torch.empty(N, dtype=torch.uint8, device=centroids.device)
+    if labels is not None:
+        _need(labels, "labels", torch.uint8, shape=(N,))
+    if inertia is None:
+        inertia = torch.zeros(max(iters, 0), dtype=torch.float64, device=centroids.device)
+    _need(inertia, "inertia", torch.float64, shape=(max(iters, 0),))
+    need = vq_kmeans_workspace_bytes(N, d, n_c)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=centroids.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _on_device(vectors=vectors, centroids=centroids, labels=labels, inertia=inertia,
+               workspace=workspace)
+    return _call("vq_kmeans", _ptr(vectors), ctypes.c_longlong(N), d, _ptr(centroids), n_c, iters,
+                 _ptr(labels), _ptr(inertia), _ptr(workspace), workspace.numel(), _stream(stream),
+                 prepare=prepare, result=(centroids, labels, inertia))
+
+
 def vq_attend_workspace_bytes(B, H_q, S_q, D, H_kv, S_cap, sliding_window=0) -> int:
     return int(_lib.load().vq_attend_workspace_bytes(B, H_q, S_q, D, H_kv, S_cap, sliding_window))
 

@@ -477,4 +477,57 @@ int vq_attend_noalloc(const void* q_f16, int B, int H_q, int S_q, int D, const u
                      true, stream);
 }
 
+int vq_transform(const void* keys_f16, int B, int H, int S, int D, const float* smooth,
+                 int smooth_rows, int transform, const float* mat, float* out, void* stream) {
+  g_last_error[0] = 0;
+  const char* what = "vq_transform";
+  if (B < 0 || H <= 0 || S < 0)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0, H > 0, S >= 0 (got %d, %d, %d)", what, B, H, S);
+  if (!keys_f16 || !out) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: keys and out must be non-null", what);
+  if (!supported_head_dim(D))
+    return fail(VQ_ERR_UNSUPPORTED, "%s: head_dim must be 32, 64, 128 or 256 (got %d)", what, D);
+  int st = check_smooth(what, smooth, smooth_rows, H);
+  if (st) return st;
+  if ((st = check_transform(what, transform, D, mat, nullptr, 1))) return st;
+  if ((st = check_aligned(what, {keys_f16, smooth, mat, out}))) return st;
+  // the transform-only kernels use an 8-wide lane layout (the result does
+  // not depend on it)
+  return run_encode(what, keys_f16, nullptr, B, H, S, D, nullptr, 1, 8, 8, smooth, smooth_rows,
+                    transform, mat, nullptr, nullptr, S, 0, nullptr, out, 0, 3, stream);
+}
+
+size_t vq_kmeans_workspace_bytes(long long N, int sub_dim, int n_centroids) {
+  if (N < 0 || !supported_sub_dim(sub_dim) || n_centroids < 1 || n_centroids > 256) return 0;
+  return kmeans_workspace_bytes(N, sub_dim, n_centroids);
+}
+
+int vq_kmeans(const float* vectors, long long N, int sub_dim, float* centroids, int n_centroids,
+              int iters, uint8_t* labels, double* inertia, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  g_last_error[0] = 0;
+  const char* what = "vq_kmeans";
+  if (N < 0 || N > (1LL << 48))
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: N must be in [0, 2^48] (got %lld)", what, N);
+  if (!supported_sub_dim(sub_dim))
+    return fail(VQ_ERR_UNSUPPORTED, "%s: sub_dim must be 1, 2, 4, 8 or 16 (got %d)", what, sub_dim);
+  if (n_centroids < 1 || n_centroids > 256)
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: n_centroids must be in [1, 256] (got %d)", what, n_centroids);
+  if (iters < 0) return fail(VQ_ERR_INVALID_ARGUMENT, "%s: iters must be >= 0 (got %d)", what, iters);
+  if (!centroids || (N > 0 && !vectors))
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: centroids (and vectors when N > 0) must be non-null", what);
+  int st = check_aligned(what, {vectors, centroids, workspace});
+  if (st) return st;
+  if (iters == 0) return VQ_OK;
+  const size_t need = kmeans_workspace_bytes(N, sub_dim, n_centroids);
+  if (!workspace || workspace_bytes < need)
+    return fail(VQ_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", what, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((st = check_device(what))) return st;
+  KmeansArgs a{};
+  a.vectors = vectors; a.N = N; a.sub_dim = sub_dim; a.n_c = n_centroids; a.iters = iters;
+  a.centroids = centroids; a.labels = labels; a.inertia = inertia;
+  a.partials = reinterpret_cast<double*>(workspace);
+  return hip_status(what, launch_kmeans(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -176,7 +176,9 @@ struct Dims {
   int code_bits;         // 8, or 4: two codes per byte, the even sub-vector in the low nibble
 };
 
-// MODE 0: encode; 1: encode + reconstruct; 2: decode (codes_in -> recon).
+// MODE 0: encode; 1: encode + reconstruct; 2: decode (codes_in -> recon);
+// 3: forward transform only (fp32 (x / s) . H into recon, the vectors a
+// codebook is trained on).
 // CSPLIT waves share one group of token-heads and split the codebook between
 // them (used when there are too few token-heads to fill the chip); their
 // partial argmins are combined through LDS, lowest index first on ties.
@@ -252,6 +254,10 @@ __device__ __forceinline__ void pvq_body(
       for (int e = 0; e < DS; ++e) x[e] = x[e] / sv[e];
     }
     if (d.transform) wht<D, DS>(x, j);
+    if constexpr (MODE == 3) {
+      if (valid) store_f32<DS>(reinterpret_cast<float*>(recon) + thc * D + j * DS, x);
+      return;
+    }
 
     // Nearest centroid: fp32 squared distance summed over e in order,
     // strict '<' keeps the lowest index on exact ties.  The centroid index is
@@ -310,7 +316,7 @@ __device__ __forceinline__ void pvq_body(
     }
   }
 
-  if constexpr (MODE != 0) {
+  if constexpr (MODE == 1 || MODE == 2) {
     const float* cc = cbk + idx * DS;
 #pragma unroll
     for (int e = 0; e < DS; ++e) x[e] = cc[e];
@@ -419,6 +425,10 @@ __global__ __launch_bounds__(kThreads) void pvq_dense_kernel(
         for (int e = 0; e < DS; ++e) x[e] = x[e] / srow[e];
       }
       rotate(x, mat);
+      if constexpr (MODE == 3) {
+        if (valid) store_f32<DS>(reinterpret_cast<float*>(recon) + thc * D + j * DS, x);
+        continue;
+      }
       // nearest centroid (fp32 squared distance over e in order, strict '<')
       float best = INFINITY;
 #pragma unroll 8
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void pvq_dense_kernel(
         idx = min(c, d.n_c - 1);
       }
     }
-    if constexpr (MODE != 0) {
+    if constexpr (MODE == 1 || MODE == 2) {
       const float* cc = cb + idx * DS;
 #pragma unroll
       for (int e = 0; e < DS; ++e) x[e] = cc[e];
@@ -1158,8 +1168,13 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
       const size_t lds = (size_t)(nmat * D * D + kThreads / 64 * 64 / (D / DS) * D) * sizeof(float);
       void (*kern)(const __half*, const uint8_t*, const float*, const float*, const float*,
                    const float*, uint8_t*, void*, Dims, RowOffsets);
-      kern = mode == 0 ? pvq_dense_kernel<D, DS, 0>
-                       : (mode == 1 ? pvq_dense_kernel<D, DS, 1> : pvq_dense_kernel<D, DS, 2>);
+      if (mode == 3) {
+        if constexpr (DS == 8) kern = pvq_dense_kernel<D, DS, 3>;
+        else return hipErrorInvalidValue;
+      } else {
+        kern = mode == 0 ? pvq_dense_kernel<D, DS, 0>
+                         : (mode == 1 ? pvq_dense_kernel<D, DS, 1> : pvq_dense_kernel<D, DS, 2>);
+      }
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
@@ -1176,6 +1191,13 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
       const unsigned blocks = (unsigned)std::max(1LL, std::min(want, (long long)per_cu * cus));
       hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, st, a.keys, a.codes_in, a.codebook,
                          a.smooth, a.rot, a.rot_inv, a.codes, a.recon, d, o);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
+  if (mode == 3) {  // forward transform only: one lane layout suffices
+    if constexpr (DS == 8) {
+      launch_one<D, DS, 3, 1>(a, d, o, st);
       return hipGetLastError();
     }
     return hipErrorInvalidValue;

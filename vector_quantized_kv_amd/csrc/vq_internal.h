@@ -37,7 +37,8 @@ struct EncodeArgs {
   const float* rot_inv;    // transform == 2: [D, D] M^-1 (decode)
 };
 
-// mode 0 = encode, 1 = encode + reconstruct, 2 = decode only.
+// mode 0 = encode, 1 = encode + reconstruct, 2 = decode only, 3 = forward
+// transform only (fp32 into recon; sub_dim must be 8).
 hipError_t launch_encode(const EncodeArgs& a, const RowOffsets* offs, int mode, hipStream_t st);
 // Keys (k) and values (v) of one append, same B, H, S, D and slots; one
 // launch for short appends with a compiled sub_dim pair, else two encodes.
@@ -148,5 +149,19 @@ bool plan_attend(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, A
 int attend_pick_rows(int rows, int nsk, int n_c, int dv, int nsv, int D, size_t* lds_bytes);
 
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, hipStream_t st);
+
+// Lloyd's k-means over vectors [N, sub_dim] fp32 (vq_kmeans.hip).
+struct KmeansArgs {
+  const float* vectors;
+  long long N;
+  int sub_dim, n_c, iters;
+  float* centroids;         // [n_c, sub_dim], updated in place
+  uint8_t* labels;          // NULL or [N]: the last iteration's assignment
+  double* inertia;          // NULL or [iters]
+  double* partials;         // kmeans_workspace_bytes(...) of scratch
+};
+int kmeans_blocks(long long N);
+size_t kmeans_workspace_bytes(long long N, int sub_dim, int n_c);
+hipError_t launch_kmeans(const KmeansArgs& a, hipStream_t st);
 
 }  // namespace vq
