@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused PVQ decode-attn µs/step & HBM GB/s; key encode Mtokens/s"
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 MIB = 1 << 20
 COPY_BYTES = 1 << 30
 ATTEND_SOURCES = ("vq_attend.hip", "vq_attend_mfma.hip", "vq_attend_stream.hip", "vq_attend_tile.hip",
@@ -46,12 +47,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
-    ap.add_argument("--mode", choices=["full", "attend", "encode", "encode_workload", "copy"],
+    ap.add_argument("--mode", choices=["full", "attend", "encode", "encode_workload", "copy", "kmeans"],
                     default="full",
                     help="attend/encode: only launch that entry point of the main workload "
                          "--steps times (for profiler runs); encode_workload: only the key "
                          "encode of [1, 8, 8192, 128] --steps times; copy: a plain elementwise copy "
-                         "of 1 GiB --steps times (calibrates the HBM byte counters); these "
+                         "of 1 GiB --steps times (calibrates the HBM byte counters); kmeans: the "
+                         "codebook-training leg alone; these "
                          "modes print no JSON line")
     return ap.parse_args()
 
@@ -253,10 +255,55 @@ def cpu_baseline(args, c, k_new, v_new, lens):
     }
 
 
+def kmeans_leg(torch, t, dev, iters=10):
+    """Codebook training on the encode workload's keys: vq_transform of
+    [1, 8, 8192, 128] (smooth + WHT, fp32 out), then Lloyd iterations over the
+    1,048,576 sub-vectors of 8 with 256 centroids.  The assignment is a
+    nearest-centroid search on the vector ALUs: per (vector, centroid) pair 8
+    subtractions and 8 multiply-adds (3 d = 24 flops), against the fp32
+    vector peak."""
+    from vector_quantized_kv_amd import synth, vq_kmeans, vq_kmeans_workspace_bytes, vq_transform
+    e = synth.encode()
+    ke, se = t(e["keys"]), t(e["smooth"])
+    vt = torch.empty((1, 8, 8192, 128), dtype=torch.float32, device=dev)
+    f_t = vq_transform(ke, smooth=se, out=vt, prepare=True)
+    us_t = time_events(lambda i: f_t(), 50, torch)
+    f_t()
+    N, d, n_c = 1 << 20, 8, 256
+    init = vt.view(-1, d)[torch.arange(0, N, N // n_c, device=dev)].clone()
+    C = init.clone()
+    ws = torch.empty(vq_kmeans_workspace_bytes(N, d, n_c), dtype=torch.uint8, device=dev)
+    inert = torch.zeros(iters, dtype=torch.float64, device=dev)
+    f_k = vq_kmeans(vt.view(-1, d), C, iters, inertia=inert, workspace=ws, prepare=True)
+
+    def run(i):
+        C.copy_(init)
+        f_k()
+    run(0)
+    us_total = time_events(run, 5, torch, warm=1)
+    us_it = us_total / iters
+    flops = N * n_c * 3 * d
+    tflops = flops / us_it / 1e6
+    log(f"[bench] codebook training: transform {us_t:.1f} us, {us_it:.1f} us per Lloyd iteration "
+        f"({tflops:.1f} TFLOP/s)")
+    return {
+        "shape": "keys [1,8,8192,128] -> 1048576 sub-vectors of 8, 256 centroids",
+        "transform_us": round(us_t, 2),
+        "transform_GBps": round((16777216 + 33554432) / us_t / 1e3, 1),
+        "us_per_iteration": round(us_it, 2), "iterations": iters,
+        "inertia_first_last": [float(inert[0]), float(inert[-1])],
+        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+                     "flops_per_iteration": flops,
+                     "note": "3 d flops per (vector, centroid) pair; the non-packed fp32 issue "
+                             "rate is half the peak"},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library has no "
               "multi-GPU path; the decode attention would shard by (batch row, kv head) with no "
               "exchange.", file=sys.stderr)
         sys.exit(2)
@@ -270,6 +317,10 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if args.mode == "kmeans":
+        log(json.dumps(kmeans_leg(torch, t, dev)))
+        return
 
     if args.mode == "encode_workload":
         e = synth.encode()
@@ -443,6 +494,8 @@ def main():
             "frac_of_argmin_floor": round(argmin_floor_us / us_e, 4),
         }
         log(f"[bench] encode: {us_ed:.1f} us (enc+dec), {us_e:.1f} us (enc)")
+
+        extra["codebook_training"] = kmeans_leg(torch, t, dev)
 
         # single-query decode, B=1 H=8 D=128
         for S in (512, 2048, 8192):
