@@ -497,6 +497,28 @@ def main():
 
         extra["codebook_training"] = kmeans_leg(torch, t, dev)
 
+        # explicit transform matrix (transform = 2): a random orthogonal M in
+        # place of the Walsh-Hadamard rotation, for the key encode and for the
+        # decode step's attention (the query's dual transform runs as a
+        # pre-pass from M^-1)
+        rng_m = np.random.default_rng(7)
+        qm, rm = np.linalg.qr(rng_m.standard_normal((128, 128)))
+        M = qm * np.sign(np.diag(rm))[None, :]
+        Mt, Mit = t(M.astype(np.float32)), t(np.linalg.inv(M).astype(np.float32))
+        f_de = vq_encode(ke, Ce, 8, smooth=se, codes=codes_e, mat=Mt, prepare=True)
+        us_de = time_events(lambda i: f_de(), 20, torch)
+        fdm = [vq_attend(q, kcs[j], Ck, vcs[j], Cv, scale=c["scale"], smooth=sm, kv_lens=kl,
+                         out=out, workspace=ws, mat_inv=Mit, prepare=True) for j in range(n_sets)]
+        us_da = time_events(lambda i: fdm[i % n_sets](), 100, torch)
+        extra["dense_transform"] = {
+            "encode_us": round(us_de, 2), "encode_Mtok_s": round(8192 / us_de, 3),
+            "attend_gqa_long_W0_us": round(us_da, 2),
+            "attend_GBps": round(attn_bytes / us_da / 1e3, 1),
+            "note": "random orthogonal M [128,128] fp32; encode on the dense-matrix kernel "
+                    "(rotation and search on the vector ALUs), attention with the query pre-pass"}
+        log(f"[bench] dense transform: encode {us_de:.1f} us, gqa W=0 attend {us_da:.1f} us")
+        del fdm
+
         # single-query decode, B=1 H=8 D=128
         for S in (512, 2048, 8192):
             d = synth.decode(S)
