@@ -522,6 +522,19 @@ def test_stream_kernel_window_cuts():
     check_attn(out, ref, "stream window 2100")
 
 
+def test_stream_kernel_short_ragged_units():
+    """Many short ragged units (B = 16, GQA-4, lengths 1..2048, no window):
+    the chunk plan charges every segment switch, so whole chunks fall on
+    switch cost and carry no keys, and most chunks hold two or three unit
+    segments; every row against the oracle."""
+    c = small_case(97, B=16, Hq=32, Hkv=8, Sq=1, D=128, dk=8, dv=4, S_cap=2048)
+    c["kv_lens"] = np.random.default_rng(98).integers(1, 2049, size=16).astype(np.int32)
+    c["kv_lens"][:4] = [2048, 1, 0, 513]
+    assert path_of(c) == "stream"
+    out = run_attend(c)
+    check_attn(out, oracle_attend(c, c["k_codes"], c["v_codes"]), "stream short ragged units")
+
+
 @pytest.mark.parametrize("transform,smooth,n_c", [
     (False, "none", 256),     # no rotation, no smoothing
     (True, "shared", 256),    # one smooth row for every kv head

@@ -73,6 +73,10 @@ constexpr uint32_t kLens = kScan + 64;  // int lens[B], clamped to [0, S_cap]
 constexpr uint32_t kPrefix = kLens + 4 * (kMaxUnits + 1);  // int prefix[U + 1]
 constexpr float kLazyMargin = 8.f;
 constexpr int kMaxChunks = 4096;       // partial slots reserved for chunks (>= workgroups)
+// Keys charged for a segment switch when chunks are planned: the combine,
+// the next table build and the refill of the load pipeline cost about as
+// much time as streaming this many keys.
+constexpr int kSegCharge = 2048;
 // int slots of the scan area: 0..3 the chunk plan, kW the block-claim
 // counter, kQExp and kQExp + 1 the exponents of the two query buffers
 constexpr int kQExp = kW + 4;
@@ -331,6 +335,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   // written.  (A wave's LDS accesses execute in issue order, so its reads of
   // lens and pre see its own writes.)
   float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), vq = kq;
+  // value codebook as fp16 rows, replicated 32 times; rotated by code so
+  // that the 16 lanes of a write hit distinct bank quads
+  auto write_val_table = [&]() {
+    const uint32_t h0 = pack_half2(vq.x, vq.y), h1 = pack_half2(vq.z, vq.w);
+    const uint4 two = make_uint4(h0, h1, h0, h1);
+    const int code = tid >> 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint4*>(lds + kValTab + code * 256 + (tid & 1) * 128 + 16 * ((i + code) & 7)) = two;
+  };
   if ((tid >> 1) < p.n_c) {
     kq = reinterpret_cast<const float4*>(k_codebook)[tid];
     vq = reinterpret_cast<const float4*>(v_codebook)[tid >> 1];
@@ -360,28 +374,55 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       carry += __builtin_amdgcn_readlane(incl, 63);
     }
     const int Tw = carry;         // T <= U * S_cap < 2^30 is checked on the host
-    const int C0 = max(p.cmin, (Tw + G - 1) / G);
-    const int st = c * C0 < Tw ? c * C0 : Tw;
-    const int en = min(Tw, st + C0);
     if (lane == 0) pre[p.U] = Tw;
     lds_order();
-    // the nonempty unit holding position st
-    int uf = 0;
-    if (st < Tw) {
+    // Chunks are equal shares of a virtual key space in which every unit
+    // after the first is preceded by p.charge virtual keys (the cost of a
+    // segment switch: combine, table build, refill of the load pipeline, in
+    // keys): unit u owns virtual [vs(u) - charge [u > 0], vs(u) + len) with
+    // vs(u) = pre[u] + charge u, and virtual y in it maps to key
+    // pre[u] + max(0, y - vs(u)).  These spans tile the virtual space (an
+    // empty unit's span maps to the next unit's first key), so every key
+    // falls in exactly one chunk.
+    const int V = Tw + p.charge * (p.U - 1);
+    const int C0 = max(p.cmin, (V + G - 1) / G);
+    const int ys = c * C0 < V ? c * C0 : V;
+    const int ye = min(V, ys + C0);
+    int st = Tw, en = Tw, uf = 0;
+    if (ys < V) {
+      bool found_s = false;
       for (int base = 0; base < p.U; base += 64) {
         const int uu = base + lane;
-        bool hit = false;
+        bool hs = false, he = false;
+        int a0 = 0, vs = 0;
         if (uu < p.U) {
-          const int a0 = pre[uu], a1 = pre[uu + 1];
-          hit = a0 < a1 && a0 <= st && st < a1;
+          a0 = pre[uu];
+          const int a1 = pre[uu + 1];
+          vs = a0 + p.charge * uu;
+          const int lo = uu > 0 ? vs - p.charge : vs, hi = vs + (a1 - a0);
+          hs = lo <= ys && ys < hi;
+          he = lo < ye && ye <= hi;   // the unit holding the chunk's last key
         }
-        const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
-        if (m) {
-          uf = base + (int)__builtin_ctzll(m);
+        const uint64_t ms = __builtin_amdgcn_ballot_w64(hs);
+        const uint64_t me = __builtin_amdgcn_ballot_w64(he);
+        if (ms && !found_s) {
+          const int l = (int)__builtin_ctzll(ms);
+          uf = base + l;
+          st = __builtin_amdgcn_readlane(a0 + max(0, ys - vs), l);
+          found_s = true;
+        }
+        if (me) {
+          const int l = (int)__builtin_ctzll(me);
+          en = __builtin_amdgcn_readlane(a0 + max(0, ye - vs), l);
           break;
         }
       }
-      qraw = query_load(uf);
+      if (st >= en) {
+        st = en = Tw;  // the chunk holds switch cost only
+      } else {
+        while (pre[uf + 1] == pre[uf]) ++uf;  // an empty unit's span maps onto the next start
+        qraw = query_load(uf);
+      }
     }
     if (lane == 0) {
       plan[0] = Tw;
@@ -395,13 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // per-wave maximum magnitude of the key codebook
     const float kmx = wave_max_u(fmaxf(fmaxf(fabsf(kq.x), fabsf(kq.y)), fmaxf(fabsf(kq.z), fabsf(kq.w))));
     if (lane == 0) reinterpret_cast<float*>(lds + kWaveMax)[wave] = kmx;
-    const uint32_t h0 = pack_half2(vq.x, vq.y), h1 = pack_half2(vq.z, vq.w);
-    const uint4 two = make_uint4(h0, h1, h0, h1);
-    const int code = tid >> 1;
-    // rotated by code so that the 16 lanes of a write hit distinct bank quads
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4*>(lds + kValTab + code * 256 + (tid & 1) * 128 + 16 * ((i + code) & 7)) = two;
+    write_val_table();
   }
   __syncthreads();
   const int* const lens = lens_w;
@@ -909,6 +944,10 @@ bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, i
   if (sp) {
     sp->B = B; sp->Hq = Hq; sp->Sq = Sq; sp->Hkv = Hkv; sp->S_cap = S_cap; sp->n_c = n_c;
     sp->G = (int)G; sp->GS = (int)GS; sp->n_rg = (int)n_rg; sp->U = (int)U; sp->cmin = kW * 64;
+    // units of a sliding window usually have equal lengths, which equal
+    // shares tend to split at unit starts: charging switches there only
+    // breaks that alignment
+    sp->charge = window > 0 ? 0 : kSegCharge;
     sp->div_g = make_fastdiv((uint32_t)G);
     sp->div_nrg = make_fastdiv((uint32_t)n_rg);
     sp->div_hkv = make_fastdiv((uint32_t)Hkv);

@@ -113,6 +113,7 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
 struct StreamParams {
   int B, Hq, Sq, Hkv, S_cap, n_c, smooth_rows, transform, causal, window;
   int G, GS, n_rg, U, cmin;
+  int charge;  // virtual keys charged for a segment switch in the chunk plan
   FastDiv div_g, div_nrg, div_hkv;  // by G, n_rg and H_kv
   float fold;  // WHT normalization (if any) * scale * log2(e)
 };
