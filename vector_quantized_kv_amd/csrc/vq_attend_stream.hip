@@ -34,6 +34,12 @@
 // LDS byte address of a gathered row has the code in byte 1, so one v_perm
 // per code both extracts the code byte and forms the address.
 //
+// 4-bit codes (at most 16 centroids): the score table is built for the 16
+// codes into scratch, then expanded into a byte-pair table LUT2[byte][slot]
+// [row] = LUT[byte & 15][2 p][row] + LUT[byte >> 4][2 p + 1][row] (p = slot
+// mod 8, slots p and p + 8 duplicated so 16 lanes read 16 distinct bank
+// quads): a key's 8 code bytes need 8 gathers and 28 adds.
+//
 // Per 64-key block and wave (lane = key for the scores):
 //   scores  16 b128 table gathers and 60 fp32 adds: 4 rows at once.
 //   softmax lazy: the running max m_r moves only when a score exceeds it by
@@ -473,6 +479,19 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       w |= (uint32_t)(16 * (4 * ((a + rdw) & 3) + ((b + rb) & 3))) << (8 * b);
     jt[a] = w;
   }
+  if constexpr (BITS == 4) {
+    // pair table [byte][slot][row]: at step k = 4 a + b the lane reads byte
+    // pair p = 4 ((a + rdw) mod 2) + (b + rb) mod 4 (sub-vectors 2p, 2p + 1)
+    // from slot p + 8 ((lane / 8) mod 2), 16 distinct slots over 16 lanes
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        w |= (uint32_t)(16 * (4 * ((a + rdw) & 1) + ((b + rb) & 3) + 8 * ((lane >> 3) & 1))) << (8 * b);
+      jt[a] = w;
+    }
+  }
 #pragma unroll
   for (int b = 0; b < 4; ++b) sel[b] = 0x0c0c0000u | ((4u + ((b + rb) & 3)) << 8) | (uint32_t)b;
   const uint32_t vbase = (uint32_t)(lane & 31) * 8u | (1u << 16);      // value replica + 64 KiB
@@ -596,7 +615,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       // K = the 8 dims of a sub-vector.  Both operands are scaled by powers
       // of two into [2^13, 2^14) and split into fp16 high and low parts; the
       // products hi.hi + lo.hi + hi.lo carry the result to fp32 accuracy.
-      {
+      // 4-bit codes: wave 0 builds the 16-code table into the p staging
+      // area; the byte-pair table LUT2[byte][slot][r] = LUT[b & 15][2 p][r] +
+      // LUT[b >> 4][2 p + 1][r] (p = slot mod 8) then fills the table area.
+      if (BITS == 8 || wave == 0) {
         const int l32 = lane & 31, kh = lane >> 5;
         const int eq = scan[kQExp + qbuf];
         const float* cbk = reinterpret_cast<const float*>(lds + kCbk);
@@ -618,8 +640,23 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int code = 32 * wave + 8 * (v >> 2) + 4 * kh + (v & 3);
-            *reinterpret_cast<float*>(lds + kLut + code * 256 + 128 * t2 + 4 * l32) = ldexpf(d[v], unscale);
+            if constexpr (BITS == 8)
+              *reinterpret_cast<float*>(lds + kLut + code * 256 + 128 * t2 + 4 * l32) = ldexpf(d[v], unscale);
+            else if (code < 16)
+              *reinterpret_cast<float*>(lds + kPStage + code * 256 + 128 * t2 + 4 * l32) = ldexpf(d[v], unscale);
           }
+        }
+      }
+      if constexpr (BITS == 4) {
+        __syncthreads();
+        const float* small = reinterpret_cast<const float*>(lds + kPStage);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e = tid + kThreads * i;  // (byte, slot) = (e / 16, e mod 16)
+          const int byte = e >> 4, pr = e & 7;
+          const float4 x = *reinterpret_cast<const float4*>(small + 64 * (byte & 15) + 4 * (2 * pr));
+          const float4 y = *reinterpret_cast<const float4*>(small + 64 * (byte >> 4) + 4 * (2 * pr + 1));
+          *reinterpret_cast<float4*>(lds + kLut + 16 * e) = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
         }
       }
     }
@@ -665,43 +702,49 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       // halves, each overlapping half of the previous block's value MFMAs
       float4_t sc;
       {
-        // dw[a] = kw[(a + rdw) mod 4]: rotate by rdw bit 0, then by bit 1,
-        // with bit selects (no divergent branches)
-        uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
-        if constexpr (BITS == 4) {
-          // nibbles to bytes: word d of the key holds sub-vectors 8 d .. 8 d + 7
-          // (the even one of each pair in the low nibble); kw[2 d + h] gets
-          // sub-vectors 8 d + 4 h .. 8 d + 4 h + 3, one per byte
+        if constexpr (BITS == 8) {
+          // dw[a] = kw[(a + rdw) mod 4]: rotate by rdw bit 0, then by bit 1,
+          // with bit selects (no divergent branches)
+          const uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+          uint32_t r1[4], dw[4];
 #pragma unroll
-          for (int d2 = 1; d2 >= 0; --d2) {
-            const uint32_t w = d2 ? kc.y : kc.x;
-            const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-            kw[2 * d2] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-            kw[2 * d2 + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-          }
+          for (int a = 0; a < 4; ++a) r1[a] = (kw[(a + 1) & 3] & rot1) | (kw[a] & ~rot1);
+#pragma unroll
+          for (int a = 0; a < 4; ++a) dw[a] = (r1[(a + 2) & 3] & rot2) | (r1[a] & ~rot2);
+          float4_t L[8];
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              L[4 * a + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw[a], jt[a], sel[b]));
+          __builtin_amdgcn_sched_barrier(0);
+          if (pending) value_mfmas(lo_half);
+          sc = ((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]));
+#pragma unroll
+          for (int a = 2; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              L[4 * (a - 2) + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw[a], jt[a], sel[b]));
+          __builtin_amdgcn_sched_barrier(0);
+          if (pending) value_mfmas(hi_half);
+          sc += ((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]));
+        } else {
+          // 4-bit: the 8 code bytes (sub-vector pairs) of the key, words
+          // swapped by rdw bit 0; one pair-table gather per byte
+          const uint32_t dw[2] = {(kc.y & rot1) | (kc.x & ~rot1), (kc.x & rot1) | (kc.y & ~rot1)};
+          float4_t L[8];
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            L[b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw[0], jt[0], sel[b]));
+          __builtin_amdgcn_sched_barrier(0);
+          if (pending) value_mfmas(lo_half);
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            L[4 + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw[1], jt[1], sel[b]));
+          __builtin_amdgcn_sched_barrier(0);
+          if (pending) value_mfmas(hi_half);
+          sc = ((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]));
         }
-        uint32_t r1[4], dw[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) r1[a] = (kw[(a + 1) & 3] & rot1) | (kw[a] & ~rot1);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) dw[a] = (r1[(a + 2) & 3] & rot2) | (r1[a] & ~rot2);
-        float4_t L[8];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            L[4 * a + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw[a], jt[a], sel[b]));
-        __builtin_amdgcn_sched_barrier(0);
-        if (pending) value_mfmas(lo_half);
-        sc = ((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]));
-#pragma unroll
-        for (int a = 2; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            L[4 * (a - 2) + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw[a], jt[a], sel[b]));
-        __builtin_amdgcn_sched_barrier(0);
-        if (pending) value_mfmas(hi_half);
-        sc += ((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]));
       }
 
       // ---- masks and lazy online softmax -------------------------------
