@@ -143,6 +143,8 @@ def check_step(tag, vec_ref, vec_gpu, tbound, init, C_gpu, lab_gpu, e_gpu):
     (1, 2, 100, 64, 2, 32, "values"),
     (1, 1, 70, 32, 1, 8, "keys"),
     (1, 1, 3, 32, 8, 256, "keys"),          # fewer vectors (12) than centroids
+    (1, 8, 600, 128, 8, 256, "keys"),       # 76,800 sub-vectors of 8: the matrix-core search
+    (2, 2, 1100, 128, 8, 16, "keys"),       # 70,400 of 8, a 16-centroid codebook
 ])
 def test_lloyd_step(B, H, S, D, d, n_c, kind):
     """vq_transform then one vq_kmeans iteration, from centroids sampled from
@@ -167,12 +169,13 @@ def test_lloyd_step(B, H, S, D, d, n_c, kind):
                float(inertia.cpu().numpy()[0]))
 
 
-def test_separated_blobs_many_iterations():
+@pytest.mark.parametrize("n", [300, 1100])
+def test_separated_blobs_many_iterations(n):
     """Blobs far apart: ten GPU iterations land on the oracle's centroids,
     labels equal throughout (no near-ties exist), and the inertia sequence
-    matches."""
-    rng = np.random.default_rng(5200)
-    k, n, d = 64, 300, 8
+    matches (64 x 1100 vectors run the matrix-core search)."""
+    rng = np.random.default_rng(5200 + n)
+    k, d = 64, 8
     centres = rng.standard_normal((k, d)) * 50
     x = np.concatenate([c + rng.standard_normal((n, d)) for c in centres]).astype(np.float32)
     blob = np.repeat(np.arange(k), n)

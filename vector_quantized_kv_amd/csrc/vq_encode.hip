@@ -1264,7 +1264,215 @@ bool try_kv_fused(const EncodeArgs& k, const EncodeArgs& v, const RowOffsets& o,
   return true;
 }
 
+
+// Lloyd assignment of fp32 sub-vectors of 8 on the matrix cores: the search
+// of pvq_f16_kernel (|c|^2 - 2 c.x on v_mfma_f32_32x32x8_f16 with split-fp16
+// operands and power-of-two scales, lowest index on ties; a rescaled step
+// when values would leave the fp16 range) over vectors [N, 8], followed by
+// the accumulation of the vector-ALU assignment kernel: per-centroid fp64
+// sums and counts in LDS and the direct fp32 distance to the chosen
+// centroid, written to the workgroup's row of partials.  Twelve waves per
+// workgroup (three per SIMD), a wave step is 64 vectors.
+constexpr int kKmWaves = 12;
+__global__ __launch_bounds__(kKmWaves * 64) void kmeans_f16_kernel(
+    const float* __restrict__ vecs, long long N, const float* __restrict__ cb, int n_c,
+    double* __restrict__ partials, uint8_t* __restrict__ labels) {
+  constexpr int DS = 8, W = DS + 1, NT = kKmWaves * 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hi = lane >> 5, l32 = lane & 31;
+  __shared__ double acc[256 * W + 1];
+  __shared__ float s_red[kKmWaves];
+  __shared__ half4_t s_ah[8 * 64], s_al[8 * 64];
+  __shared__ float s_norm[256];
+  __shared__ float s_seeded[kKmWaves][256];
+  const int slots = n_c * W + 1;
+  for (int i = threadIdx.x; i < slots; i += NT) acc[i] = 0.0;
+  int sc;
+  {
+    const int c = threadIdx.x;
+    float m = 0.f;
+    if (c < n_c) {
+#pragma unroll
+      for (int e = 0; e < DS; ++e) m = fmaxf(m, fabsf(cb[c * DS + e]));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    m = 0.f;
+#pragma unroll
+    for (int w = 0; w < kKmWaves; ++w) m = fmaxf(m, s_red[w]);
+    sc = m > 0.f ? 14 - __builtin_amdgcn_frexp_expf(m) : 0;
+    if (c < 256) {
+      float n = INFINITY;
+      if (c < n_c) {
+        n = 0.f;
+#pragma unroll
+        for (int e = 0; e < DS; ++e) {
+          const float v = ldexpf(cb[c * DS + e], sc);
+          n = fmaf(v, v, n);
+        }
+      }
+      s_norm[c] = n;
+    }
+    if (wave < 4) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int T = 2 * wave + r;
+        const int cc = 32 * T + l32;
+        half4_t ah, al;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float v = cc < n_c ? -2.f * ldexpf(cb[cc * DS + 4 * hi + u], sc) : 0.f;
+          ah[u] = (_Float16)v;
+          al[u] = (_Float16)(v - (float)ah[u]);
+        }
+        s_ah[T * 64 + lane] = ah;
+        s_al[T * 64 + lane] = al;
+      }
+    }
+  }
+  __syncthreads();
+
+  double inert = 0.0;
+  const long long n_steps = (N + 63) / 64;
+  for (long long step = (long long)blockIdx.x * kKmWaves + wave; step < n_steps;
+       step += (long long)gridDim.x * kKmWaves) {
+    // lane l holds elements 4 (l / 32) + u of vectors 64 step + 32 g + l mod 32
+    float x[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const long long row = step * 64 + 32 * g + l32;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row < N) v = *reinterpret_cast<const float4*>(vecs + row * DS + 4 * hi);
+      x[g][0] = v.x; x[g][1] = v.y; x[g][2] = v.z; x[g][3] = v.w;
+    }
+    float mx = 0.f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fabsf(x[g][u]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    int s = sc;
+    const float* nrm = s_norm;
+    if (ldexpf(mx, sc) >= 32768.f) {
+      s = 14 - __builtin_amdgcn_frexp_expf(mx);
+      float* w = s_seeded[wave];
+      const float4 nv = *reinterpret_cast<const float4*>(s_norm + 4 * lane);
+      const float f = ldexpf(1.f, s - sc);
+      *reinterpret_cast<float4*>(w + 4 * lane) = make_float4(nv.x * f, nv.y * f, nv.z * f, nv.w * f);
+      nrm = w;
+    }
+    half4_t bh[2], bl[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float v = ldexpf(x[g][u], s);
+        bh[g][u] = (_Float16)v;
+        bl[g][u] = (_Float16)(v - (float)bh[g][u]);
+      }
+    struct TileIn {
+      half4_t ah, al;
+      float16_t n;
+    };
+    float best[2] = {INFINITY, INFINITY};
+    int bi[2] = {0, 0}, bt[2] = {0, 0};
+    auto tile_in = [&](int T) {
+      asm volatile("" ::: "memory");
+      TileIn t;
+      t.ah = s_ah[T * 64 + lane];
+      t.al = s_al[T * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 nv = *reinterpret_cast<const float4*>(nrm + 32 * T + 8 * q + 4 * hi);
+        t.n[4 * q] = nv.x; t.n[4 * q + 1] = nv.y; t.n[4 * q + 2] = nv.z; t.n[4 * q + 3] = nv.w;
+      }
+      return t;
+    };
+    auto chains = [&](const TileIn& t, float16_t (&a)[2]) {
+      a[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bh[0], t.n, 0, 0, 0);
+      a[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bh[1], t.n, 0, 0, 0);
+      a[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.al, bh[0], a[0], 0, 0, 0);
+      a[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.al, bh[1], a[1], 0, 0, 0);
+      a[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bl[0], a[0], 0, 0, 0);
+      a[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bl[1], a[1], 0, 0, 0);
+    };
+    auto scan = [&](const float16_t (&r)[2], int T) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float before = best[g];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (r[g][v] < best[g]) { best[g] = r[g][v]; bi[g] = 8 * (v >> 2) + (v & 3); }
+        if (best[g] < before) bt[g] = T;
+      }
+    };
+    float16_t a[2];
+    chains(tile_in(0), a);
+    TileIn nxt_in = tile_in(1);
+#pragma unroll
+    for (int T = 0; T < 8; ++T) {
+      float16_t r[2] = {a[0], a[1]};
+      if (T + 1 < 8) {
+        chains(nxt_in, a);
+        if (T + 2 < 8) nxt_in = tile_in(T + 2);
+      }
+      scan(r, T);
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        asm volatile("" : "+v"(best[g]), "+v"(bi[g]), "+v"(bt[g]), "+v"(a[g]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // merge lanes l and l ^ 32, lowest index on ties; then accumulate
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float bv = best[g];
+      int bx = 32 * bt[g] + bi[g] + 4 * hi;
+      const float ov = __shfl_xor(bv, 32);
+      const int ox = __shfl_xor(bx, 32);
+      if (ov < bv || (ov == bv && ox < bx)) bx = ox;
+      const int ci = min(bx, n_c - 1);
+      const float4 cv = *reinterpret_cast<const float4*>(cb + ci * DS + 4 * hi);
+      const float cvv[4] = {cv.x, cv.y, cv.z, cv.w};
+      float d = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float df = x[g][u] - cvv[u];
+        d = fmaf(df, df, d);
+      }
+      d += __shfl_xor(d, 32);
+      const long long row = step * 64 + 32 * g + l32;
+      if (row < N) {
+        double* slot = acc + ci * W;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) atomicAdd(slot + 4 * hi + u, (double)x[g][u]);
+        if (!hi) {
+          atomicAdd(slot + DS, 1.0);
+          inert += (double)d;
+          if (labels) labels[row] = (uint8_t)ci;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) inert += __shfl_xor(inert, m);
+  if (lane == 0) atomicAdd(acc + n_c * W, inert);
+  __syncthreads();
+  double* row = partials + (size_t)blockIdx.x * slots;
+  for (int i = threadIdx.x; i < slots; i += NT) row[i] = acc[i];
+}
+
 }  // namespace
+
+hipError_t launch_kmeans_assign_f16(const float* vecs, long long N, const float* cb, int n_c,
+                                    double* partials, int blocks, uint8_t* labels, hipStream_t st) {
+  hipLaunchKernelGGL(kmeans_f16_kernel, dim3(blocks), dim3(kKmWaves * 64), 0, st, vecs, N, cb, n_c,
+                     partials, labels);
+  return hipGetLastError();
+}
 
 hipError_t launch_encode_kv(const EncodeArgs& k, const EncodeArgs& v, const RowOffsets* offs,
                             hipStream_t st) {

@@ -164,5 +164,9 @@ struct KmeansArgs {
 int kmeans_blocks(long long N);
 size_t kmeans_workspace_bytes(long long N, int sub_dim, int n_c);
 hipError_t launch_kmeans(const KmeansArgs& a, hipStream_t st);
+// The assignment step for sub-vectors of 8 on the matrix cores (vq_encode.hip):
+// writes the same per-workgroup partial rows as the vector-ALU kernel.
+hipError_t launch_kmeans_assign_f16(const float* vecs, long long N, const float* cb, int n_c,
+                                    double* partials, int blocks, uint8_t* labels, hipStream_t st);
 
 }  // namespace vq

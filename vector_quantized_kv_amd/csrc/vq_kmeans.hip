@@ -12,7 +12,10 @@
 //
 // One iteration is two launches on the caller's stream, with no host
 // synchronization between iterations:
-//   assign  at most one 16-wave workgroup per CU.  A lane takes one vector at
+//   assign  sub-vectors of 8, from 65,536 of them: the encode's matrix-core
+//           search (kmeans_f16_kernel in the encode source) with the same
+//           accumulation as below.  Otherwise:
+//           at most one 16-wave workgroup per CU.  A lane takes one vector at
 //           a time (grid-stride), walks the codebook with a wave-uniform
 //           centroid index (scalar loads shared by the 64 lanes), and adds
 //           the vector, a count and its smallest distance into fp64
@@ -31,6 +34,10 @@ namespace {
 
 constexpr int kAssignThreads = 1024;  // 16 waves
 constexpr int kUpdateThreads = 256;
+// From this many vectors of 8 the assignment runs on the matrix cores (the
+// encode's split-fp16 search); below it the direct fp32 search, whose
+// decisions match the per-lane encode exactly.
+constexpr long long kMatrixMin = 65536;
 
 template <int DS>
 __device__ __forceinline__ void load_vec(const float* __restrict__ p, float (&x)[DS]) {
@@ -158,8 +165,15 @@ template <int DS>
 hipError_t run_kmeans(const KmeansArgs& a, hipStream_t st) {
   const int G = kmeans_blocks(a.N);
   for (int it = 0; it < a.iters; ++it) {
-    hipLaunchKernelGGL(kmeans_assign_kernel<DS>, dim3(G), dim3(kAssignThreads), 0, st, a.vectors,
-                       a.N, a.centroids, a.n_c, a.partials, it + 1 == a.iters ? a.labels : nullptr);
+    uint8_t* labels = it + 1 == a.iters ? a.labels : nullptr;
+    if (DS == 8 && a.N >= kMatrixMin) {
+      const hipError_t e = launch_kmeans_assign_f16(a.vectors, a.N, a.centroids, a.n_c, a.partials, G,
+                                                    labels, st);
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL(kmeans_assign_kernel<DS>, dim3(G), dim3(kAssignThreads), 0, st, a.vectors,
+                         a.N, a.centroids, a.n_c, a.partials, labels);
+    }
     hipLaunchKernelGGL(kmeans_update_kernel<DS>, dim3(a.n_c + 1), dim3(kUpdateThreads), 0, st,
                        a.partials, G, a.n_c, a.centroids, a.inertia ? a.inertia + it : nullptr);
     const hipError_t e = hipGetLastError();
