@@ -230,11 +230,13 @@ size_t vq_kmeans_workspace_bytes(long long N, int sub_dim, int n_centroids);
  * The pages encode keys against a pre-trained codebook ("veloxquant_mlx.
  * cache.vecinfer_cache module" page, module description) and say no more;
  * this is the plain k-means reading of that training.  Each iteration
- * assigns every vector to its nearest centroid (the encode's rule: fp32
+ * assigns every vector to its nearest centroid by the encode's rules (fp32
  * squared distance summed over the sub-vector in index order, lowest index
- * on exact ties), then moves every centroid to the mean of its members
+ * on exact ties; from 65,536 vectors of sub_dim 8, the matrix-core encode's
+ * fp32-accurate argmin of |c|^2 - 2 c.x, which can differ from the former
+ * only at near-ties), then moves every centroid to the mean of its members
  * (summed in fp64, rounded to fp32); a centroid with no member keeps its
- * value.
+ * value.  The inertia adds the direct fp32 distances.
  *
  *   vectors     [N, sub_dim] fp32 (e.g. vq_transform's output of the keys,
  *               or raw values converted to fp32); NULL allowed when N = 0
