@@ -342,6 +342,172 @@ __global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kernel(
   pvq_body<D, DS, MODE, CSPLIT>(blockIdx.x, keys, codes_in, cb, smooth, codes, recon, d, offs);
 }
 
+// ---------------------------------------------------------------------------
+// Nearest centroid for rows of 8 on the matrix cores (the search of
+// pvq_f16_kernel below, as helpers for the k-means and dense-matrix kernels):
+// |c|^2 - 2 c.x on v_mfma_f32_32x32x8_f16 with each operand split into fp16
+// high and low parts (three passes), the codebook scaled by 2^sc (largest
+// |C| in [2^13, 2^14)) and a step's rows by the same scale unless they would
+// leave the fp16 range (then their own scale, with rescaled norm seeds).
+// Layout: lane l holds elements 4 (l / 32) + u of rows 32 g + l mod 32 of a
+// 64-row step; candidates run in increasing index order, the lanes l and
+// l ^ 32 holding the two halves of a tile merge lowest index first.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+struct F16Codebook {
+  half4_t ah[8 * 64], al[8 * 64];  // A operands [tile][lane], -2 C 2^sc hi and lo
+  float norm[256];                 // |C 2^sc|^2, +inf past n_c
+};
+
+// Stage a codebook of up to 256 rows of 8: every thread of the workgroup
+// (NT >= 256) takes part; ends with a barrier.  Returns sc.
+template <int NT>
+__device__ __forceinline__ int f16_stage(const float* __restrict__ cb, int n_c, F16Codebook& t,
+                                         float* s_red) {
+  constexpr int DS = 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int c = threadIdx.x;
+  float m = 0.f;
+  if (c < n_c) {
+#pragma unroll
+    for (int e = 0; e < DS; ++e) m = fmaxf(m, fabsf(cb[c * DS + e]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) m = fmaxf(m, s_red[w]);
+  const int sc = m > 0.f ? 14 - __builtin_amdgcn_frexp_expf(m) : 0;
+  if (c < 256) {
+    float n = INFINITY;
+    if (c < n_c) {
+      n = 0.f;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) {
+        const float v = ldexpf(cb[c * DS + e], sc);
+        n = fmaf(v, v, n);
+      }
+    }
+    t.norm[c] = n;
+  }
+  if (wave < 4) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int T = 2 * wave + r;
+      const int cc = 32 * T + l32;
+      half4_t ah, al;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float v = cc < n_c ? -2.f * ldexpf(cb[cc * DS + 4 * hi + u], sc) : 0.f;
+        ah[u] = (_Float16)v;
+        al[u] = (_Float16)(v - (float)ah[u]);
+      }
+      t.ah[T * 64 + lane] = ah;
+      t.al[T * 64 + lane] = al;
+    }
+  }
+  __syncthreads();
+  return sc;
+}
+
+// Nearest centroids of the two rows a lane holds (idx[g]: row 32 g + l mod
+// 32, the same in lanes l and l ^ 32).  seeded: this wave's 256 floats.
+__device__ __forceinline__ void f16_nearest(const float (&x)[2][4], int sc, const F16Codebook& t,
+                                            float* seeded, int n_c, int (&idx)[2]) {
+  const int lane = threadIdx.x & 63;
+  const int hi = lane >> 5;
+  float mx = 0.f;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fabsf(x[g][u]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  int s = sc;
+  const float* nrm = t.norm;
+  if (ldexpf(mx, sc) >= 32768.f) {
+    s = 14 - __builtin_amdgcn_frexp_expf(mx);
+    const float4 nv = *reinterpret_cast<const float4*>(t.norm + 4 * lane);
+    const float f = ldexpf(1.f, s - sc);
+    *reinterpret_cast<float4*>(seeded + 4 * lane) = make_float4(nv.x * f, nv.y * f, nv.z * f, nv.w * f);
+    nrm = seeded;
+  }
+  half4_t bh[2], bl[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float v = ldexpf(x[g][u], s);
+      bh[g][u] = (_Float16)v;
+      bl[g][u] = (_Float16)(v - (float)bh[g][u]);
+    }
+  struct TileIn {
+    half4_t ah, al;
+    float16_t n;
+  };
+  float best[2] = {INFINITY, INFINITY};
+  int bi[2] = {0, 0}, bt[2] = {0, 0};
+  auto tile_in = [&](int T) {
+    asm volatile("" ::: "memory");
+    TileIn ti;
+    ti.ah = t.ah[T * 64 + lane];
+    ti.al = t.al[T * 64 + lane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 nv = *reinterpret_cast<const float4*>(nrm + 32 * T + 8 * q + 4 * hi);
+      ti.n[4 * q] = nv.x; ti.n[4 * q + 1] = nv.y; ti.n[4 * q + 2] = nv.z; ti.n[4 * q + 3] = nv.w;
+    }
+    return ti;
+  };
+  auto chains = [&](const TileIn& ti, float16_t (&a)[2]) {
+    a[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(ti.ah, bh[0], ti.n, 0, 0, 0);
+    a[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(ti.ah, bh[1], ti.n, 0, 0, 0);
+    a[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(ti.al, bh[0], a[0], 0, 0, 0);
+    a[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(ti.al, bh[1], a[1], 0, 0, 0);
+    a[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(ti.ah, bl[0], a[0], 0, 0, 0);
+    a[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(ti.ah, bl[1], a[1], 0, 0, 0);
+  };
+  auto scan = [&](const float16_t (&r)[2], int T) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float before = best[g];
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (r[g][v] < best[g]) { best[g] = r[g][v]; bi[g] = 8 * (v >> 2) + (v & 3); }
+      if (best[g] < before) bt[g] = T;
+    }
+  };
+  float16_t a[2];
+  chains(tile_in(0), a);
+  TileIn nxt_in = tile_in(1);
+#pragma unroll
+  for (int T = 0; T < 8; ++T) {
+    float16_t r[2] = {a[0], a[1]};
+    if (T + 1 < 8) {
+      chains(nxt_in, a);
+      if (T + 2 < 8) nxt_in = tile_in(T + 2);
+    }
+    scan(r, T);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      asm volatile("" : "+v"(best[g]), "+v"(bi[g]), "+v"(bt[g]), "+v"(a[g]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float bv = best[g];
+    int bx = 32 * bt[g] + bi[g] + 4 * hi;
+    const float ov = __shfl_xor(bv, 32);
+    const int ox = __shfl_xor(bx, 32);
+    if (ov < bv || (ov == bv && ox < bx)) bx = ox;
+    idx[g] = min(bx, n_c - 1);
+  }
+}
+
 // Dense rotation (transform == 2): an explicit invertible [D, D] matrix M,
 // the H_mat argument of vecinfer_encode_decode_metal ("Metal Kernels API",
 // "VecInfer kernels"): encode rotates x / s by M (x~ = (x / s) . M, a row
@@ -350,16 +516,22 @@ __global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kernel(
 // forms its sub_dim outputs y[e] = sum_i x[i] A[i][j d + e] with the
 // matrix A held in LDS for the whole (grid-stride) launch.  fp32 products
 // summed in index order; then the same nearest-centroid search.
-template <int D, int DS, int MODE>
-__global__ __launch_bounds__(kThreads) void pvq_dense_kernel(
+template <int D, int DS, int MODE, int NT>
+__global__ __launch_bounds__(NT) void pvq_dense_kernel(
     const __half* __restrict__ keys, const uint8_t* __restrict__ codes_in,
     const float* __restrict__ cb, const float* __restrict__ smooth,
     const float* __restrict__ rot, const float* __restrict__ rot_inv,
     uint8_t* __restrict__ codes, void* __restrict__ recon, Dims d, RowOffsets offs) {
   constexpr int NSUB = D / DS;      // lanes per token-head
   constexpr int TPW = 64 / NSUB;    // token-heads per wave step
-  constexpr int WPB = kThreads / 64;
+  constexpr int WPB = NT / 64;
   constexpr int NMAT = MODE == 1 ? 2 : 1;  // M (encode), M^-1 (decode), or both
+  // sub-vectors of 8 with 8-bit codes: the nearest centroid on the matrix
+  // cores (f16_nearest), after moving the rows into its lane layout
+  constexpr bool kMF = DS == 8 && (MODE == 0 || MODE == 1);
+  __shared__ std::conditional_t<kMF, F16Codebook, char> tab;
+  __shared__ float s_red[WPB];
+  __shared__ std::conditional_t<kMF, float[WPB][256], char> s_seeded;
   extern __shared__ __align__(16) float dl[];
   float* const mat = dl;                          // [NMAT][D][D]
   float* const xs = dl + NMAT * D * D;            // [WPB][TPW][D] staged vectors
@@ -368,13 +540,17 @@ __global__ __launch_bounds__(kThreads) void pvq_dense_kernel(
   const int j = lane % NSUB, tok = lane / NSUB;
   {
     const float* src0 = MODE == 2 ? rot_inv : rot;
-    for (int i = threadIdx.x; i < D * D / 4; i += kThreads)
+    for (int i = threadIdx.x; i < D * D / 4; i += NT)
       reinterpret_cast<float4*>(mat)[i] = reinterpret_cast<const float4*>(src0)[i];
     if constexpr (MODE == 1)
-      for (int i = threadIdx.x; i < D * D / 4; i += kThreads)
+      for (int i = threadIdx.x; i < D * D / 4; i += NT)
         reinterpret_cast<float4*>(mat + D * D)[i] = reinterpret_cast<const float4*>(rot_inv)[i];
   }
   __syncthreads();
+  int sc = 0;
+  if constexpr (kMF) {
+    if (d.code_bits == 8) sc = f16_stage<NT>(cb, d.n_c, tab, s_red);
+  }
   float* const xw = xs + (wave * TPW + tok) * D;  // this lane's token-head vector
   // y = x . A for the lane's sub-vector: x staged in xw (the wave's own LDS
   // accesses execute in issue order, so the reads see the writes)
@@ -429,18 +605,41 @@ __global__ __launch_bounds__(kThreads) void pvq_dense_kernel(
         if (valid) store_f32<DS>(reinterpret_cast<float*>(recon) + thc * D + j * DS, x);
         continue;
       }
-      // nearest centroid (fp32 squared distance over e in order, strict '<')
-      float best = INFINITY;
-#pragma unroll 8
-      for (int c = 0; c < d.n_c; ++c) {
-        const float* cc = cb + c * DS;
-        float acc = 0.f;
+      bool searched = false;
+      if constexpr (kMF) {
+        if (d.code_bits == 8) {
+          // row r of the step is lane r; the matrix-core layout wants
+          // elements 4 (l / 32) + u of rows 32 g + l mod 32 in lane l
+          const int hi = lane >> 5, l32 = lane & 31;
+          float xm[2][4];
 #pragma unroll
-        for (int e = 0; e < DS; ++e) {
-          const float df = x[e] - cc[e];
-          acc = fmaf(df, df, acc);
+          for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float lo_v = __shfl(x[u], 32 * g + l32);
+              const float hi_v = __shfl(x[4 + u], 32 * g + l32);
+              xm[g][u] = hi ? hi_v : lo_v;
+            }
+          int ids[2];
+          f16_nearest(xm, sc, tab, s_seeded[wave], d.n_c, ids);
+          idx = hi ? ids[1] : ids[0];
+          searched = true;
         }
-        if (acc < best) { best = acc; idx = c; }
+      }
+      if (!searched) {
+        // nearest centroid (fp32 squared distance over e in order, strict '<')
+        float best = INFINITY;
+#pragma unroll 8
+        for (int c = 0; c < d.n_c; ++c) {
+          const float* cc = cb + c * DS;
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < DS; ++e) {
+            const float df = x[e] - cc[e];
+            acc = fmaf(df, df, acc);
+          }
+          if (acc < best) { best = acc; idx = c; }
+        }
       }
       const int idx_next = __shfl_down(idx, 1);
       if (valid) {
@@ -802,9 +1001,6 @@ __global__ __launch_bounds__(kThreads) void pvq_mfma_kernel(
 // 0-1 are u, element bit 2 is lane bit 5, sub-vector bits are lane bits 0-4.
 // Tile T gives lane l the centroids 32 T + 8 (v / 4) + 4 (l / 32) + v mod 4
 // (v < 16) of its row; lanes l and l ^ 32 hold the two halves.
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef float float16_t __attribute__((ext_vector_type(16)));
-
 template <int D>
 __device__ __forceinline__ void wht_b8(float (&x)[2][4], int lane) {
   constexpr int NSUB = D / 8;  // 4..32: sub-vector bits are lane bits 0..4
@@ -1163,33 +1359,38 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
   if (offs) o = *offs;
   if (a.transform == 2) {
     if constexpr (D <= 128) {
-      // one grid-stride pass: as many workgroups as are resident at once
+      // one grid-stride pass: as many workgroups as are resident at once;
+      // the encode of sub-vectors of 8 (one matrix in LDS) runs 12 waves per
+      // workgroup to keep the matrix-core search fed
       const int nmat = mode == 1 ? 2 : 1;
-      const size_t lds = (size_t)(nmat * D * D + kThreads / 64 * 64 / (D / DS) * D) * sizeof(float);
+      const int nt = (DS == 8 && mode == 0) ? 768 : kThreads;
+      const size_t lds = (size_t)(nmat * D * D + nt / 64 * 64 / (D / DS) * D) * sizeof(float);
       void (*kern)(const __half*, const uint8_t*, const float*, const float*, const float*,
                    const float*, uint8_t*, void*, Dims, RowOffsets);
       if (mode == 3) {
-        if constexpr (DS == 8) kern = pvq_dense_kernel<D, DS, 3>;
+        if constexpr (DS == 8) kern = pvq_dense_kernel<D, DS, 3, kThreads>;
         else return hipErrorInvalidValue;
+      } else if (mode == 0) {
+        if constexpr (DS == 8) kern = pvq_dense_kernel<D, DS, 0, 768>;
+        else kern = pvq_dense_kernel<D, DS, 0, kThreads>;
       } else {
-        kern = mode == 0 ? pvq_dense_kernel<D, DS, 0>
-                         : (mode == 1 ? pvq_dense_kernel<D, DS, 1> : pvq_dense_kernel<D, DS, 2>);
+        kern = mode == 1 ? pvq_dense_kernel<D, DS, 1, kThreads> : pvq_dense_kernel<D, DS, 2, kThreads>;
       }
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
       int per_cu = 0, cus = 0, dev = 0;
       (void)hipGetDevice(&dev);
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kThreads, lds) != hipSuccess ||
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, nt, lds) != hipSuccess ||
           per_cu <= 0)
         per_cu = 1;
       if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
           cus <= 0)
         cus = 256;
       const long long steps = (n_th + 64 / (D / DS) - 1) / (64 / (D / DS));
-      const long long want = (steps + kThreads / 64 - 1) / (kThreads / 64);
+      const long long want = (steps + nt / 64 - 1) / (nt / 64);
       const unsigned blocks = (unsigned)std::max(1LL, std::min(want, (long long)per_cu * cus));
-      hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), lds, st, a.keys, a.codes_in, a.codebook,
+      hipLaunchKernelGGL(kern, dim3(blocks), dim3(nt), lds, st, a.keys, a.codes_in, a.codebook,
                          a.smooth, a.rot, a.rot_inv, a.codes, a.recon, d, o);
       return hipGetLastError();
     }
@@ -1283,57 +1484,11 @@ __global__ __launch_bounds__(kKmWaves * 64) void kmeans_f16_kernel(
   const int hi = lane >> 5, l32 = lane & 31;
   __shared__ double acc[256 * W + 1];
   __shared__ float s_red[kKmWaves];
-  __shared__ half4_t s_ah[8 * 64], s_al[8 * 64];
-  __shared__ float s_norm[256];
+  __shared__ F16Codebook tab;
   __shared__ float s_seeded[kKmWaves][256];
   const int slots = n_c * W + 1;
   for (int i = threadIdx.x; i < slots; i += NT) acc[i] = 0.0;
-  int sc;
-  {
-    const int c = threadIdx.x;
-    float m = 0.f;
-    if (c < n_c) {
-#pragma unroll
-      for (int e = 0; e < DS; ++e) m = fmaxf(m, fabsf(cb[c * DS + e]));
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if (lane == 0) s_red[wave] = m;
-    __syncthreads();
-    m = 0.f;
-#pragma unroll
-    for (int w = 0; w < kKmWaves; ++w) m = fmaxf(m, s_red[w]);
-    sc = m > 0.f ? 14 - __builtin_amdgcn_frexp_expf(m) : 0;
-    if (c < 256) {
-      float n = INFINITY;
-      if (c < n_c) {
-        n = 0.f;
-#pragma unroll
-        for (int e = 0; e < DS; ++e) {
-          const float v = ldexpf(cb[c * DS + e], sc);
-          n = fmaf(v, v, n);
-        }
-      }
-      s_norm[c] = n;
-    }
-    if (wave < 4) {
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int T = 2 * wave + r;
-        const int cc = 32 * T + l32;
-        half4_t ah, al;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float v = cc < n_c ? -2.f * ldexpf(cb[cc * DS + 4 * hi + u], sc) : 0.f;
-          ah[u] = (_Float16)v;
-          al[u] = (_Float16)(v - (float)ah[u]);
-        }
-        s_ah[T * 64 + lane] = ah;
-        s_al[T * 64 + lane] = al;
-      }
-    }
-  }
-  __syncthreads();
+  const int sc = f16_stage<NT>(cb, n_c, tab, s_red);
 
   double inert = 0.0;
   const long long n_steps = (N + 63) / 64;
@@ -1348,93 +1503,12 @@ __global__ __launch_bounds__(kKmWaves * 64) void kmeans_f16_kernel(
       if (row < N) v = *reinterpret_cast<const float4*>(vecs + row * DS + 4 * hi);
       x[g][0] = v.x; x[g][1] = v.y; x[g][2] = v.z; x[g][3] = v.w;
     }
-    float mx = 0.f;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fabsf(x[g][u]));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    int s = sc;
-    const float* nrm = s_norm;
-    if (ldexpf(mx, sc) >= 32768.f) {
-      s = 14 - __builtin_amdgcn_frexp_expf(mx);
-      float* w = s_seeded[wave];
-      const float4 nv = *reinterpret_cast<const float4*>(s_norm + 4 * lane);
-      const float f = ldexpf(1.f, s - sc);
-      *reinterpret_cast<float4*>(w + 4 * lane) = make_float4(nv.x * f, nv.y * f, nv.z * f, nv.w * f);
-      nrm = w;
-    }
-    half4_t bh[2], bl[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float v = ldexpf(x[g][u], s);
-        bh[g][u] = (_Float16)v;
-        bl[g][u] = (_Float16)(v - (float)bh[g][u]);
-      }
-    struct TileIn {
-      half4_t ah, al;
-      float16_t n;
-    };
-    float best[2] = {INFINITY, INFINITY};
-    int bi[2] = {0, 0}, bt[2] = {0, 0};
-    auto tile_in = [&](int T) {
-      asm volatile("" ::: "memory");
-      TileIn t;
-      t.ah = s_ah[T * 64 + lane];
-      t.al = s_al[T * 64 + lane];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 nv = *reinterpret_cast<const float4*>(nrm + 32 * T + 8 * q + 4 * hi);
-        t.n[4 * q] = nv.x; t.n[4 * q + 1] = nv.y; t.n[4 * q + 2] = nv.z; t.n[4 * q + 3] = nv.w;
-      }
-      return t;
-    };
-    auto chains = [&](const TileIn& t, float16_t (&a)[2]) {
-      a[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bh[0], t.n, 0, 0, 0);
-      a[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bh[1], t.n, 0, 0, 0);
-      a[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.al, bh[0], a[0], 0, 0, 0);
-      a[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.al, bh[1], a[1], 0, 0, 0);
-      a[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bl[0], a[0], 0, 0, 0);
-      a[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(t.ah, bl[1], a[1], 0, 0, 0);
-    };
-    auto scan = [&](const float16_t (&r)[2], int T) {
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const float before = best[g];
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (r[g][v] < best[g]) { best[g] = r[g][v]; bi[g] = 8 * (v >> 2) + (v & 3); }
-        if (best[g] < before) bt[g] = T;
-      }
-    };
-    float16_t a[2];
-    chains(tile_in(0), a);
-    TileIn nxt_in = tile_in(1);
-#pragma unroll
-    for (int T = 0; T < 8; ++T) {
-      float16_t r[2] = {a[0], a[1]};
-      if (T + 1 < 8) {
-        chains(nxt_in, a);
-        if (T + 2 < 8) nxt_in = tile_in(T + 2);
-      }
-      scan(r, T);
-#pragma unroll
-      for (int g = 0; g < 2; ++g)
-        asm volatile("" : "+v"(best[g]), "+v"(bi[g]), "+v"(bt[g]), "+v"(a[g]));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // merge lanes l and l ^ 32, lowest index on ties; then accumulate
+    int idx[2];
+    f16_nearest(x, sc, tab, s_seeded[wave], n_c, idx);
+    // accumulate the two rows
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      float bv = best[g];
-      int bx = 32 * bt[g] + bi[g] + 4 * hi;
-      const float ov = __shfl_xor(bv, 32);
-      const int ox = __shfl_xor(bx, 32);
-      if (ov < bv || (ov == bv && ox < bx)) bx = ox;
-      const int ci = min(bx, n_c - 1);
+      const int ci = idx[g];
       const float4 cv = *reinterpret_cast<const float4*>(cb + ci * DS + 4 * hi);
       const float cvv[4] = {cv.x, cv.y, cv.z, cv.w};
       float d = 0.f;
