@@ -410,10 +410,10 @@ def main():
     log(f"[bench] step: {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s")
 
     # attention kernel alone, HIP events on the launch stream, same rotation
-    attn_us = time_events(lambda i: steps[i % n_sets][1](), max(args.steps, 100), torch)
+    attn_us = time_events(lambda i: steps[i % n_sets][1](), max(args.steps, 100), torch, warm=100)
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     log(f"[bench] vq_attend: {attn_us:.1f} us, {achieved:.0f} GB/s")
-    each = time_events_each(lambda i: steps[i % n_sets][1](), max(args.steps, 100), torch)
+    each = time_events_each(lambda i: steps[i % n_sets][1](), max(args.steps, 100), torch, warm=100)
     log(f"[bench] vq_attend per call: p10 {pct(each, 0.1):.1f} p50 {pct(each, 0.5):.1f} "
         f"p90 {pct(each, 0.9):.1f} us")
     # practical HBM reference: a plain 1 GiB elementwise copy (1 GiB read + 1 GiB written)

@@ -554,24 +554,46 @@ __global__ __launch_bounds__(NT) void pvq_dense_kernel(
   float* const xw = xs + (wave * TPW + tok) * D;  // this lane's token-head vector
   // y = x . A for the lane's sub-vector: x staged in xw (the wave's own LDS
   // accesses execute in issue order, so the reads see the writes)
+  // For sub-vectors of 8, lanes j and j + 8 of a token-head would read the
+  // same bank quads of a matrix row (32 B apart per lane): lanes with bit 3
+  // of j set read the row's two halves in the other order and accumulate
+  // them swapped, undone once at the end.
+  const bool swap = DS == 8 && ((j >> 3) & 1);
   auto rotate = [&](float (&x)[DS], const float* A) {
 #pragma unroll
     for (int e = 0; e < DS; ++e) xw[j * DS + e] = x[e];
     float y[DS];
 #pragma unroll
     for (int e = 0; e < DS; ++e) y[e] = 0.f;
+    const int h0 = swap ? 4 : 0;
     for (int i = 0; i < D; i += 4) {
       const float4 xv = *reinterpret_cast<const float4*>(xw + i);
       const float xi[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float* arow = A + (i + k) * D + j * DS;
+        if constexpr (DS == 8) {
+          const float4 a0 = *reinterpret_cast<const float4*>(arow + h0);
+          const float4 a1 = *reinterpret_cast<const float4*>(arow + (4 - h0));
+          const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-        for (int e = 0; e < DS; ++e) y[e] = fmaf(xi[k], arow[e], y[e]);
+          for (int e = 0; e < DS; ++e) y[e] = fmaf(xi[k], av[e], y[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < DS; ++e) y[e] = fmaf(xi[k], arow[e], y[e]);
+        }
       }
     }
+    if constexpr (DS == 8) {
 #pragma unroll
-    for (int e = 0; e < DS; ++e) x[e] = y[e];
+      for (int e = 0; e < 4; ++e) {
+        x[e] = swap ? y[4 + e] : y[e];
+        x[4 + e] = swap ? y[e] : y[4 + e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DS; ++e) x[e] = y[e];
+    }
   };
 
   const long long n_th = (long long)d.B * d.H * d.S;
