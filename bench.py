@@ -519,8 +519,8 @@ def main():
             "attend_gqa_long_W0_us": round(us_da, 2),
             "attend_GBps": round(attn_bytes / us_da / 1e3, 1),
             "note": "random orthogonal M [128,128] fp32; encode on the dense-matrix kernel "
-                    "(rotation on the vector ALUs, search on the matrix cores), attention with "
-                    "the query pre-pass"}
+                    "(rotation and search on the matrix cores), attention with the query "
+                    "pre-pass"}
         log(f"[bench] dense transform: encode {us_de:.1f} us, gqa W=0 attend {us_da:.1f} us")
         del fdm
 

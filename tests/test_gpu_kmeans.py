@@ -7,8 +7,12 @@ trained).
 Bars, derived from the arithmetic (fp32 on the GPU, fp64 in the oracle):
   transform   |gpu - ref| <= gamma_n * (|x / s| . |M|) elementwise, n the
               roundings on the path (division, log2 D butterfly stages and
-              the final scale; D + 1 for a dense matrix), gamma_n =
-              n u / (1 - n u), u = 2^-24 (Higham's bound for sums).
+              the final scale), gamma_n = n u / (1 - n u), u = 2^-24
+              (Higham's bound for sums).  A dense matrix runs on the matrix
+              cores as three split-fp16 products per term (each within
+              3 * 2^-22 of the exact product: two split roundings and the
+              dropped lo.lo part) summed in fp32 in an unspecified order:
+              n = 3 D + 14.
   labels      equal, except at near-ties (the oracle's top-2 gap below 1e-5
               relative), where the GPU's centroid must be within 1e-5 d2 of
               the nearest (as for codes).
@@ -53,7 +57,7 @@ def transform_bound(keys, smooth, transform):
         return gamma(int(math.log2(D)) + 3) * (x.sum(-1, keepdims=True) / math.sqrt(D)) * np.ones(D)
     if transform is False:
         return gamma(1) * x
-    return gamma(D + 2) * (x @ np.abs(np.asarray(transform, np.float64)))
+    return gamma(3 * D + 14) * (x @ np.abs(np.asarray(transform, np.float64)))
 
 
 def mats(M):

@@ -1356,6 +1356,156 @@ void launch_one(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStre
                      a.keys, a.codes_in, a.codebook, a.smooth, a.codes, a.recon, d, o);
 }
 
+// Dense rotation on the matrix cores, for the encode (sub-vectors of 8, 8-bit
+// codes) and the transform-only mode: a wave takes 32 token-heads and forms
+// Y^T = M^T X^T on v_mfma_f32_32x32x8_f16, A = M^T (32 output dims x 8 input
+// dims per step, from LDS), B = X^T (8 input dims x 32 token-heads, the
+// lane's own token-head), each operand split into fp16 high and low parts
+// (three passes; the dropped lo.lo term is below 2^-22 of each product) and
+// scaled by powers of two: M so that its largest entry lands in
+// [2^13, 2^14), each token-head's x / s likewise.  The accumulator of output
+// tile ct gives lane l the dims 32 ct + 8 q + 4 (l / 32) + u of token-head
+// l mod 32: sub-vector j = 4 ct + q, elements 4 (l / 32) + u, which is the
+// row layout of f16_nearest, so the search follows with no reshuffle.
+template <int D, int MODE>
+__global__ __launch_bounds__(512) void pvq_dense_mfma_kernel(
+    const __half* __restrict__ keys, const float* __restrict__ cb, const float* __restrict__ smooth,
+    const float* __restrict__ rot, uint8_t* __restrict__ codes, float* __restrict__ out, Dims d,
+    RowOffsets offs) {
+  constexpr int NW = 8, NT = NW * 64;
+  constexpr int KC = D / 8, CT = D / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hi = lane >> 5, l32 = lane & 31;
+  __shared__ half4_t s_mh[KC * CT * 64], s_ml[KC * CT * 64];  // [kc][ct][lane]
+  __shared__ float s_red[NW];
+  __shared__ std::conditional_t<MODE == 0, F16Codebook, char> tab;
+  __shared__ std::conditional_t<MODE == 0, float[NW][256], char> s_seeded;
+  // M's scale: its largest magnitude in [2^13, 2^14)
+  int em;
+  {
+    float m = 0.f;
+    for (int i = threadIdx.x; i < D * D / 4; i += NT) {
+      const float4 v = reinterpret_cast<const float4*>(rot)[i];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    m = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, s_red[w]);
+    em = m > 0.f ? 14 - __builtin_amdgcn_frexp_expf(m) : 0;
+    // entry (kc, ct, lane): M[8 kc + 4 hi + u][32 ct + l32], u < 4
+    for (int e = threadIdx.x; e < KC * CT * 64; e += NT) {
+      const int kc = e / (CT * 64), ct = (e / 64) % CT, ln = e & 63;
+      const int row = 8 * kc + 4 * (ln >> 5), col = 32 * ct + (ln & 31);
+      half4_t h, l;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float v = ldexpf(rot[(row + u) * D + col], em);
+        h[u] = (_Float16)v;
+        l[u] = (_Float16)(v - (float)h[u]);
+      }
+      s_mh[e] = h;
+      s_ml[e] = l;
+    }
+  }
+  __syncthreads();  // s_red is reused by the codebook staging
+  int sc = 0;
+  if constexpr (MODE == 0) sc = f16_stage<NT>(cb, d.n_c, tab, s_red);
+  else __syncthreads();
+
+  const long long n_th = (long long)d.B * d.H * d.S;
+  const long long n_tiles = (n_th + 31) / 32;
+  for (long long tile = (long long)blockIdx.x * NW + wave; tile < n_tiles;
+       tile += (long long)gridDim.x * NW) {
+    const long long th = tile * 32 + l32;
+    const bool valid = th < n_th;
+    const long long thc = valid ? th : 0;
+    const int bh = (int)(thc / d.S);
+    const int h = bh % d.H;
+    const __half* xr = keys + thc * D + 4 * hi;
+    const float* sr = smooth ? smooth + (size_t)(d.smooth_rows == 1 ? 0 : h) * D + 4 * hi : nullptr;
+    auto load = [&](int kc, float (&v)[4]) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(xr + 8 * kc);
+      const float2 f0 = __half22float2(*reinterpret_cast<const __half2*>(&raw.x));
+      const float2 f1 = __half22float2(*reinterpret_cast<const __half2*>(&raw.y));
+      v[0] = f0.x; v[1] = f0.y; v[2] = f1.x; v[3] = f1.y;
+      if (!valid) v[0] = v[1] = v[2] = v[3] = 0.f;
+      if (sr) {
+        const float4 sv = *reinterpret_cast<const float4*>(sr + 8 * kc);
+        v[0] = v[0] / sv.x; v[1] = v[1] / sv.y; v[2] = v[2] / sv.z; v[3] = v[3] / sv.w;
+      }
+    };
+    // this token-head's scale (both halves of the lane pair)
+    float mx = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      float v[4];
+      load(kc, v);
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const int ex = mx > 0.f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
+    half4_t bh_[KC], bl_[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      float v[4];
+      load(kc, v);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = ldexpf(v[u], ex);
+        bh_[kc][u] = (_Float16)w;
+        bl_[kc][u] = (_Float16)(w - (float)bh_[kc][u]);
+      }
+    }
+    const int unscale = -(ex + em);
+    const int t = (int)(thc - (long long)bh * d.S);
+    const int b = bh / d.H;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float16_t acc = {};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const half4_t ah = s_mh[(kc * CT + ct) * 64 + lane], al = s_ml[(kc * CT + ct) * 64 + lane];
+        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(ah, bh_[kc], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(al, bh_[kc], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(ah, bl_[kc], acc, 0, 0, 0);
+      }
+      float y[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) y[v] = ldexpf(acc[v], unscale);
+      if constexpr (MODE == 3) {
+        if (valid) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(out + th * D + 32 * ct + 8 * q + 4 * hi) =
+                make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+        }
+        // one output tile at a time (the scheduler would otherwise keep every
+        // tile's accumulators live)
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        const int off = d.use_row_offsets ? offs.v[b] : d.S_off;
+#pragma unroll
+        for (int qp = 0; qp < 2; ++qp) {
+          const float x2[2][4] = {{y[8 * qp], y[8 * qp + 1], y[8 * qp + 2], y[8 * qp + 3]},
+                                  {y[8 * qp + 4], y[8 * qp + 5], y[8 * qp + 6], y[8 * qp + 7]}};
+          int idx[2];
+          f16_nearest(x2, sc, tab, s_seeded[wave], d.n_c, idx);
+          if (valid && !hi) {
+            uint8_t* cp = codes + ((long long)bh * d.S_cap + off + t) * (D / 8) + 4 * ct + 2 * qp;
+            cp[0] = (uint8_t)idx[0];
+            cp[1] = (uint8_t)idx[1];
+          }
+        }
+      }
+    }
+  }
+}
+
+
 Dims make_dims(const EncodeArgs& a) {
   return Dims{a.B, a.H, a.S, a.n_c, a.smooth_rows, a.transform, a.S_cap, a.S_off,
               a.use_row_offsets, a.recon_dtype, make_fastdiv((uint32_t)a.S), make_fastdiv((uint32_t)a.H),
@@ -1381,6 +1531,25 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
   if (offs) o = *offs;
   if (a.transform == 2) {
     if constexpr (D <= 128) {
+      // forward rotations on the matrix cores: the transform-only mode and
+      // the encode of sub-vectors of 8 with 8-bit codes
+      if (mode == 3 || (mode == 0 && DS == 8 && a.code_bits == 8)) {
+        void (*mk)(const __half*, const float*, const float*, const float*, uint8_t*, float*, Dims,
+                   RowOffsets) = mode == 3 ? pvq_dense_mfma_kernel<D, 3> : pvq_dense_mfma_kernel<D, 0>;
+        int per_cu = 0, cus = 0, dev = 0;
+        (void)hipGetDevice(&dev);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mk, 512, 0) != hipSuccess || per_cu <= 0)
+          per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+          cus = 256;
+        const long long tiles = (n_th + 31) / 32;
+        const long long want = (tiles + 7) / 8;
+        const unsigned blocks = (unsigned)std::max(1LL, std::min(want, (long long)per_cu * cus));
+        hipLaunchKernelGGL(mk, dim3(blocks), dim3(512), 0, st, a.keys, a.codebook, a.smooth, a.rot,
+                           a.codes, reinterpret_cast<float*>(a.recon), d, o);
+        return hipGetLastError();
+      }
       // one grid-stride pass: as many workgroups as are resident at once;
       // the encode of sub-vectors of 8 (one matrix in LDS) runs 12 waves per
       // workgroup to keep the matrix-core search fed
