@@ -337,9 +337,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   // (clamped) go to LDS, the unit prefix is a DPP scan over rounds of 64
   // units, the chunk is the equal share [c C0, (c + 1) C0) of the T keys,
   // and the unit holding its first key is found by a ballot.  That unit's
-  // query rows are requested at once, so they arrive while the tables are
-  // written.  (A wave's LDS accesses execute in issue order, so its reads of
-  // lens and pre see its own writes.)
+  // query rows are requested before the first barrier, so they arrive while
+  // the first segment is set up.  (A wave's LDS accesses execute in issue
+  // order, so its reads of lens and pre see its own writes.)
   float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), vq = kq;
   // value codebook as fp16 rows, replicated 32 times; rotated by code so
   // that the 16 lanes of a write hit distinct bank quads
@@ -351,19 +351,26 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     for (int i = 0; i < 8; ++i)
       *reinterpret_cast<uint4*>(lds + kValTab + code * 256 + (tid & 1) * 128 + 16 * ((i + code) & 7)) = two;
   };
-  if ((tid >> 1) < p.n_c) {
-    kq = reinterpret_cast<const float4*>(k_codebook)[tid];
-    vq = reinterpret_cast<const float4*>(v_codebook)[tid >> 1];
-  }
+  // The plan's chain of round trips starts with wave 0's kv length loads, so
+  // they are issued first; the codebook loads follow at once, and their
+  // values are not touched until the plan is done.
+  int lv0 = p.S_cap;
+  if (wave == 0 && kv_lens && lane < p.B) lv0 = kv_lens[lane];
+  // (unconditional loads, rows past n_c re-read row 0 and are zeroed below:
+  // no select on the loaded registers before the plan)
+  const bool cb_row = (tid >> 1) < p.n_c;
+  kq = reinterpret_cast<const float4*>(k_codebook)[cb_row ? tid : 0];
+  vq = reinterpret_cast<const float4*>(v_codebook)[cb_row ? tid >> 1 : 0];
   int* const lens_w = reinterpret_cast<int*>(lds + kLens);
   int* const pre = reinterpret_cast<int*>(lds + kPrefix);
   int* const plan = scan;  // T, start, end, first unit (ints 0..3 of the scan area)
   const int c = blockIdx.x;
   const int G = gridDim.x;
   QueryRaw qraw;
+  int quf = -1;  // wave 0: the first unit, whose query rows it requests
   if (wave == 0) {
     for (int b = lane; b < p.B; b += 64) {
-      const int lv = kv_lens ? kv_lens[b] : p.S_cap;
+      const int lv = b == lane ? lv0 : (kv_lens ? kv_lens[b] : p.S_cap);
       lens_w[b] = lv < 0 ? 0 : (lv > p.S_cap ? p.S_cap : lv);
     }
     lds_order();
@@ -427,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         st = en = Tw;  // the chunk holds switch cost only
       } else {
         while (pre[uf + 1] == pre[uf]) ++uf;  // an empty unit's span maps onto the next start
-        qraw = query_load(uf);
+        quf = uf;
       }
     }
     if (lane == 0) {
@@ -437,6 +444,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       plan[3] = uf;
     }
   }
+  // opaque to the compiler: the codebook conversions stay below the plan
+  asm volatile("" : "+v"(kq.x), "+v"(kq.y), "+v"(kq.z), "+v"(kq.w));
+  asm volatile("" : "+v"(vq.x), "+v"(vq.y), "+v"(vq.z), "+v"(vq.w));
+  if (!cb_row) kq = vq = make_float4(0.f, 0.f, 0.f, 0.f);
   {
     *reinterpret_cast<float4*>(lds + kCbk + 16 * tid) = kq;
     // per-wave maximum magnitude of the key codebook
@@ -444,6 +455,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     if (lane == 0) reinterpret_cast<float*>(lds + kWaveMax)[wave] = kmx;
     write_val_table();
   }
+  // the first unit's query rows are requested after the codebook stores, so
+  // that those stores wait for the codebook loads only; they arrive while
+  // every wave sets up its first segment
+  if (wave == 0 && quf >= 0) qraw = query_load(quf);
   __syncthreads();
   const int* const lens = lens_w;
   // magnitude exponent of the key codebook
@@ -460,6 +475,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   const int end = __builtin_amdgcn_readfirstlane(plan[2]);
   int u = __builtin_amdgcn_readfirstlane(plan[3]);
   if (start >= T) return;
+  // the first unit's query rows (requested before the barrier) into buffer
+  // 0, before anything else is issued, so that their waits cover nothing
+  // but those loads; later units' rows are written during the previous
+  // segment's streaming
+  if (wave == 0) query_finish(qraw, u, 0);
 
   // ---- lane constants ------------------------------------------------------
   // Score gathers: at step k = 4 a + b the lane reads sub-vector
@@ -508,7 +528,6 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
 
   int pos = start;
   int qbuf = 0;          // query buffer of the current unit
-  bool q_ready = false;  // its rows were written during the previous segment
   while (true) {
     // ---- segment: unit u, chunk positions [pos, seg_end) ----------------
     const int Pu = pre[u], Pn = pre[u + 1];
@@ -603,8 +622,6 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       load_codes(blk(nB), kcB, vrB);
     }
 
-    // first segment: the rows wave 0 requested during the plan
-    if (!q_ready && wave == 0) query_finish(qraw, u, qbuf);
     if (tid == 0) *claim_ctr = 2 * kW;
     __syncthreads();  // query rows ready; the previous combine has read the table area
     {
@@ -895,7 +912,6 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     pos = seg_end;
     u = u_next;
     qbuf ^= 1;
-    q_ready = true;
   }
 }
 
