@@ -157,6 +157,33 @@ __device__ __forceinline__ float wave_total_f(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// One cross-lane Walsh-Hadamard butterfly over lane bit M: returns
+// sg x + x(lane ^ M) with sg = -1 where lane bit M is set, +1 elsewhere
+// (the same fma as with a shuffle), without a trip through LDS:
+//   M = 4   DPP row_shl:4 into banks 0, 2 and row_shr:4 into banks 1, 3;
+//   M = 8   DPP row_ror:8;
+//   M = 16  v_permlane16_swap of x with itself gives (own, partner) in the
+//           even rows and (partner, own) in the odd rows;
+//   M = 32  v_permlane32_swap, the same over the two halves of the wave.
+template <int M>
+__device__ __forceinline__ float xor_butterfly(float x, float sg) {
+  const int xi = __float_as_int(x);
+  if constexpr (M == 4) {
+    int t = __builtin_amdgcn_update_dpp(0, xi, 0x104, 0xf, 0x5, false);
+    t = __builtin_amdgcn_update_dpp(t, xi, 0x114, 0xf, 0xa, false);
+    return fmaf(sg, x, __int_as_float(t));
+  } else if constexpr (M == 8) {
+    return fmaf(sg, x, __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x128, 0xf, 0xf, false)));
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)xi, (unsigned)xi, false, false);
+    return fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  } else {
+    static_assert(M == 32, "lane bit");
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)xi, (unsigned)xi, false, false);
+    return fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  }
+}
+
 __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
   const __half2 h = __floats2half2_rn(a, b);
   return *reinterpret_cast<const uint32_t*>(&h);
@@ -308,11 +335,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       }
       // dim bits 2..5 are lane bits 2..5
 #pragma unroll
-      for (int m = 4; m < 64; m <<= 1) {
-        const float sg = (lane & m) ? -1.f : 1.f;
+      for (int i = 0; i < 8; ++i) x[i] = xor_butterfly<4>(x[i], (lane & 4) ? -1.f : 1.f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = fmaf(sg, x[i], __shfl_xor(x[i], m));
-      }
+      for (int i = 0; i < 8; ++i) x[i] = xor_butterfly<8>(x[i], (lane & 8) ? -1.f : 1.f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = xor_butterfly<16>(x[i], (lane & 16) ? -1.f : 1.f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = xor_butterfly<32>(x[i], (lane & 32) ? -1.f : 1.f);
     }
     const float f = rho < p.GS ? p.fold : 0.f;
     float* const qd = reinterpret_cast<float*>(lds + kQs) + qbuf * kRows * kD;
