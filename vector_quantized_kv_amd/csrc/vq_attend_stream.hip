@@ -372,10 +372,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   float4 kq = make_float4(0.f, 0.f, 0.f, 0.f), vq = kq;
   // value codebook as fp16 rows, replicated 32 times; rotated by code so
   // that the 16 lanes of a write hit distinct bank quads
+  // 4-bit codes: a byte-pair table instead, entry [byte] = the fp16 rows of
+  // codes byte & 15 and byte >> 4 (the two sub-vectors of one code byte),
+  // 16 bytes, replicated 16 times ([byte][replica][8 halves], 64 KiB): the
+  // 16 lanes of a b128 gather read replicas lane mod 16, distinct bank quads
+  float4 vq_hi = make_float4(0.f, 0.f, 0.f, 0.f);
   auto write_val_table = [&]() {
-    const uint32_t h0 = pack_half2(vq.x, vq.y), h1 = pack_half2(vq.z, vq.w);
-    const uint4 two = make_uint4(h0, h1, h0, h1);
     const int code = tid >> 1;
+    const uint32_t h0 = pack_half2(vq.x, vq.y), h1 = pack_half2(vq.z, vq.w);
+    uint4 two = make_uint4(h0, h1, h0, h1);
+    if constexpr (BITS == 4) two = make_uint4(h0, h1, pack_half2(vq_hi.x, vq_hi.y), pack_half2(vq_hi.z, vq_hi.w));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       *reinterpret_cast<uint4*>(lds + kValTab + code * 256 + (tid & 1) * 128 + 16 * ((i + code) & 7)) = two;
@@ -389,7 +395,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   // no select on the loaded registers before the plan)
   const bool cb_row = (tid >> 1) < p.n_c;
   kq = reinterpret_cast<const float4*>(k_codebook)[cb_row ? tid : 0];
-  vq = reinterpret_cast<const float4*>(v_codebook)[cb_row ? tid >> 1 : 0];
+  // value rows: code tid / 2 (8-bit); codes byte & 15 and byte >> 4 of byte
+  // tid / 2 (4-bit pair table; n_c <= 16)
+  const int vlo = BITS == 4 ? (tid >> 1) & 15 : tid >> 1, vhi = (tid >> 5) & 15;
+  const bool vlo_ok = vlo < p.n_c, vhi_ok = vhi < p.n_c;
+  vq = reinterpret_cast<const float4*>(v_codebook)[vlo_ok ? vlo : 0];
+  if constexpr (BITS == 4) vq_hi = reinterpret_cast<const float4*>(v_codebook)[vhi_ok ? vhi : 0];
   int* const lens_w = reinterpret_cast<int*>(lds + kLens);
   int* const pre = reinterpret_cast<int*>(lds + kPrefix);
   int* const plan = scan;  // T, start, end, first unit (ints 0..3 of the scan area)
@@ -476,7 +487,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   // opaque to the compiler: the codebook conversions stay below the plan
   asm volatile("" : "+v"(kq.x), "+v"(kq.y), "+v"(kq.z), "+v"(kq.w));
   asm volatile("" : "+v"(vq.x), "+v"(vq.y), "+v"(vq.z), "+v"(vq.w));
-  if (!cb_row) kq = vq = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (BITS == 4) asm volatile("" : "+v"(vq_hi.x), "+v"(vq_hi.y), "+v"(vq_hi.z), "+v"(vq_hi.w));
+  if (!cb_row) kq = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (!vlo_ok) vq = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (!vhi_ok) vq_hi = make_float4(0.f, 0.f, 0.f, 0.f);
   {
     *reinterpret_cast<float4*>(lds + kCbk + 16 * tid) = kq;
     // per-wave maximum magnitude of the key codebook
@@ -543,7 +557,9 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   }
 #pragma unroll
   for (int b = 0; b < 4; ++b) sel[b] = 0x0c0c0000u | ((4u + ((b + rb) & 3)) << 8) | (uint32_t)b;
-  const uint32_t vbase = (uint32_t)(lane & 31) * 8u | (1u << 16);      // value replica + 64 KiB
+  // value replica + 64 KiB: 8-byte rows, replica lane mod 32 (8-bit); 16-byte
+  // pair rows, replica lane mod 16 (4-bit)
+  const uint32_t vbase = BITS == 8 ? (uint32_t)(lane & 31) * 8u | (1u << 16) : (uint32_t)(lane & 15) * 16u | (1u << 16);
   const int e_a = lane & 3;          // A operand of the value MFMA: row (rA, e_a)
   const int rA = (lane & 15) >> 2;
   const int grp16 = lane >> 4;       // K group of the 16x16x32 operands
@@ -723,6 +739,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // consecutive blocks alternate between two register sets, so the
     // prefetch of the next block is only waited for when it is used.
     u32x2_t vg[8][4];  // value rows of the block whose value MFMAs are pending
+    u32x4_t vp[8][2];  // (4-bit) its pair-table rows: [key 0 | key 1][sub 2n, sub 2n + 1]
     uint32_t pp[8];    // that block's p, staged into the A operand layout
 
     auto value_mfmas = [&](auto half) {
@@ -731,8 +748,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         const uint32_t x = pp[k];
         const uint4 au = make_uint4(__builtin_amdgcn_perm(0u, x, sa0), __builtin_amdgcn_perm(0u, x, sa1),
                                     __builtin_amdgcn_perm(0u, x, sa2), __builtin_amdgcn_perm(0u, x, sa3));
-        const uint4 b0 = make_uint4(vg[k][0].x, vg[k][0].y, vg[k][1].x, vg[k][1].y);
-        const uint4 b1 = make_uint4(vg[k][2].x, vg[k][2].y, vg[k][3].x, vg[k][3].y);
+        const uint4 b0 = BITS == 8 ? make_uint4(vg[k][0].x, vg[k][0].y, vg[k][1].x, vg[k][1].y)
+                                   : make_uint4(vp[k][0][0], vp[k][0][1], vp[k][1][0], vp[k][1][1]);
+        const uint4 b1 = BITS == 8 ? make_uint4(vg[k][2].x, vg[k][2].y, vg[k][3].x, vg[k][3].y)
+                                   : make_uint4(vp[k][0][2], vp[k][0][3], vp[k][1][2], vp[k][1][3]);
         const half8_t A = *reinterpret_cast<const half8_t*>(&au);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, *reinterpret_cast<const half8_t*>(&b0), acc0,
                                                       0, 0, 0);
@@ -858,19 +877,18 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       // rows of key pair k: [key 0 sub 2n, key 1 sub 2n, key 0 sub 2n+1, key 1 sub 2n+1]
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        // [code(key 0, 2n), code(key 0, 2n+1), code(key 1, 2n), code(key 1, 2n+1)]
-        uint32_t w;
         if constexpr (BITS == 8) {
-          w = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x05040100u);
+          // [code(key 0, 2n), code(key 0, 2n+1), code(key 1, 2n), code(key 1, 2n+1)]
+          const uint32_t w = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x05040100u);
+          vg[k][0] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020400u));
+          vg[k][1] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020600u));
+          vg[k][2] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020500u));
+          vg[k][3] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020700u));
         } else {
-          // [key 0 byte, key 1 byte] -> [key 0 lo, key 0 hi, key 1 lo, key 1 hi]
-          const uint32_t x = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x0c0c0400u);
-          w = __builtin_amdgcn_perm((x >> 4) & 0x0f0fu, x & 0x0f0fu, 0x05010400u);
+          // one pair-table row per key: its code byte of sub-vectors 2n, 2n + 1
+          vp[k][0] = lds_ld<u32x4_t>((vr[2 * k] << 8) | vbase);
+          vp[k][1] = lds_ld<u32x4_t>((vr[2 * k + 1] << 8) | vbase);
         }
-        vg[k][0] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020400u));
-        vg[k][1] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020600u));
-        vg[k][2] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020500u));
-        vg[k][3] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020700u));
       }
     };
 
