@@ -739,6 +739,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // consecutive blocks alternate between two register sets, so the
     // prefetch of the next block is only waited for when it is used.
     u32x2_t vg[8][4];  // value rows of the block whose value MFMAs are pending
+    uint32_t wq[4];    // (8-bit) its packed codes of key pairs 4..7, gathered mid-stage
     u32x4_t vp[8][2];  // (4-bit) its pair-table rows: [key 0 | key 1][sub 2n, sub 2n + 1]
     uint32_t pp[8];    // that block's p, staged into the A operand layout
 
@@ -757,6 +758,16 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
                                                       0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, *reinterpret_cast<const half8_t*>(&b1), acc1,
                                                       0, 0, 0);
+      }
+    };
+    auto gather_hi = [&]() {
+#pragma unroll
+      for (int k = 4; k < 8; ++k) {
+        const uint32_t w = wq[k - 4];
+        vg[k][0] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020400u));
+        vg[k][1] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020600u));
+        vg[k][2] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020500u));
+        vg[k][3] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020700u));
       }
     };
     const std::integral_constant<int, 0> lo_half;
@@ -784,6 +795,8 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
               L[4 * a + b] = lds_ld<float4_t>(kLut + __builtin_amdgcn_perm(dw[a], jt[a], sel[b]));
           __builtin_amdgcn_sched_barrier(0);
           if (pending) value_mfmas(lo_half);
+          if (pending) gather_hi();
+          __builtin_amdgcn_sched_barrier(0);
           sc = ((L[0] + L[1]) + (L[2] + L[3])) + ((L[4] + L[5]) + (L[6] + L[7]));
 #pragma unroll
           for (int a = 2; a < 4; ++a)
@@ -880,6 +893,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         if constexpr (BITS == 8) {
           // [code(key 0, 2n), code(key 0, 2n+1), code(key 1, 2n), code(key 1, 2n+1)]
           const uint32_t w = __builtin_amdgcn_perm(vr[2 * k + 1], vr[2 * k], 0x05040100u);
+          if (k >= 4) {
+            wq[k - 4] = w;
+            continue;
+          }
           vg[k][0] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020400u));
           vg[k][1] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020600u));
           vg[k][2] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020500u));
@@ -911,6 +928,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         if (t0 + 64 * nA >= t1) break;
       }
       value_mfmas(lo_half);
+      if constexpr (BITS == 8) gather_hi();
       value_mfmas(hi_half);
     }
 
