@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--prewarm-seconds", type=float, default=0.25,
+                    help="untimed steps run for this long before the warmup steps (GPU clocks)")
     ap.add_argument("--mode", choices=["full", "attend", "encode", "encode_workload", "copy", "kmeans"],
                     default="full",
                     help="attend/encode: only launch that entry point of the main workload "
@@ -397,6 +399,18 @@ def main():
         log(f"[bench] mode={args.mode}: {args.warmup + args.steps} launches done")
         return
 
+    # The setup above is host work and copies, after which the GPU clocks
+    # ramp up over the first 10-20 ms of kernels (calls right after an idle
+    # period run 10-25% slower); untimed steps for a fixed wall time first,
+    # so that the warmup and timed steps see the steady state.
+    t_pre = time.perf_counter() + args.prewarm_seconds
+    n_pre = 0
+    while time.perf_counter() < t_pre:
+        for _ in range(50):
+            step(n_pre)
+            n_pre += 1
+        torch.cuda.synchronize()
+    log(f"[bench] clock warm-up: {n_pre} untimed steps in {args.prewarm_seconds} s")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
