@@ -150,15 +150,49 @@ __device__ __forceinline__ void wht_in_lane(float (&x)[DS]) {
 // partner of lane j for bit m is lane j ^ m in the same token-head group.
 template <int NSUB, int DS>
 __device__ __forceinline__ void wht_cross_lane(float (&x)[DS], int j) {
-#pragma unroll
-  for (int m = 1; m < NSUB; m <<= 1) {
-    const bool upper = (j & m) != 0;
-#pragma unroll
-    for (int e = 0; e < DS; ++e) {
-      const float y = __shfl_xor(x[e], m);
-      x[e] = upper ? (y - x[e]) : (x[e] + y);
+  // the value of lane ^ M without a trip through LDS: DPP quad permutes
+  // (M = 1, 2), row shifts into alternate 4-lane banks (M = 4), a row
+  // rotation (M = 8), and v_permlane16/32_swap of x with itself, which
+  // leaves (own, partner) in lanes with bit M clear and (partner, own) where
+  // it is set (M = 16, 32)
+  auto partner = [](float v, auto mc) {
+    constexpr int M = decltype(mc)::value;
+    const int vi = __float_as_int(v);
+    if constexpr (M == 1) {
+      return __int_as_float(__builtin_amdgcn_mov_dpp(vi, 0xb1, 0xf, 0xf, false));
+    } else if constexpr (M == 2) {
+      return __int_as_float(__builtin_amdgcn_mov_dpp(vi, 0x4e, 0xf, 0xf, false));
+    } else if constexpr (M == 4) {
+      const int t = __builtin_amdgcn_update_dpp(0, vi, 0x104, 0xf, 0x5, false);
+      return __int_as_float(__builtin_amdgcn_update_dpp(t, vi, 0x114, 0xf, 0xa, false));
+    } else if constexpr (M == 8) {
+      return __int_as_float(__builtin_amdgcn_update_dpp(0, vi, 0x128, 0xf, 0xf, false));
+    } else if constexpr (M == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap((unsigned)vi, (unsigned)vi, false, false);
+      return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+    } else {
+      static_assert(M == 32, "lane bit");
+      const auto r = __builtin_amdgcn_permlane32_swap((unsigned)vi, (unsigned)vi, false, false);
+      return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
     }
-  }
+  };
+  auto stage = [&](auto mc) {
+    constexpr int M = decltype(mc)::value;
+    if constexpr (M < NSUB) {
+      const bool upper = (j & M) != 0;
+#pragma unroll
+      for (int e = 0; e < DS; ++e) {
+        const float y = partner(x[e], mc);
+        x[e] = upper ? (y - x[e]) : (x[e] + y);
+      }
+    }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
+  stage(std::integral_constant<int, 16>{});
+  stage(std::integral_constant<int, 32>{});
 }
 
 template <int D, int DS>
@@ -206,6 +240,9 @@ __device__ __forceinline__ void pvq_body(
   const int h = (int)(bh % d.H);
   const int b = (int)(bh / d.H);
   const float* srow = smooth ? smooth + (long long)(d.smooth_rows == 1 ? 0 : h) * D + j * DS : nullptr;
+  // the output slot's row offset (a kernel-argument array indexed by the
+  // lane's batch row) is requested with the inputs, not after the search
+  const int off = (MODE == 0 || MODE == 1) && d.use_row_offsets ? offs.v[b] : d.S_off;
 
   // The row's inputs (raw fp16 bits of the clamped row, smooth factors)
   // are requested before the codebook staging below, so all loads are in
@@ -284,18 +321,28 @@ __device__ __forceinline__ void pvq_body(
       s_idx[threadIdx.x] = idx;
       __syncthreads();
       if (part != 0) return;  // the first wave of the group finishes the token-heads
-      // later parts hold higher indices: only a strictly smaller distance wins
+      // later parts hold higher indices: only a strictly smaller distance
+      // wins (every partial is read before any is compared: no chain of
+      // dependent LDS reads)
+      float bk[CSPLIT];
+      int ik[CSPLIT];
 #pragma unroll
       for (int k = 1; k < CSPLIT; ++k) {
-        const int o = threadIdx.x + k * 64;
-        if (s_best[o] < best) { best = s_best[o]; idx = s_idx[o]; }
+        bk[k] = s_best[threadIdx.x + k * 64];
+        ik[k] = s_idx[threadIdx.x + k * 64];
+      }
+#pragma unroll
+      for (int k = 1; k < CSPLIT; ++k) {
+        const bool lt = bk[k] < best;
+        best = lt ? bk[k] : best;
+        idx = lt ? ik[k] : idx;
       }
     }
     // 4-bit codes: the even sub-vector's lane packs its odd neighbour's
-    // code (lane + 1, the same token-head) into the high nibble
-    const int idx_next = __shfl_down(idx, 1);
+    // code (lane + 1, the same token-head and the same row of 16 lanes: DPP
+    // row_shl:1) into the high nibble
+    const int idx_next = __builtin_amdgcn_mov_dpp(idx, 0x101, 0xf, 0xf, false);
     if (valid) {
-      const int off = d.use_row_offsets ? offs.v[b] : d.S_off;
       if (d.code_bits == 4) {
         if (!(j & 1))
           codes[(bh * d.S_cap + off + t) * (NSUB / 2) + j / 2] = (uint8_t)((idx & 15) | ((idx_next & 15) << 4));
