@@ -90,13 +90,28 @@ def read_traffic(path, workload):
         return None
 
 
+WARM_SECONDS = 0.15
+
+
+def warm_up(fn, warm, torch):
+    """At least `warm` untimed calls of fn, and calls for WARM_SECONDS of
+    wall time: each leg's inputs are made on the host first, and after such
+    an idle stretch the GPU clocks take 10-20 ms of work to come back up."""
+    t_end = time.perf_counter() + WARM_SECONDS
+    n = 0
+    while n < warm or time.perf_counter() < t_end:
+        fn(n)
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_events_each(fn, reps, torch, warm=3):
     """Per-call device times (us) of fn(i): one HIP event between consecutive
     calls on the current stream, read after a single synchronize, so the
     queue stays full while they are recorded."""
-    for _ in range(warm):
-        fn(0)
-    torch.cuda.synchronize()
+    warm_up(fn, warm, torch)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev[0].record()
     for i in range(reps):
@@ -113,9 +128,7 @@ def pct(xs, q):
 
 def time_events(fn, reps, torch, warm=3):
     """Average device time of fn() over reps (HIP events on the current stream)."""
-    for _ in range(warm):
-        fn(0)
-    torch.cuda.synchronize()
+    warm_up(fn, warm, torch)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record()
     for i in range(reps):
