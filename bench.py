@@ -330,7 +330,7 @@ def main():
     import numpy as np
     import torch
 
-    from vector_quantized_kv_amd import (attend_workspace, synth, vq_attend, vq_encode,
+    from vector_quantized_kv_amd import (attend_workspace, synth, vq_attend, vq_decode, vq_encode,
                                          vq_encode_decode, vq_encode_kv)
 
     dev = "cuda:0"
@@ -538,18 +538,26 @@ def main():
         Mt, Mit = t(M.astype(np.float32)), t(np.linalg.inv(M).astype(np.float32))
         f_de = vq_encode(ke, Ce, 8, smooth=se, codes=codes_e, mat=Mt, prepare=True)
         us_de = time_events(lambda i: f_de(), 20, torch)
+        rec_m = torch.empty((1, 8, 8192, 128), dtype=torch.float16, device=dev)
+        f_dr = vq_encode_decode(ke, Ce, 8, smooth=se, codes=codes_e, recon=rec_m, mat=Mt,
+                                mat_inv=Mit, prepare=True)
+        us_dr = time_events(lambda i: f_dr(), 20, torch)
+        f_dd = vq_decode(codes_e, Ce, smooth=se, out=rec_m, mat_inv=Mit, prepare=True)
+        us_dd = time_events(lambda i: f_dd(), 20, torch)
         fdm = [vq_attend(q, kcs[j], Ck, vcs[j], Cv, scale=c["scale"], smooth=sm, kv_lens=kl,
                          out=out, workspace=ws, mat_inv=Mit, prepare=True) for j in range(n_sets)]
         us_da = time_events(lambda i: fdm[i % n_sets](), 100, torch)
         extra["dense_transform"] = {
             "encode_us": round(us_de, 2), "encode_Mtok_s": round(8192 / us_de, 3),
+            "encode_decode_us": round(us_dr, 2), "decode_us": round(us_dd, 2),
             "attend_gqa_long_W0_us": round(us_da, 2),
             "attend_GBps": round(attn_bytes / us_da / 1e3, 1),
-            "note": "random orthogonal M [128,128] fp32; encode on the dense-matrix kernel "
-                    "(rotation and search on the matrix cores), attention with the query "
-                    "pre-pass"}
-        log(f"[bench] dense transform: encode {us_de:.1f} us, gqa W=0 attend {us_da:.1f} us")
-        del fdm
+            "note": "random orthogonal M [128,128] fp32; encode, round trip (encode then "
+                    "decode by M^-1) and decode (fp16 out) with the rotations and the search "
+                    "on the matrix cores, attention with the query pre-pass"}
+        log(f"[bench] dense transform: encode {us_de:.1f} us, encode+decode {us_dr:.1f} us, "
+            f"decode {us_dd:.1f} us, gqa W=0 attend {us_da:.1f} us")
+        del fdm, rec_m
 
         # single-query decode, B=1 H=8 D=128
         for S in (512, 2048, 8192):

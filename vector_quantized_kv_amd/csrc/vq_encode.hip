@@ -1403,6 +1403,46 @@ void launch_one(const EncodeArgs& a, const Dims& d, const RowOffsets& o, hipStre
                      a.keys, a.codes_in, a.codebook, a.smooth, a.codes, a.recon, d, o);
 }
 
+// Stage a [D, D] matrix as the A operands of Y^T = M^T X^T on
+// v_mfma_f32_32x32x8_f16: entry (kc, ct, lane) holds M[8 kc + 4 (lane / 32)
+// + u][32 ct + lane mod 32], u < 4, scaled by 2^em so that the largest
+// magnitude lands in [2^13, 2^14), split into fp16 hi and lo.  Every thread
+// of the workgroup takes part; ends with a barrier.  Returns em.
+template <int D, int NT>
+__device__ __forceinline__ int stage_split_matrix(const float* __restrict__ rot, half4_t* s_mh,
+                                                  half4_t* s_ml, float* s_red) {
+  constexpr int NW = NT / 64, KC = D / 8, CT = D / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float m = 0.f;
+  for (int i = threadIdx.x; i < D * D / 4; i += NT) {
+    const float4 v = reinterpret_cast<const float4*>(rot)[i];
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) m = fmaxf(m, s_red[w]);
+  const int em = m > 0.f ? 14 - __builtin_amdgcn_frexp_expf(m) : 0;
+  for (int e = threadIdx.x; e < KC * CT * 64; e += NT) {
+    const int kc = e / (CT * 64), ct = (e / 64) % CT, ln = e & 63;
+    const int row = 8 * kc + 4 * (ln >> 5), col = 32 * ct + (ln & 31);
+    half4_t h, l;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float v = ldexpf(rot[(row + u) * D + col], em);
+      h[u] = (_Float16)v;
+      l[u] = (_Float16)(v - (float)h[u]);
+    }
+    s_mh[e] = h;
+    s_ml[e] = l;
+  }
+  __syncthreads();  // the matrix is staged; s_red may be reused
+  return em;
+}
+
 // Dense rotation on the matrix cores, for the encode (sub-vectors of 8, 8-bit
 // codes) and the transform-only mode: a wave takes 32 token-heads and forms
 // Y^T = M^T X^T on v_mfma_f32_32x32x8_f16, A = M^T (32 output dims x 8 input
@@ -1427,38 +1467,7 @@ __global__ __launch_bounds__(512) void pvq_dense_mfma_kernel(
   __shared__ float s_red[NW];
   __shared__ std::conditional_t<MODE == 0, F16Codebook, char> tab;
   __shared__ std::conditional_t<MODE == 0, float[NW][256], char> s_seeded;
-  // M's scale: its largest magnitude in [2^13, 2^14)
-  int em;
-  {
-    float m = 0.f;
-    for (int i = threadIdx.x; i < D * D / 4; i += NT) {
-      const float4 v = reinterpret_cast<const float4*>(rot)[i];
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    if (lane == 0) s_red[wave] = m;
-    __syncthreads();
-    m = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) m = fmaxf(m, s_red[w]);
-    em = m > 0.f ? 14 - __builtin_amdgcn_frexp_expf(m) : 0;
-    // entry (kc, ct, lane): M[8 kc + 4 hi + u][32 ct + l32], u < 4
-    for (int e = threadIdx.x; e < KC * CT * 64; e += NT) {
-      const int kc = e / (CT * 64), ct = (e / 64) % CT, ln = e & 63;
-      const int row = 8 * kc + 4 * (ln >> 5), col = 32 * ct + (ln & 31);
-      half4_t h, l;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float v = ldexpf(rot[(row + u) * D + col], em);
-        h[u] = (_Float16)v;
-        l[u] = (_Float16)(v - (float)h[u]);
-      }
-      s_mh[e] = h;
-      s_ml[e] = l;
-    }
-  }
-  __syncthreads();  // s_red is reused by the codebook staging
+  const int em = stage_split_matrix<D, NT>(rot, s_mh, s_ml, s_red);
   int sc = 0;
   if constexpr (MODE == 0) sc = f16_stage<NT>(cb, d.n_c, tab, s_red);
   else __syncthreads();
@@ -1553,6 +1562,86 @@ __global__ __launch_bounds__(512) void pvq_dense_mfma_kernel(
 }
 
 
+// Decode with an explicit matrix (sub-vectors of 8) on the matrix cores, and
+// the reconstruction half of a round trip: a wave takes 32 token-heads, reads
+// each one's codes, gathers the centroid rows straight into the B operand
+// layout from the staged search codebook (-2 C 2^sc as fp16 hi + lo, entry
+// [code / 32][lane half][code mod 32]), and forms Y^T = (M^-1)^T X^T in three
+// split-fp16 passes as the forward rotation; Y is unscaled by
+// -2^-(sc + 1 + em), multiplied by s and stored (fp16 rounds to nearest).
+// A code past n_c decodes as centroid n_c - 1, as on the per-lane path.
+template <int D>
+__global__ __launch_bounds__(512) void pvq_dense_mfma_decode_kernel(
+    const uint8_t* __restrict__ codes_in, const float* __restrict__ cb, const float* __restrict__ smooth,
+    const float* __restrict__ rot_inv, void* __restrict__ recon, Dims d, RowOffsets offs) {
+  constexpr int NW = 8, NT = NW * 64;
+  constexpr int KC = D / 8, CT = D / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hi = lane >> 5, l32 = lane & 31;
+  __shared__ half4_t s_mh[KC * CT * 64], s_ml[KC * CT * 64];  // [kc][ct][lane]
+  __shared__ float s_red[NW];
+  __shared__ F16Codebook tab;
+  const int em = stage_split_matrix<D, NT>(rot_inv, s_mh, s_ml, s_red);
+  const int sc = f16_stage<NT>(cb, d.n_c, tab, s_red);
+  const int unscale = -(sc + 1 + em);
+  const int row_bytes = d.code_bits == 4 ? KC / 2 : KC;
+
+  const long long n_th = (long long)d.B * d.H * d.S;
+  const long long n_tiles = (n_th + 31) / 32;
+  for (long long tile = (long long)blockIdx.x * NW + wave; tile < n_tiles;
+       tile += (long long)gridDim.x * NW) {
+    const long long th = tile * 32 + l32;
+    const bool valid = th < n_th;
+    const long long thc = valid ? th : 0;
+    const int bh = (int)(thc / d.S);
+    const int h = bh % d.H;
+    const int t = (int)(thc - (long long)bh * d.S);
+    const int off = d.use_row_offsets ? offs.v[bh / d.H] : d.S_off;
+    const uint8_t* cr = codes_in + ((long long)bh * d.S_cap + off + t) * row_bytes;
+    half4_t bh_[KC], bl_[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      int c = d.code_bits == 4 ? ((cr[kc >> 1] >> (4 * (kc & 1))) & 15) : cr[kc];
+      c = min(c, d.n_c - 1);
+      const int e = (c >> 5) * 64 + hi * 32 + (c & 31);
+      bh_[kc] = tab.ah[e];
+      bl_[kc] = tab.al[e];
+    }
+    const float* sr = smooth ? smooth + (size_t)(d.smooth_rows == 1 ? 0 : h) * D + 4 * hi : nullptr;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float16_t acc = {};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const half4_t ah = s_mh[(kc * CT + ct) * 64 + lane], al = s_ml[(kc * CT + ct) * 64 + lane];
+        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(ah, bh_[kc], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(al, bh_[kc], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x8f16(ah, bl_[kc], acc, 0, 0, 0);
+      }
+      if (valid) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float y[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) y[u] = -ldexpf(acc[4 * q + u], unscale);
+          if (sr) {
+            const float4 sv = *reinterpret_cast<const float4*>(sr + 32 * ct + 8 * q);
+            y[0] *= sv.x; y[1] *= sv.y; y[2] *= sv.z; y[3] *= sv.w;
+          }
+          const long long o = th * D + 32 * ct + 8 * q + 4 * hi;
+          if (d.recon_dtype == 1)
+            store_f16<4>(reinterpret_cast<__half*>(recon) + o, y);
+          else
+            store_f32<4>(reinterpret_cast<float*>(recon) + o, y);
+        }
+      }
+      // one output tile at a time (the scheduler would otherwise keep every
+      // tile's accumulators live)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 Dims make_dims(const EncodeArgs& a) {
   return Dims{a.B, a.H, a.S, a.n_c, a.smooth_rows, a.transform, a.S_cap, a.S_off,
               a.use_row_offsets, a.recon_dtype, make_fastdiv((uint32_t)a.S), make_fastdiv((uint32_t)a.H),
@@ -1580,22 +1669,43 @@ hipError_t launch_ds(const EncodeArgs& a, const RowOffsets* offs, int mode, hipS
     if constexpr (D <= 128) {
       // forward rotations on the matrix cores: the transform-only mode and
       // the encode of sub-vectors of 8 with 8-bit codes
-      if (mode == 3 || (mode == 0 && DS == 8 && a.code_bits == 8)) {
-        void (*mk)(const __half*, const float*, const float*, const float*, uint8_t*, float*, Dims,
-                   RowOffsets) = mode == 3 ? pvq_dense_mfma_kernel<D, 3> : pvq_dense_mfma_kernel<D, 0>;
+      // one grid-stride pass of 512-thread workgroups, as many as are
+      // resident at once, over tiles of 32 token-heads
+      auto mfma_blocks = [&](const void* k) {
         int per_cu = 0, cus = 0, dev = 0;
         (void)hipGetDevice(&dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mk, 512, 0) != hipSuccess || per_cu <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 512, 0) != hipSuccess || per_cu <= 0)
           per_cu = 1;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
           cus = 256;
         const long long tiles = (n_th + 31) / 32;
         const long long want = (tiles + 7) / 8;
-        const unsigned blocks = (unsigned)std::max(1LL, std::min(want, (long long)per_cu * cus));
-        hipLaunchKernelGGL(mk, dim3(blocks), dim3(512), 0, st, a.keys, a.codebook, a.smooth, a.rot,
-                           a.codes, reinterpret_cast<float*>(a.recon), d, o);
-        return hipGetLastError();
+        return (unsigned)std::max(1LL, std::min(want, (long long)per_cu * cus));
+      };
+      const bool fwd = mode == 3 || ((mode == 0 || mode == 1) && DS == 8 && a.code_bits == 8);
+      if (fwd) {
+        // the forward rotation (and the search): the transform-only mode,
+        // and the encode of sub-vectors of 8 with 8-bit codes, also as the
+        // first half of a round trip
+        void (*mk)(const __half*, const float*, const float*, const float*, uint8_t*, float*, Dims,
+                   RowOffsets) = mode == 3 ? pvq_dense_mfma_kernel<D, 3> : pvq_dense_mfma_kernel<D, 0>;
+        hipLaunchKernelGGL(mk, dim3(mfma_blocks(reinterpret_cast<const void*>(mk))), dim3(512), 0, st,
+                           a.keys, a.codebook, a.smooth, a.rot, a.codes, reinterpret_cast<float*>(a.recon),
+                           d, o);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess || mode != 1) return e;
+      }
+      if constexpr (DS == 8) {
+        if (mode == 2 || (mode == 1 && fwd)) {
+          // decode by M^-1: of the given codes, or (round trip) of the codes
+          // the launch above wrote
+          auto dk = pvq_dense_mfma_decode_kernel<D>;
+          hipLaunchKernelGGL(dk, dim3(mfma_blocks(reinterpret_cast<const void*>(dk))), dim3(512), 0, st,
+                             mode == 2 ? a.codes_in : a.codes, a.codebook, a.smooth, a.rot_inv, a.recon,
+                             d, o);
+          return hipGetLastError();
+        }
       }
       // one grid-stride pass: as many workgroups as are resident at once;
       // the encode of sub-vectors of 8 (one matrix in LDS) runs 12 waves per
