@@ -257,6 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const float* __restrict__ qpre, StreamParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   constexpr uint32_t kKRow = 16 * BITS / 8, kVRow = 32 * BITS / 8;  // code bytes per token
+  constexpr int kVR = BITS == 8 ? 16 : 4;  // value-code registers per block and lane
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -557,6 +558,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
   }
 #pragma unroll
   for (int b = 0; b < 4; ++b) sel[b] = 0x0c0c0000u | ((4u + ((b + rb) & 3)) << 8) | (uint32_t)b;
+  // 4 x 4 byte transpose across a lane quad (4-bit value codes): selectors
+  // of its two v_perm steps at quad position lane mod 4
+  const uint32_t tsel1 = (lane & 3) < 2 ? 0x05040100u : 0x03020706u;
+  const uint32_t tsel2 = (lane & 1) ? 0x03070105u : 0x06020400u;
   // value replica + 64 KiB: 8-byte rows, replica lane mod 32 (8-bit); 16-byte
   // pair rows, replica lane mod 16 (4-bit)
   const uint32_t vbase = BITS == 8 ? (uint32_t)(lane & 31) * 8u | (1u << 16) : (uint32_t)(lane & 15) * 16u | (1u << 16);
@@ -619,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // (one per register) so that the prefetch of the next block is not
     // waited for until that block is processed.  Load j of the wave reads
     // keys 4 j .. 4 j + 3: one contiguous span.
-    auto load_codes = [&](int tb, uint4& kc, uint32_t (&vr)[16]) {
+    auto load_codes = [&](int tb, uint4& kc, uint32_t (&vr)[kVR]) {
       if constexpr (BITS == 8) {
         const u32x4_t k4 = __builtin_amdgcn_raw_buffer_load_b128(krs, (uint32_t)(tb + lane) * 16u, 0, 0);
         kc = make_uint4(k4[0], k4[1], k4[2], k4[3]);
@@ -629,9 +634,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       } else {
         const u32x2_t k2 = __builtin_amdgcn_raw_buffer_load_b64(krs, (uint32_t)(tb + lane) * 8u, 0, 0);
         kc = make_uint4(k2[0], k2[1], 0u, 0u);
-        const uint32_t vo = (uint32_t)(tb + grp16) * 16u + (uint32_t)(lane & 15);
+        // lane (quad position j, quad m) of a row reads the 4 code bytes
+        // 4 m .. 4 m + 3 of keys 4 (4 i + j) + g, i = 0..3; a 4 x 4 byte
+        // transpose across the quad (in the stage) then gives each lane its
+        // byte 4 m + j of keys 4 (4 i + 0..3) + g
+        const uint32_t vo = (uint32_t)(tb + grp16 + 4 * (lane & 3)) * 16u + 4u * (uint32_t)((lane & 15) >> 2);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) vr[k] = __builtin_amdgcn_raw_buffer_load_b8(vrs, vo + 64u * k, 0, 0);
+        for (int i = 0; i < 4; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b32(vrs, vo + 256u * i, 0, 0);
       }
     };
 
@@ -661,7 +670,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     };
     int nA = wave, nB = wave + kW, nC = 0;
     uint4 kcA, kcB, kcC;
-    uint32_t vrA[16], vrB[16], vrC[16];
+    uint32_t vrA[kVR], vrB[kVR], vrC[kVR];
     if (t0 + 64 * nA < t1) {
       load_codes(blk(nA), kcA, vrA);
       load_codes(blk(nB), kcB, vrB);
@@ -773,7 +782,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     const std::integral_constant<int, 0> lo_half;
     const std::integral_constant<int, 1> hi_half;
 
-    auto stage = [&](int tb, const uint4& kc, const uint32_t (&vr)[16], bool pending) {
+    auto stage = [&](int tb, const uint4& kc, const uint32_t (&vr)[kVR], bool pending) {
       // ---- scores: 16 table rows of 4 fp32 (one per query row), in two
       // halves, each overlapping half of the previous block's value MFMAs
       float4_t sc;
@@ -888,6 +897,17 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
 
       // ---- this block's value rows, consumed by the next stage ---------
       // rows of key pair k: [key 0 sub 2n, key 1 sub 2n, key 0 sub 2n+1, key 1 sub 2n+1]
+      uint32_t t4[4];  // (4-bit) byte 4 m + j of keys 4 (4 i + 0..3) + g, per i
+      if constexpr (BITS == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t X = vr[i];
+          const uint32_t Z = __builtin_amdgcn_perm(
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)X, 0x4e, 0xf, 0xf, true), X, tsel1);
+          t4[i] = __builtin_amdgcn_perm(
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)Z, 0xb1, 0xf, 0xf, true), Z, tsel2);
+        }
+      }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         if constexpr (BITS == 8) {
@@ -903,8 +923,10 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
           vg[k][3] = lds_ld<u32x2_t>(__builtin_amdgcn_perm(w, vbase, 0x0c020700u));
         } else {
           // one pair-table row per key: its code byte of sub-vectors 2n, 2n + 1
-          vp[k][0] = lds_ld<u32x4_t>((vr[2 * k] << 8) | vbase);
-          vp[k][1] = lds_ld<u32x4_t>((vr[2 * k + 1] << 8) | vbase);
+          const uint32_t y = t4[k >> 1];
+          const uint32_t s0 = (k & 1) ? 0x0c020600u : 0x0c020400u, s1 = (k & 1) ? 0x0c020700u : 0x0c020500u;
+          vp[k][0] = lds_ld<u32x4_t>(__builtin_amdgcn_perm(y, vbase, s0));
+          vp[k][1] = lds_ld<u32x4_t>(__builtin_amdgcn_perm(y, vbase, s1));
         }
       }
     };
