@@ -126,8 +126,9 @@ int vq_supports_shape(int n_centroids, int n_sub, int head_dim);
  *               each with 0 <= off_b and off_b + S <= S_cap.
  * The centroid index minimizes the fp32 squared distance summed over the
  * sub-vector; exact ties resolve to the lowest index.
- * Errors: INVALID_ARGUMENT for null pointers, nonpositive sizes, S_off or
- * offsets out of range, D % sub_dim != 0, smooth_rows not in {1, H},
+ * Errors: INVALID_ARGUMENT for null pointers, nonpositive sizes, B * H * S
+ * of 2^31 or more, S_off or offsets out of range, D % sub_dim != 0,
+ * smooth_rows not in {1, H},
  * code_bits not in {8, 4}, n_centroids > 16 or an odd number of
  * sub-vectors with 4-bit codes; UNSUPPORTED outside the caps.  S = 0 or
  * B = 0 is a no-op returning VQ_OK.

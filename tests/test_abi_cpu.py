@@ -84,6 +84,8 @@ def test_encode_validation(lib):
     assert enc(lib, S_off=4) == INVALID                 # 4 + 8 > 8
     assert enc(lib, S_off=-1) == INVALID
     assert enc(lib, H=0) == INVALID
+    assert enc(lib, B=1 << 16, H=1 << 8, S=1 << 7, S_cap=1 << 7) == INVALID   # 2^31 token-heads
+    assert b"2^31" in lib.vq_last_error()
     assert enc(lib, D=96, dsub=4) == UNSUPPORTED        # head dim cap
     assert enc(lib, D=128, dsub=1) == UNSUPPORTED       # 128 sub-vectors > 64
     offs = (ctypes.c_int32 * 2)(0, 5)
@@ -117,6 +119,9 @@ def test_decode_and_encode_decode_validation(lib):
     assert st == INVALID                                # 4-bit codes, 32 centroids
     st = lib.vq_decode(P, 1, 2, 8, 8, 0, P, 256, 4, 8, None, 1, 2, P, None, 64, P, 0, None)
     assert st == INVALID                                # decode reads mat_inv
+    st = lib.vq_decode(P, 1 << 16, 1 << 8, 1 << 7, 1 << 7, 0, P, 256, 4, 8, None, 1, 1, None, None, 64, P, 0,
+                       None)
+    assert st == INVALID and b"2^31" in lib.vq_last_error()   # 2^31 token-heads
 
 
 def enc_kv(lib, B=1, H=2, S=8, D=128, dk=8, dv=4, nk=256, nv=256, S_cap=8, S_off=0, offs=None,

@@ -107,6 +107,15 @@ int hip_status(const char* what, hipError_t e) {
   return fail(VQ_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
 }
 
+// The encode and decode kernels index token-heads (b, h, t) with 32-bit
+// arithmetic.
+int check_token_heads(const char* what, int B, int H, int S) {
+  if ((long long)B * H * S >= (1LL << 31))
+    return fail(VQ_ERR_INVALID_ARGUMENT, "%s: B * H * S = %lld token-heads, need fewer than 2^31", what,
+                (long long)B * H * S);
+  return VQ_OK;
+}
+
 // Shared validation of vq_encode / vq_encode_decode.
 int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
                  const float* codebook, int n_c, int sub_dim, int code_bits, const float* smooth,
@@ -116,7 +125,9 @@ int check_encode(const char* what, const void* keys, int B, int H, int S, int D,
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0, H > 0, S >= 0 (got %d, %d, %d)", what, B, H, S);
   if (!keys || !codebook || !codes)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: keys, codebook and codes must be non-null", what);
-  int st = check_quantizer(what, D, n_c, sub_dim);
+  int st = check_token_heads(what, B, H, S);
+  if (st) return st;
+  if ((st = check_quantizer(what, D, n_c, sub_dim))) return st;
   if (st) return st;
   if ((st = check_code_bits(what, code_bits, n_c, D / sub_dim, 2))) return st;
   if ((st = check_smooth(what, smooth, smooth_rows, H))) return st;
@@ -395,7 +406,9 @@ int vq_decode(const uint8_t* codes, int B, int H, int S, int S_cap, int S_off,
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0, H > 0, S >= 0 (got %d, %d, %d)", what, B, H, S);
   if (!codes || !codebook || !out)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: codes, codebook and out must be non-null", what);
-  int st = check_quantizer(what, D, n_centroids, sub_dim);
+  int st = check_token_heads(what, B, H, S);
+  if (st) return st;
+  if ((st = check_quantizer(what, D, n_centroids, sub_dim))) return st;
   if (st) return st;
   if ((st = check_code_bits(what, code_bits, n_centroids, D / sub_dim, 2))) return st;
   if ((st = check_smooth(what, smooth, smooth_rows, H))) return st;

@@ -150,41 +150,40 @@ __device__ __forceinline__ void wht_in_lane(float (&x)[DS]) {
 // partner of lane j for bit m is lane j ^ m in the same token-head group.
 template <int NSUB, int DS>
 __device__ __forceinline__ void wht_cross_lane(float (&x)[DS], int j) {
-  // the value of lane ^ M without a trip through LDS: DPP quad permutes
-  // (M = 1, 2), row shifts into alternate 4-lane banks (M = 4), a row
-  // rotation (M = 8), and v_permlane16/32_swap of x with itself, which
-  // leaves (own, partner) in lanes with bit M clear and (partner, own) where
-  // it is set (M = 16, 32)
-  auto partner = [](float v, auto mc) {
+  // Lane j gets x + x(j ^ M) where bit M of j is clear and x(j ^ M) - x
+  // where it is set: fma(sg, a, b) with sg = -1 / +1, which rounds as that
+  // sum or difference.  The partner's value comes without a trip through
+  // LDS: DPP quad permutes (M = 1, 2), row shifts into alternate 4-lane
+  // banks (M = 4), a row rotation (M = 8); v_permlane16/32_swap of x with
+  // itself (M = 16, 32) returns (own, partner) where bit M is clear and
+  // (partner, own) where it is set, so fma(sg, second, first) needs no select.
+  auto butterfly = [](float v, float sg, auto mc) {
     constexpr int M = decltype(mc)::value;
     const int vi = __float_as_int(v);
     if constexpr (M == 1) {
-      return __int_as_float(__builtin_amdgcn_mov_dpp(vi, 0xb1, 0xf, 0xf, false));
+      return fmaf(sg, v, __int_as_float(__builtin_amdgcn_mov_dpp(vi, 0xb1, 0xf, 0xf, false)));
     } else if constexpr (M == 2) {
-      return __int_as_float(__builtin_amdgcn_mov_dpp(vi, 0x4e, 0xf, 0xf, false));
+      return fmaf(sg, v, __int_as_float(__builtin_amdgcn_mov_dpp(vi, 0x4e, 0xf, 0xf, false)));
     } else if constexpr (M == 4) {
       const int t = __builtin_amdgcn_update_dpp(0, vi, 0x104, 0xf, 0x5, false);
-      return __int_as_float(__builtin_amdgcn_update_dpp(t, vi, 0x114, 0xf, 0xa, false));
+      return fmaf(sg, v, __int_as_float(__builtin_amdgcn_update_dpp(t, vi, 0x114, 0xf, 0xa, false)));
     } else if constexpr (M == 8) {
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, vi, 0x128, 0xf, 0xf, false));
+      return fmaf(sg, v, __int_as_float(__builtin_amdgcn_update_dpp(0, vi, 0x128, 0xf, 0xf, false)));
     } else if constexpr (M == 16) {
       const auto r = __builtin_amdgcn_permlane16_swap((unsigned)vi, (unsigned)vi, false, false);
-      return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+      return fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
     } else {
       static_assert(M == 32, "lane bit");
       const auto r = __builtin_amdgcn_permlane32_swap((unsigned)vi, (unsigned)vi, false, false);
-      return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+      return fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
     }
   };
   auto stage = [&](auto mc) {
     constexpr int M = decltype(mc)::value;
     if constexpr (M < NSUB) {
-      const bool upper = (j & M) != 0;
+      const float sg = (j & M) ? -1.f : 1.f;
 #pragma unroll
-      for (int e = 0; e < DS; ++e) {
-        const float y = partner(x[e], mc);
-        x[e] = upper ? (y - x[e]) : (x[e] + y);
-      }
+      for (int e = 0; e < DS; ++e) x[e] = butterfly(x[e], sg, mc);
     }
   };
   stage(std::integral_constant<int, 1>{});
@@ -231,14 +230,18 @@ __device__ __forceinline__ void pvq_body(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = wave / CSPLIT, part = wave % CSPLIT;
   const int j = lane % NSUB;
-  const long long n_th = (long long)d.B * d.H * d.S;
-  const long long th = (long long)block * TPB + grp * TPW + lane / NSUB;
+  // token-head indices are below 2^31 (checked on the host), so the index
+  // arithmetic is 32-bit with the divisors' precomputed multipliers
+  const uint32_t n_th = (uint32_t)d.B * (uint32_t)d.H * (uint32_t)d.S;
+  const uint32_t th = (uint32_t)block * TPB + grp * TPW + lane / NSUB;
   const bool valid = th < n_th;
-  const long long thc = valid ? th : 0;
-  const int t = (int)(thc % d.S);
-  const long long bh = thc / d.S;
-  const int h = (int)(bh % d.H);
-  const int b = (int)(bh / d.H);
+  const uint32_t th32 = valid ? th : 0u;
+  const uint32_t bh32 = fast_div(th32, d.div_S);
+  const uint32_t b32 = fast_div(bh32, d.div_H);
+  const int t = (int)(th32 - bh32 * (uint32_t)d.S);
+  const int h = (int)(bh32 - b32 * (uint32_t)d.H);
+  const int b = (int)b32;
+  const long long thc = th32, bh = bh32;
   const float* srow = smooth ? smooth + (long long)(d.smooth_rows == 1 ? 0 : h) * D + j * DS : nullptr;
   // the output slot's row offset (a kernel-argument array indexed by the
   // lane's batch row) is requested with the inputs, not after the search
@@ -768,6 +771,126 @@ __global__ __launch_bounds__(threads_for<CSPLIT>()) void pvq_kv_kernel(
   else
     pvq_body<D, DSV, 0, CSPLIT>(blockIdx.x - k_blocks, values, nullptr, v_cb, nullptr, v_codes, nullptr,
                                 dv, offs);
+}
+
+// Encode of one token-head by a workgroup of 4 waves, for appends of a few
+// token-heads (one new token per row of a decode step): the search is
+// spread over many workgroups instead of the waves of a few, whose shared
+// SIMDs would serialize it.  Lane (replica r, sub-vector j) of wave w holds
+// the token-head's sub-vector j (every wave and replica computes the same
+// smoothing and rotation) and scans the centroids c = p, p + P, p + 2 P, ...
+// of part p = R w + r (R = 64 / NSUB replicas per wave, P = 4 R parts), with
+// the fp32 squared distance summed over e in order and a strict '<'.  The P
+// partial minima merge as (distance, index) pairs, so the result is the
+// lowest index among the centroids at the minimal distance: the sequential
+// search's answer.
+template <int D, int DS>
+__device__ __forceinline__ void pvq_short_body(
+    uint32_t th, const __half* __restrict__ keys, const float* __restrict__ cb,
+    const float* __restrict__ smooth, uint8_t* __restrict__ codes, const Dims& d,
+    const RowOffsets& offs) {
+  constexpr int NSUB = D / DS;  // sub-vectors per token-head (<= 64)
+  constexpr int R = 64 / NSUB;  // replicas per wave
+  constexpr int P = 4 * R;      // parts of the codebook
+  static_assert(NSUB <= 64 && 64 % NSUB == 0 && 256 * DS % (4 * kThreads) == 0, "layout");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane % NSUB;
+  const int part = R * wave + lane / NSUB;
+  const uint32_t bh = fast_div(th, d.div_S);
+  const uint32_t b = fast_div(bh, d.div_H);
+  const int t = (int)(th - bh * (uint32_t)d.S);
+  const int h = (int)(bh - b * (uint32_t)d.H);
+  const float* srow = smooth ? smooth + (d.smooth_rows == 1 ? 0 : h) * D + j * DS : nullptr;
+  const int off = d.use_row_offsets ? offs.v[b] : d.S_off;
+
+  // the row's inputs and the codebook (zero rows past n_c) are requested
+  // together
+  const RawHalves<DS> raw = load_raw_f16<DS>(keys + (size_t)th * D + j * DS);
+  float sv[DS];
+  if (srow) {
+#pragma unroll
+    for (int e = 0; e < DS; ++e) sv[e] = srow[e];
+  }
+  __shared__ float s_cb[256 * DS];
+  __shared__ float s_best[kThreads];
+  __shared__ int s_idx[kThreads];
+  {
+    constexpr int kPer = 256 * DS / (4 * kThreads);  // float4 per thread
+    float4 v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int i = threadIdx.x + k * kThreads;  // float4 index
+      v[k] = 4 * i < d.n_c * DS ? reinterpret_cast<const float4*>(cb)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) reinterpret_cast<float4*>(s_cb)[threadIdx.x + k * kThreads] = v[k];
+  }
+  __syncthreads();
+
+  float x[DS];
+  cvt_raw_f16<DS>(raw, x);
+  if (srow) {
+#pragma unroll
+    for (int e = 0; e < DS; ++e) x[e] = x[e] / sv[e];
+  }
+  if (d.transform) wht<D, DS>(x, j);
+
+  float best = INFINITY;
+  int idx = part < d.n_c ? part : 0x7fffffff;
+  for (int c = part; c < d.n_c; c += P) {
+    const float* cc = s_cb + c * DS;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < DS; ++e) {
+      const float df = x[e] - cc[e];
+      acc = fmaf(df, df, acc);
+    }
+    if (acc < best) { best = acc; idx = c; }
+  }
+  s_best[threadIdx.x] = best;
+  s_idx[threadIdx.x] = idx;
+  __syncthreads();
+  if (wave != 0 || lane >= NSUB) return;
+  // lane j of wave 0 merges the P parts of sub-vector j (every partial is
+  // read before any is compared)
+  float bk[P];
+  int ik[P];
+#pragma unroll
+  for (int k = 1; k < P; ++k) {
+    const int src = 64 * (k / R) + NSUB * (k % R) + j;  // part k
+    bk[k] = s_best[src];
+    ik[k] = s_idx[src];
+  }
+#pragma unroll
+  for (int k = 1; k < P; ++k) {
+    const bool lt = bk[k] < best || (bk[k] == best && ik[k] < idx);
+    best = lt ? bk[k] : best;
+    idx = lt ? ik[k] : idx;
+  }
+  // 4-bit codes: the even sub-vector's lane packs its odd neighbour's code
+  // (lane + 1, the same row of 16 lanes: DPP row_shl:1) into the high nibble
+  const int idx_next = __builtin_amdgcn_mov_dpp(idx, 0x101, 0xf, 0xf, false);
+  const size_t slot = (size_t)bh * d.S_cap + off + t;
+  if (d.code_bits == 4) {
+    if (!(j & 1)) codes[slot * (NSUB / 2) + j / 2] = (uint8_t)((idx & 15) | ((idx_next & 15) << 4));
+  } else {
+    codes[slot * NSUB + j] = (uint8_t)idx;
+  }
+}
+
+// The keys (workgroups [0, n_th)) and the values (the rest) of a short
+// append, one token-head per workgroup.
+template <int D, int DSK, int DSV>
+__global__ __launch_bounds__(kThreads) void pvq_short_kv_kernel(
+    const __half* __restrict__ keys, const __half* __restrict__ values,
+    const float* __restrict__ k_cb, const float* __restrict__ v_cb, const float* __restrict__ smooth,
+    uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes, Dims dk, Dims dv,
+    RowOffsets offs, uint32_t n_th) {
+  if (blockIdx.x < n_th)
+    pvq_short_body<D, DSK>(blockIdx.x, keys, k_cb, smooth, k_codes, dk, offs);
+  else
+    pvq_short_body<D, DSV>(blockIdx.x - n_th, values, v_cb, nullptr, v_codes, dv, offs);
 }
 
 // Nearest centroid as a dense contraction on the matrix cores.  For a
@@ -1808,8 +1931,15 @@ template <int D, int DSK, int DSV>
 bool try_kv_fused(const EncodeArgs& k, const EncodeArgs& v, const RowOffsets& o, int split,
                   hipStream_t st) {
   if (k.sub_dim != DSK || v.sub_dim != DSV) return false;
-  if (split == 16) launch_kv_fused<D, DSK, DSV, 16>(k, v, o, st);
-  else launch_kv_fused<D, DSK, DSV, 4>(k, v, o, st);
+  if (split == 16) {
+    // the shortest appends: one token-head per workgroup
+    const uint32_t n_th = (uint32_t)k.B * (uint32_t)k.H * (uint32_t)k.S;
+    hipLaunchKernelGGL((pvq_short_kv_kernel<D, DSK, DSV>), dim3(2 * n_th), dim3(kThreads), 0, st, k.keys,
+                       v.keys, k.codebook, v.codebook, k.smooth, k.codes, v.codes, make_dims(k),
+                       make_dims(v), o, n_th);
+  } else {
+    launch_kv_fused<D, DSK, DSV, 4>(k, v, o, st);
+  }
   return true;
 }
 
