@@ -5,11 +5,13 @@ One step = one pass of the whole decode hot path over a batch of the long-
 context GQA workload (B=16, H_q=32, H_kv=8, D=128, 32768-slot code buffers,
 ragged lengths uniform in [16384, 32768], causal, no window):
   1. encode each row's new key (smooth + Walsh-Hadamard + product VQ, d_k=8)
-     and value (product VQ, d_v=4) into the code buffers at slot len_b - 1
-     (one vq_encode_kv call);
+     and value (product VQ, d_v=4) into the code buffers at slot len_b - 1;
   2. fused attention of the 32 query heads straight from the key and value
      codes (dual transform, LUT scores, online softmax over split-K chunks,
      value-codebook gather, split merge).
+Both run as one vq_decode_step call (the attention kernel's workgroups
+encode the new tokens while they set up); the same step as two calls
+(vq_encode_kv, then vq_attend) is timed beside it.
 The code buffers rotate over enough copies to exceed the 256 MiB Infinity
 Cache, so the attention reads come from HBM.  `value` is the step's
 algorithmic HBM bytes / step time (GB/s).  Secondary workloads (key encode
@@ -35,7 +37,7 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0
 MIB = 1 << 20
 COPY_BYTES = 1 << 30
 ATTEND_SOURCES = ("vq_attend.hip", "vq_attend_mfma.hip", "vq_attend_stream.hip", "vq_attend_tile.hip",
-                  "vq_internal.h")
+                  "vq_internal.h", "vq_lane.h")
 
 
 def parse():
@@ -330,8 +332,8 @@ def main():
     import numpy as np
     import torch
 
-    from vector_quantized_kv_amd import (attend_workspace, synth, vq_attend, vq_decode, vq_encode,
-                                         vq_encode_decode, vq_encode_kv)
+    from vector_quantized_kv_amd import (attend_workspace, synth, vq_attend, vq_decode, vq_decode_step,
+                                         vq_encode, vq_encode_decode, vq_encode_kv)
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -385,13 +387,17 @@ def main():
     q, kn, vn, kl = t(c["q"]), t(k_new), t(v_new), t(c["kv_lens"])
     out = torch.empty((B, Hq, 1, D), dtype=torch.float16, device=dev)
     ws = attend_workspace(q, kc0, 0)
-    steps = []
+    steps, fused = [], []
     for i in range(n_sets):
         ekv = vq_encode_kv(kn, vn, Ck, dk, Cv, dv, smooth=sm, k_codes=kcs[i], v_codes=vcs[i],
                            row_offsets=offs, prepare=True)
         at = vq_attend(q, kcs[i], Ck, vcs[i], Cv, scale=c["scale"], smooth=sm, kv_lens=kl,
                        causal=True, sliding_window=0, out=out, workspace=ws, prepare=True)
         steps.append((ekv, at))
+        # the same step in one launch: the append runs inside the attention kernel
+        fused.append(vq_decode_step(q, kn, vn, kcs[i], Ck, vcs[i], Cv, scale=c["scale"], smooth=sm,
+                                    kv_lens=kl, causal=True, sliding_window=0, out=out, workspace=ws,
+                                    prepare=True))
 
     enc_bytes = 2 * B * Hkv * D * 2 + B * Hkv * (D // dk + D // dv) + (256 * (dk + dv) + Hkv * D) * 4
     attn_fixed = 2 * B * Hq * D * 2 + 256 * (dk + dv) * 4 + Hkv * D * 4 + B * 4
@@ -399,6 +405,9 @@ def main():
     step_bytes = attn_bytes + enc_bytes
 
     def step(i):
+        fused[i % n_sets]()
+
+    def step_two_calls(i):
         ekv, at = steps[i % n_sets]
         ekv(); at()
 
@@ -434,7 +443,16 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
-    log(f"[bench] step: {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s")
+    log(f"[bench] step: {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s (vq_decode_step, one launch)")
+    for i in range(args.warmup):
+        step_two_calls(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step_two_calls(i)
+    torch.cuda.synchronize()
+    two_call_us = (time.perf_counter() - t0) * 1e6 / args.steps
+    log(f"[bench] step as two calls (vq_encode_kv + vq_attend): {two_call_us:.1f} us")
 
     # attention kernel alone, HIP events on the launch stream, same rotation
     attn_us = time_events(lambda i: steps[i % n_sets][1](), max(args.steps, 100), torch, warm=100)
@@ -468,12 +486,13 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "gqa_long decode step: encode 1 new K/V token per row + fused attention "
-                        "from codes, B=16 H_q=32 H_kv=8 D=128 S_cap=32768 ragged lens "
-                        "U[16384,32768] causal W=0, d_k=8 d_v=4, 256 centroids",
+                        "from codes (vq_decode_step, one launch), B=16 H_q=32 H_kv=8 D=128 "
+                        "S_cap=32768 ragged lens U[16384,32768] causal W=0, d_k=8 d_v=4, 256 centroids",
             "global_batch": B, "seq_len": int(lens.max()), "sum_kv_len": int(lens.sum()),
             "step_bytes": step_bytes, "code_buffer_sets": n_sets,
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_two_calls": round(two_call_us, 2),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),

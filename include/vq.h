@@ -336,6 +336,44 @@ int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D,
               float scale, int causal, int sliding_window,
               void* out_f16, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * One decode step of a code cache in one launch: the append of one new
+ * token per row (the cache's update_and_fetch, "veloxquant_mlx.cache.
+ * vecinfer_cache module") followed by the fused attention of vq_attend with
+ * S_q = 1 (fused_sdpa on the same page, "Metal Kernels API", "Fused SDPA").
+ * Same result as
+ *   vq_encode_kv(k_new, v_new -> k_codes, v_codes at per-row offsets
+ *                kv_lens[b] - 1, the same codebooks, smooth and transform)
+ *   vq_attend(q over the updated caches, kv_lens)
+ * (the same codes byte for byte, the same output), with the encode done by
+ * the attention kernel's workgroups while they set up, before any of them
+ * reads the new slots.
+ *
+ *   q_f16       [B, H_q, 1, D] fp16 raw queries
+ *   k_new_f16, v_new_f16   [B, H_kv, 1, D] fp16: the new token's key and
+ *               value of every (row, kv head)
+ *   k_codes, v_codes       the caches as in vq_attend; slot kv_lens[b] - 1
+ *               of row b is written (rows with kv_lens[b] <= 0 get no
+ *               append), every other slot is only read
+ *   kv_lens     DEVICE int32 [B], required: the lengths after the append,
+ *               clamped to [0, S_cap]
+ *   other arguments as for vq_attend (n_centroids for both codebooks,
+ *   code_bits 8 or 4, transform 0 or 1)
+ * Errors: those of vq_attend; INVALID_ARGUMENT when k_new, v_new or kv_lens
+ * is NULL; UNSUPPORTED unless the shape runs on the streaming kernel
+ * (vq_attend_path(...) == VQ_PATH_STREAM with S_q = 1) with head dim 128,
+ * key / value sub_dim 8 / 4 and transform 0 or 1: for other shapes call
+ * vq_encode_kv and vq_attend.
+ */
+int vq_decode_step(const void* q_f16, const void* k_new_f16, const void* v_new_f16,
+                   int B, int H_q, int D,
+                   uint8_t* k_codes, const float* k_codebook, int k_sub_dim,
+                   const float* smooth, int smooth_rows, int transform,
+                   uint8_t* v_codes, const float* v_codebook, int v_sub_dim,
+                   int n_centroids, int code_bits, int H_kv, int S_cap, const int32_t* kv_lens,
+                   float scale, int causal, int sliding_window,
+                   void* out_f16, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of the per-GPU device scratch array used by vq_attend_noalloc. */
 #define VQ_NOALLOC_SCRATCH_BYTES (16u << 20)
 

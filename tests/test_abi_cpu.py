@@ -174,6 +174,29 @@ def test_attend_validation(lib):
     assert att(lib, transform=2, mat_inv=P, B=0) == OK
 
 
+def step(lib, B=16, Hq=32, D=128, dk=8, dv=4, n_c=256, Hkv=8, S_cap=32768, W=0, causal=1, ws=P,
+         ws_bytes=1 << 30, smooth=P, srows=8, bits=8, transform=1, kn=P, vn=P, lens=P):
+    return lib.vq_decode_step(P, kn, vn, B, Hq, D, P, P, dk, smooth, srows, transform, P, P, dv, n_c, bits,
+                              Hkv, S_cap, lens, 0.1, causal, W, P, ws, ws_bytes, None)
+
+
+def test_decode_step_validation(lib):
+    assert step(lib, kn=None) == INVALID
+    assert step(lib, vn=None) == INVALID
+    assert step(lib, lens=None) == INVALID                # the lengths after the append are required
+    assert b"kv_lens" in lib.vq_last_error()
+    assert step(lib, Hq=30) == INVALID                    # H_q % H_kv, as vq_attend
+    assert step(lib, dk=4) == UNSUPPORTED                 # key sub_dim other than 8
+    assert b"vq_encode_kv and vq_attend" in lib.vq_last_error()
+    assert step(lib, S_cap=64) == UNSUPPORTED             # too few keys for the streaming kernel
+    assert step(lib, D=64) == UNSUPPORTED
+    assert step(lib, ws_bytes=16) == WORKSPACE
+    assert step(lib, B=0) == OK
+    if not torch.cuda.is_available():
+        assert step(lib) == NO_DEVICE                     # valid: stops at the device check
+        assert step(lib, bits=4, n_c=16, transform=0) == NO_DEVICE
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="a device is visible")
 def test_valid_calls_report_no_device(lib):
     assert enc(lib) == NO_DEVICE

@@ -48,6 +48,13 @@ SIGNATURES = {
                           c_int, c_int, c_int, c_int, c_void_p,
                           c_float, c_int, c_int,
                           c_void_p, c_void_p, c_size_t, c_void_p]),
+    "vq_decode_step": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
+                               c_void_p, c_void_p, c_int,
+                               c_void_p, c_int, c_int,
+                               c_void_p, c_void_p, c_int,
+                               c_int, c_int, c_int, c_int, c_void_p,
+                               c_float, c_int, c_int,
+                               c_void_p, c_void_p, c_size_t, c_void_p]),
     "vq_attend_noalloc": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
                                   c_void_p, c_void_p, c_int,
                                   c_void_p, c_int, c_int, c_void_p, c_void_p,

@@ -377,6 +377,38 @@ def vq_attend(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None
                  prepare=prepare, result=out)
 
 
+def vq_decode_step(q, k_new, v_new, k_codes, k_codebook, v_codes, v_codebook, *, scale, kv_lens,
+                   smooth=None, transform=True, causal=True, sliding_window=0, out=None,
+                   workspace=None, code_bits=8, stream=None, prepare=False):
+    """One decode step in one launch: the codes of the new token k_new /
+    v_new [B, H_kv, 1, D] (fp16) go to slot kv_lens[b] - 1 of k_codes /
+    v_codes (kv_lens: device int32 [B], the lengths after the append), then
+    the attention of q [B, H_q, 1, D] over the updated caches, as
+    vq_encode_kv + vq_attend; returns fp16 [B, H_q, 1, D].  Shapes off the
+    streaming kernel raise VQError (UNSUPPORTED): use those two calls."""
+    B, Hq, Sq, D, dk, dv, Hkv, S_cap, sm, rows, out = _attend_args(
+        q, k_codes, k_codebook, v_codes, v_codebook, smooth, kv_lens, out, code_bits)
+    if Sq != 1:
+        raise ValueError(f"q must hold one query position per row (S_q = 1, got {Sq})")
+    if kv_lens is None:
+        raise ValueError("kv_lens (the lengths after the append) is required")
+    _need(k_new, "k_new", torch.float16, shape=(B, Hkv, 1, D))
+    _need(v_new, "v_new", torch.float16, shape=(B, Hkv, 1, D))
+    if workspace is None:
+        workspace = attend_workspace(q, k_codes, sliding_window)
+    _need(workspace, "workspace", None, 1)
+    tr, m, mi = _transform(transform, None, None, D)
+    _on_device(q=q, k_new=k_new, v_new=v_new, k_codes=k_codes, k_codebook=k_codebook,
+               v_codes=v_codes, v_codebook=v_codebook, kv_lens=kv_lens, out=out,
+               workspace=workspace, smooth=sm)
+    return _call("vq_decode_step", _ptr(q), _ptr(k_new), _ptr(v_new), B, Hq, D, _ptr(k_codes),
+                 _ptr(k_codebook), dk, _ptr(sm), rows, tr, _ptr(v_codes), _ptr(v_codebook), dv,
+                 k_codebook.shape[0], code_bits, Hkv, S_cap, _ptr(kv_lens), float(scale),
+                 int(bool(causal)), int(sliding_window), _ptr(out), _ptr(workspace),
+                 workspace.numel() * workspace.element_size(), _stream(stream), prepare=prepare,
+                 result=out)
+
+
 def vq_attend_noalloc(q, k_codes, k_codebook, v_codes, v_codebook, *, scale, smooth=None,
                       transform=True, kv_lens=None, causal=True, sliding_window=0, out=None,
                       code_bits=8, mat=None, mat_inv=None, stream=None, prepare=False):

@@ -219,7 +219,8 @@ int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, in
                 const uint8_t* v_codes, const float* v_codebook,
                 int v_sub_dim, int n_centroids, int code_bits, int H_kv, int S_cap,
                 const int32_t* kv_lens, float scale, int causal, int sliding_window, void* out_f16,
-                void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
+                void* workspace, size_t workspace_bytes, bool noalloc, void* stream,
+                const void* k_new = nullptr, const void* v_new = nullptr) {
   if (B < 0 || S_q < 0)
     return fail(VQ_ERR_INVALID_ARGUMENT, "%s: need B >= 0 and S_q >= 0 (got %d, %d)", what, B, S_q);
   if (H_q <= 0 || H_kv <= 0 || S_cap <= 0)
@@ -246,6 +247,20 @@ int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, in
   if ((st = check_aligned(what, {q_f16, k_codes, k_codebook, smooth, v_codes, v_codebook, kv_lens,
                                  out_f16, workspace, mat_inv})))
     return st;
+  const bool append = k_new != nullptr || v_new != nullptr;
+  if (append) {
+    if (!k_new || !v_new || !kv_lens)
+      return fail(VQ_ERR_INVALID_ARGUMENT, "%s: k_new, v_new and kv_lens must be non-null", what);
+    if ((st = check_aligned(what, {k_new, v_new}))) return st;
+    if (B > 0 && (S_q != 1 || transform == 2 || k_sub_dim != 8 || v_sub_dim != 4 ||
+                  attend_path(B, H_q, S_q, D, H_kv, S_cap, sliding_window, k_sub_dim, v_sub_dim,
+                              n_centroids, code_bits, transform) != VQ_PATH_STREAM))
+      return fail(VQ_ERR_UNSUPPORTED,
+                  "%s: the fused append runs on the streaming kernel only (one new token per row, "
+                  "head dim 128, key / value sub_dim 8 / 4, transform 0 or 1, enough keys); call "
+                  "vq_encode_kv and vq_attend instead",
+                  what);
+  }
   if (B == 0 || S_q == 0) return VQ_OK;
   AttendPlan plan;
   if (!plan_attend(B, H_q, S_q, D, H_kv, S_cap, sliding_window, &plan))
@@ -277,6 +292,8 @@ int attend_impl(const char* what, const void* q_f16, int B, int H_q, int S_q, in
   a.rot_inv = transform == 2 ? mat_inv : nullptr;
   a.scale_log2e = scale * 1.4426950408889634f;
   a.causal = causal; a.window = sliding_window;
+  a.k_new = reinterpret_cast<const __half*>(k_new);
+  a.v_new = reinterpret_cast<const __half*>(v_new);
   return hip_status(what, launch_attend(a, plan, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -475,6 +492,19 @@ int vq_attend(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* 
                      smooth_rows, transform, mat, mat_inv, v_codes, v_codebook, v_sub_dim, n_centroids, code_bits,
                      H_kv, S_cap, kv_lens, scale, causal, sliding_window, out_f16, workspace,
                      workspace_bytes, false, stream);
+}
+
+int vq_decode_step(const void* q_f16, const void* k_new_f16, const void* v_new_f16, int B, int H_q,
+                   int D, uint8_t* k_codes, const float* k_codebook, int k_sub_dim, const float* smooth,
+                   int smooth_rows, int transform, uint8_t* v_codes, const float* v_codebook,
+                   int v_sub_dim, int n_centroids, int code_bits, int H_kv, int S_cap,
+                   const int32_t* kv_lens, float scale, int causal, int sliding_window, void* out_f16,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  return attend_impl("vq_decode_step", q_f16, B, H_q, 1, D, k_codes, k_codebook, k_sub_dim, smooth,
+                     smooth_rows, transform, nullptr, nullptr, v_codes, v_codebook, v_sub_dim, n_centroids,
+                     code_bits, H_kv, S_cap, kv_lens, scale, causal, sliding_window, out_f16, workspace,
+                     workspace_bytes, false, stream, k_new_f16, v_new_f16);
 }
 
 int vq_attend_noalloc(const void* q_f16, int B, int H_q, int S_q, int D, const uint8_t* k_codes,

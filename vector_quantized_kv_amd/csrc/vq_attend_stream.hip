@@ -53,6 +53,7 @@
 //           staged p (rounded to nearest; the row sums add the rounded p),
 //           and B = two gathered value rows taken as they are.
 #include "vq_internal.h"
+#include "vq_lane.h"
 
 #include <algorithm>
 #include <atomic>
@@ -83,6 +84,10 @@ constexpr int kMaxChunks = 4096;       // partial slots reserved for chunks (>= 
 // the next table build and the refill of the load pipeline cost about as
 // much time as streaming this many keys.
 constexpr int kSegCharge = 2048;
+// Keys charged, in the decode step, to the chunk holding a unit's last key
+// for the encode of the unit's new token (about 3 us of that workgroup's
+// setup).
+constexpr int kAppendCharge = 1024;
 // int slots of the scan area: 0..3 the chunk plan, kW the block-claim
 // counter, kQExp and kQExp + 1 the exponents of the two query buffers
 constexpr int kQExp = kW + 4;
@@ -248,13 +253,22 @@ __device__ __forceinline__ int unit_len(const StreamParams& p, const int* lens, 
 
 // BITS: width of the key and value codes, 8 (one per byte) or 4 (two per
 // byte, the even sub-vector in the low nibble).
-template <int BITS>
+// APPEND: the decode step's append runs in the same launch.  Every row b
+// has one new token, k_new / v_new [B, H_kv, 1, D], whose codes go to slot
+// len_b - 1 of the caches before the keys are read.  The workgroup holding
+// a unit's last key encodes that unit's new token during its setup (waves
+// 1..3 the key, 4..7 the value, while wave 0 prepares the query rows), with
+// the arithmetic of the encode kernels (smoothing x / s, the same rotation
+// butterflies, fp32 squared distances summed in order, the lowest index on
+// ties), and stores its codes before any wave loads that key.
+template <int BITS, bool APPEND>
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_stream_kernel(
-    const __half* __restrict__ q, const uint8_t* __restrict__ k_codes,
+    const __half* __restrict__ q, uint8_t* k_codes,
     const float* __restrict__ k_codebook, const float* __restrict__ smooth,
-    const uint8_t* __restrict__ v_codes, const float* __restrict__ v_codebook,
+    uint8_t* v_codes, const float* __restrict__ v_codebook,
     const int32_t* __restrict__ kv_lens, int* __restrict__ header, float* __restrict__ part,
-    const float* __restrict__ qpre, StreamParams p) {
+    const float* __restrict__ qpre, const __half* __restrict__ k_new, const __half* __restrict__ v_new,
+    StreamParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   constexpr uint32_t kKRow = 16 * BITS / 8, kVRow = 32 * BITS / 8;  // code bytes per token
   constexpr int kVR = BITS == 8 ? 16 : 4;  // value-code registers per block and lane
@@ -277,7 +291,11 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     int bgq, rgq, bq_b;
     unit_coords(p, uq, bgq, rgq, bq_b);
     const int gq = bgq - bq_b * p.Hkv;
-    const int bq = lane >> 2, ir = lane & 3;
+    // (with the append, lane values re-derived here rather than hoisted:
+    // the registers are short)
+    int ql = lane;
+    if constexpr (APPEND) asm volatile("" : "+v"(ql));
+    const int bq = ql >> 2, ir = ql & 3;
     const int rho = 4 * rgq + ir;
     const int rc = rho < p.GS ? rho : p.GS - 1;
     const int ip = (int)fast_div((uint32_t)rc, p.div_g);
@@ -437,8 +455,13 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
     // vs(u) = pre[u] + charge u, and virtual y in it maps to key
     // pre[u] + max(0, y - vs(u)).  These spans tile the virtual space (an
     // empty unit's span maps to the next unit's first key), so every key
-    // falls in exactly one chunk.
-    const int V = Tw + p.charge * (p.U - 1);
+    // falls in exactly one chunk.  With the decode step's append, every span
+    // also ends in p.charge_end virtual keys (the encode of the unit's new
+    // token, done by the workgroup holding its last key): then vs(u) =
+    // pre[u] + (charge + charge_end) u, the span is [vs(u) - charge [u > 0],
+    // vs(u) + len + charge_end), and y maps to key pre[u] +
+    // min(len, max(0, y - vs(u))).
+    const int V = Tw + p.charge * (p.U - 1) + p.charge_end * p.U;
     const int C0 = max(p.cmin, (V + G - 1) / G);
     const int ys = c * C0 < V ? c * C0 : V;
     const int ye = min(V, ys + C0);
@@ -448,12 +471,12 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       for (int base = 0; base < p.U; base += 64) {
         const int uu = base + lane;
         bool hs = false, he = false;
-        int a0 = 0, vs = 0;
+        int a0 = 0, vs = 0, ln = 0;
         if (uu < p.U) {
           a0 = pre[uu];
-          const int a1 = pre[uu + 1];
-          vs = a0 + p.charge * uu;
-          const int lo = uu > 0 ? vs - p.charge : vs, hi = vs + (a1 - a0);
+          ln = pre[uu + 1] - a0;
+          vs = a0 + (p.charge + p.charge_end) * uu;
+          const int lo = uu > 0 ? vs - p.charge : vs, hi = vs + ln + p.charge_end;
           hs = lo <= ys && ys < hi;
           he = lo < ye && ye <= hi;   // the unit holding the chunk's last key
         }
@@ -462,19 +485,21 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
         if (ms && !found_s) {
           const int l = (int)__builtin_ctzll(ms);
           uf = base + l;
-          st = __builtin_amdgcn_readlane(a0 + max(0, ys - vs), l);
+          st = __builtin_amdgcn_readlane(a0 + min(ln, max(0, ys - vs)), l);
           found_s = true;
         }
         if (me) {
           const int l = (int)__builtin_ctzll(me);
-          en = __builtin_amdgcn_readlane(a0 + max(0, ye - vs), l);
+          en = __builtin_amdgcn_readlane(a0 + min(ln, max(0, ye - vs)), l);
           break;
         }
       }
       if (st >= en) {
         st = en = Tw;  // the chunk holds switch cost only
       } else {
-        while (pre[uf + 1] == pre[uf]) ++uf;  // an empty unit's span maps onto the next start
+        // the first unit with a key at or past st: skips empty units, and a
+        // unit of which the chunk holds only the append charge
+        while (pre[uf + 1] <= st) ++uf;
         quf = uf;
       }
     }
@@ -668,10 +693,160 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
       const int tb = t0 + 64 * n;
       return tb < t1 ? tb : t0;
     };
+    // ---- append: this segment holds key len - 1, the unit's new token ----
+    // Partial searches: keys on waves 1..3 (lane (r, j): sub-vector j,
+    // centroids c = 4 (w - 1) + r + 12 k), values on waves 4..7 (lane
+    // (r, j): centroids c = 2 (w - 4) + r + 8 k), each merged over its
+    // wave's replicas and written as (distance, index) pairs to the idle
+    // query buffer; wave 1 merges them after the next barrier.  The value
+    // waves stage the fp32 value codebook in the idle p staging area (each
+    // writes the same rows and reads them back in its own issue order).
+    const int tn = len - 1;
+    const bool has_new = APPEND && tn >= t0 && tn < t1;
+    // the first loads cover blocks 0 .. 2 kW - 1: if the new key is among
+    // them, they wait until its codes are stored; so do those of wave 1,
+    // which stores them (its wait for the stores then covers nothing else)
+    const bool defer_loads = has_new && (tn < t0 + 2 * kW * 64 || wave == 1);
+    float* const apx = reinterpret_cast<float*>(lds + kQs) + (qbuf ^ 1) * kRows * kD;
+    auto merge_pair = [](float& best, int& idx, float ob, int oi) {
+      const bool lt = ob < best || (ob == best && oi < idx);
+      best = lt ? ob : best;
+      idx = lt ? oi : idx;
+    };
+    // (global accesses through buffer descriptors: a wave-uniform base and a
+    // 32-bit lane offset, no per-lane 64-bit addresses held across the loop)
+    // The lane index is re-read through an empty asm so that the lane values
+    // derived from it are computed here, not hoisted out of the segment loop
+    // into registers the streaming loop needs.
+    if constexpr (APPEND) {
+      if (has_new && wave >= 1) {
+        int al = lane;
+        asm volatile("" : "+v"(al));
+        const int g = bg - bb * p.Hkv;
+        float best = INFINITY;
+        int idx = 0x7fffffff;
+        if (wave <= 3) {
+          const int r = al >> 4, jk = al & 15, pt = 4 * (wave - 1) + r;
+          const __amdgpu_buffer_rsrc_t kn_rs = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<__half*>(k_new + (size_t)bg * kD), (short)0, kD * 2, kBufWord3);
+          const u32x4_t kr = __builtin_amdgcn_raw_buffer_load_b128(kn_rs, (uint32_t)jk * 16u, 0, 0);
+          RawHalves<8> raw;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) raw.w[i] = kr[i];
+          float sv[8], x[8];
+          if (smooth) {
+            const __amdgpu_buffer_rsrc_t sm_rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(smooth + (p.smooth_rows == 1 ? 0 : g) * kD), (short)0, kD * 4, kBufWord3);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const u32x4_t sr = __builtin_amdgcn_raw_buffer_load_b128(sm_rs, (uint32_t)jk * 32u + 16u * h2, 0, 0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sv[4 * h2 + i] = __uint_as_float(sr[i]);
+            }
+          }
+          cvt_raw_f16<8>(raw, x);
+          if (smooth) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = x[e] / sv[e];
+          }
+          if (p.transform == 1) wht<kD, 8>(x, jk);
+          const float* cbk = reinterpret_cast<const float*>(lds + kCbk);
+          if (pt < p.n_c) idx = pt;
+          // unrolled so that several centroid rows are read from LDS at once
+#pragma unroll 4
+          for (int cc = pt; cc < p.n_c; cc += 12) {
+            const float* cr = cbk + cc * 8;
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float df = x[e] - cr[e];
+              acc = fmaf(df, df, acc);
+            }
+            if (acc < best) { best = acc; idx = cc; }
+          }
+          merge_pair(best, idx, __shfl_xor(best, 32), __shfl_xor(idx, 32));
+          merge_pair(best, idx, __shfl_xor(best, 16), __shfl_xor(idx, 16));
+          if (al < 16) {
+            apx[2 * (16 * (wave - 1) + jk)] = best;
+            reinterpret_cast<int*>(apx)[2 * (16 * (wave - 1) + jk) + 1] = idx;
+          }
+        } else {
+          const int r = al >> 5, jv = al & 31, pt = 2 * (wave - 4) + r;
+          const __amdgpu_buffer_rsrc_t vn_rs = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<__half*>(v_new + (size_t)bg * kD), (short)0, kD * 2, kBufWord3);
+          const u32x2_t vr2 = __builtin_amdgcn_raw_buffer_load_b64(vn_rs, (uint32_t)jv * 8u, 0, 0);
+          RawHalves<4> raw;
+          raw.w[0] = vr2[0];
+          raw.w[1] = vr2[1];
+          // rows past n_c read as zeros (outside the descriptor's range)
+          const __amdgpu_buffer_rsrc_t cv_rs = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<float*>(v_codebook), (short)0, p.n_c * 16, kBufWord3);
+          u32x4_t vrow[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vrow[i] = __builtin_amdgcn_raw_buffer_load_b128(cv_rs, (uint32_t)(al + 64 * i) * 16u, 0, 0);
+          float* const vcb = reinterpret_cast<float*>(lds + kPStage);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(vcb + 4 * (al + 64 * i)) = vrow[i];
+          lds_order();
+          float x[4];
+          cvt_raw_f16<4>(raw, x);
+          if (pt < p.n_c) idx = pt;
+#pragma unroll 8
+          for (int cc = pt; cc < p.n_c; cc += 8) {
+            const float* cr = vcb + cc * 4;
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float df = x[e] - cr[e];
+              acc = fmaf(df, df, acc);
+            }
+            if (acc < best) { best = acc; idx = cc; }
+          }
+          merge_pair(best, idx, __shfl_xor(best, 32), __shfl_xor(idx, 32));
+          if (al < 32) {
+            apx[2 * (48 + 32 * (wave - 4) + jv)] = best;
+            reinterpret_cast<int*>(apx)[2 * (48 + 32 * (wave - 4) + jv) + 1] = idx;
+          }
+        }
+      }
+    }
+    // wave 1, after the next barrier: the merged codes of the new token, and
+    // their stores (which complete before the table barrier)
+    auto append_store = [&]() {
+      int al = lane;
+      asm volatile("" : "+v"(al));
+      const int* const apxi = reinterpret_cast<const int*>(apx);
+      float best = INFINITY;
+      int idx = 0x7fffffff;
+      const int jk = al, jv = al - 32;
+      if (al < 16) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) merge_pair(best, idx, apx[2 * (16 * k + jk)], apxi[2 * (16 * k + jk) + 1]);
+      } else if (al >= 32) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          merge_pair(best, idx, apx[2 * (48 + 32 * k + jv)], apxi[2 * (48 + 32 * k + jv) + 1]);
+      }
+      // 4-bit codes: the even sub-vector's lane packs its odd neighbour's
+      // code (lane + 1, the same row of 16 lanes) into the high nibble
+      const int idx_next = __builtin_amdgcn_mov_dpp(idx, 0x101, 0xf, 0xf, false);
+      const uint8_t code = BITS == 8 ? (uint8_t)idx : (uint8_t)((idx & 15) | ((idx_next & 15) << 4));
+      // slot tn of the (b, g) code rows, through the rows' load descriptors
+      if (al < 16) {
+        if (BITS == 8 || !(jk & 1))
+          __builtin_amdgcn_raw_buffer_store_b8(code, krs, (uint32_t)tn * kKRow + (uint32_t)(BITS == 8 ? jk : jk / 2), 0, 0);
+      } else if (al >= 32) {
+        if (BITS == 8 || !(jv & 1))
+          __builtin_amdgcn_raw_buffer_store_b8(code, vrs, (uint32_t)tn * kVRow + (uint32_t)(BITS == 8 ? jv : jv / 2), 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before the barrier
+    };
+
     int nA = wave, nB = wave + kW, nC = 0;
     uint4 kcA, kcB, kcC;
     uint32_t vrA[kVR], vrB[kVR], vrC[kVR];
-    if (t0 + 64 * nA < t1) {
+    if (!defer_loads && t0 + 64 * nA < t1) {
       load_codes(blk(nA), kcA, vrA);
       load_codes(blk(nB), kcB, vrB);
     }
@@ -730,8 +905,14 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 
           *reinterpret_cast<float4*>(lds + kLut + 16 * e) = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
         }
       }
+      if (has_new && wave == 1) append_store();
     }
     __syncthreads();
+    // the first loads of a segment whose new key is among them
+    if (defer_loads && t0 + 64 * nA < t1) {
+      load_codes(blk(nA), kcA, vrA);
+      load_codes(blk(nB), kcB, vrB);
+    }
     // the next unit's query rows, written while the other waves stream
     if (u_next >= 0 && wave == 0) make_query(u_next, qbuf ^ 1);
 
@@ -1094,6 +1275,7 @@ bool stream_plan(int B, int Hq, int Sq, int D, int Hkv, int S_cap, int window, i
     // shares tend to split at unit starts: charging switches there only
     // breaks that alignment
     sp->charge = window > 0 ? 0 : kSegCharge;
+    sp->charge_end = 0;
     sp->div_g = make_fastdiv((uint32_t)G);
     sp->div_nrg = make_fastdiv((uint32_t)n_rg);
     sp->div_hkv = make_fastdiv((uint32_t)Hkv);
@@ -1120,16 +1302,19 @@ hipError_t launch_attend_stream(const AttendArgs& a, StreamParams sp, size_t lds
   sp.causal = a.causal;
   sp.window = a.window;
   sp.fold = (a.transform == 1 ? WhtNorm<kD>::value : 1.f) * a.scale_log2e;
+  sp.charge_end = a.k_new ? kAppendCharge : 0;
   const size_t header_bytes = ((size_t)sp.U * 8 + 255) / 256 * 256;
   int* header = reinterpret_cast<int*>(a.partials);
   float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.partials) + header_bytes);
-  auto kern = a.code_bits == 4 ? attend_stream_kernel<4> : attend_stream_kernel<8>;
+  const bool append = a.k_new != nullptr;
+  auto kern = a.code_bits == 4 ? (append ? attend_stream_kernel<4, true> : attend_stream_kernel<4, false>)
+                               : (append ? attend_stream_kernel<8, true> : attend_stream_kernel<8, false>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, a.q, a.k_codes,
-                     a.k_codebook, a.smooth, a.v_codes, a.v_codebook, a.kv_lens, header, part, a.q_pre,
-                     sp);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, a.q, const_cast<uint8_t*>(a.k_codes),
+                     a.k_codebook, a.smooth, const_cast<uint8_t*>(a.v_codes), a.v_codebook, a.kv_lens, header,
+                     part, a.q_pre, a.k_new, a.v_new, sp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = (long long)a.B * a.Hq * a.Sq;

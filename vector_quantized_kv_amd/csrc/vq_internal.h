@@ -62,6 +62,8 @@ struct AttendArgs {
   const float* rot_inv;     // transform == 2: [D, D] M^-1 (the query uses its transpose)
   const float* q_pre;       // set by launch_attend for transform 2: [B, H_q, S_q, D] fp32
                             // dual-transformed, scale-free query rows in the workspace
+  const __half* k_new;      // decode step: NULL, or [B, H_kv, 1, D] new keys and values whose
+  const __half* v_new;      // codes the streaming kernel writes to slot kv_lens[b] - 1 first
 };
 
 struct AttendPlan {
@@ -114,6 +116,7 @@ struct StreamParams {
   int B, Hq, Sq, Hkv, S_cap, n_c, smooth_rows, transform, causal, window;
   int G, GS, n_rg, U, cmin;
   int charge;  // virtual keys charged for a segment switch in the chunk plan
+  int charge_end;  // virtual keys charged after each unit's last key (the fused append)
   FastDiv div_g, div_nrg, div_hkv;  // by G, n_rg and H_kv
   float fold;  // WHT normalization (if any) * scale * log2(e)
 };
