@@ -326,6 +326,27 @@ def test_binding_rejects_wrong_shapes(lib):
         api.vq_attend(q, kc, cb, kc, cb, kv_lens=torch.zeros(2, dtype=i32),
                       out=torch.zeros(2, 8, 1, 64, dtype=f16), workspace=torch.zeros(16, dtype=u8),
                       smooth=torch.zeros(4, 64), **att_kw)
+    # the fused decode step: new tokens [B, H_kv, 1, D], one query position, lengths required
+    kn = torch.zeros(2, 4, 1, 64, dtype=f16)
+    lens = torch.zeros(2, dtype=i32)
+    step_cases = [
+        (lambda: api.vq_decode_step(q, torch.zeros(2, 4, 2, 64, dtype=f16), kn, kc, cb, kc, cb, kv_lens=lens,
+                                    **att_kw), "k_new"),
+        (lambda: api.vq_decode_step(q, kn, torch.zeros(2, 3, 1, 64, dtype=f16), kc, cb, kc, cb, kv_lens=lens,
+                                    **att_kw), "v_new"),
+        (lambda: api.vq_decode_step(q, kn, kn.float(), kc, cb, kc, cb, kv_lens=lens, **att_kw), "v_new"),
+        (lambda: api.vq_decode_step(q, kn, kn, kc, cb, kc, cb, kv_lens=None, **att_kw), "kv_lens"),
+        (lambda: api.vq_decode_step(torch.zeros(2, 8, 2, 64, dtype=f16), kn, kn, kc, cb, kc, cb, kv_lens=lens,
+                                    **att_kw), "S_q"),
+        (lambda: api.vq_decode_step(q, kn, kn, kc, cb, torch.zeros(2, 4, 99, 16, dtype=u8), cb,
+                                    kv_lens=lens, **att_kw), "v_codes"),
+    ]
+    for fn, what in step_cases:
+        with pytest.raises(ValueError, match=what):
+            fn()
+    with pytest.raises(ValueError, match="device tensor"):
+        api.vq_decode_step(q, kn, kn, kc, cb, kc, cb, kv_lens=lens, workspace=torch.zeros(16, dtype=u8),
+                           **att_kw)
 
 
 def test_attend_noalloc_validation(lib):
