@@ -122,3 +122,38 @@ def test_trim_rewinds_the_write_position(ring):
     out = cache.fused_sdpa(dev(q), 1 / math.sqrt(D)).cpu().numpy()
     ref = O.attend(q, kc, Ck, vc, Cv, scale=1 / math.sqrt(D), smooth=s, transform=True)
     check_attn(out, ref, f"attend after trim ring={ring}")
+
+
+@pytest.mark.parametrize("S_cap,bits", [(32768, 8), (32768, 4), (512, 8)])
+def test_decode_step(S_cap, bits):
+    """decode_step on a fused-mode cache (one vq_decode_step launch when the
+    shape runs on the streaming kernel, else update_and_fetch + fused_sdpa)
+    stores the same codes as the two calls on a twin cache, and attends
+    within the attention bar of them and of the oracle."""
+    from vector_quantized_kv_amd import vq_attend_path
+    k, v, s, Ck, Cv = make_inputs(3400 + bits + S_cap % 7, 303, bits)
+    kw = dict(smooth=dev(s), code_bits=bits)
+    a = VQKVCache(B, H, D, S_cap, dev(Ck), dev(Cv), **kw)
+    b = VQKVCache(B, H, D, S_cap, dev(Ck), dev(Cv), **kw)
+    for c in (a, b):
+        c.update_and_fetch(dev(k[:, :, :300]), dev(v[:, :, :300]))
+    rng = np.random.default_rng(3401)
+    n_c = Ck.shape[0]
+    print(f"[cache] decode_step S_cap={S_cap} {bits}-bit: path "
+          f"{vq_attend_path(B, 2 * H, 1, D, DK, DV, n_c, H, S_cap, code_bits=bits)}")
+    for t in range(300, 303):
+        q = synth.outlier_normal(rng, (B, 2 * H, 1, D), 2)
+        out_a = a.decode_step(dev(q), dev(k[:, :, t:t + 1]), dev(v[:, :, t:t + 1]), 1 / math.sqrt(D))
+        b.update_and_fetch(dev(k[:, :, t:t + 1]), dev(v[:, :, t:t + 1]))
+        out_b = b.fused_sdpa(dev(q), 1 / math.sqrt(D))
+        torch.cuda.synchronize()
+        assert a.size() == b.size() == t + 1
+        for x, y in zip(a.state, b.state):
+            assert torch.equal(x, y), "decode_step stored other codes than update_and_fetch"
+        check_attn(out_a.cpu().numpy(), out_b.cpu().numpy().astype(np.float64),
+                   f"decode_step S_cap={S_cap} {bits}-bit against the two calls")
+    kc, vc = stored_codes(a, bits)
+    check_codes(k, Ck, DK, s, True, kc, f"decode_step {bits}-bit keys")
+    check_codes(v, Cv, DV, None, False, vc, f"decode_step {bits}-bit values")
+    ref = O.attend(q, kc, Ck, vc, Cv, scale=1 / math.sqrt(D), smooth=s, transform=True)
+    check_attn(out_a.cpu().numpy(), ref, f"decode_step S_cap={S_cap} {bits}-bit against the oracle")

@@ -196,6 +196,39 @@ class VQKVCache:
                              kv_lens=self._lens, causal=causal, sliding_window=sliding_window,
                              code_bits=self.code_bits)
 
+    def decode_step(self, q, keys, values, scale, *, causal=True, sliding_window=0):
+        """One decode step of a fused-mode cache: append one token per row
+        (keys, values [B, H, 1, D]) and attend q [B, H_q, 1, D] over the
+        updated cache.  When the new token lands in slot size - 1 (a linear
+        cache, or a ring that has not wrapped) and the shape runs on the
+        streaming kernel, both happen in one vq_decode_step launch; otherwise
+        as update_and_fetch followed by fused_sdpa.  Same codes either way."""
+        if self.mode != "fused":
+            raise RuntimeError("decode_step needs a fused-mode cache")
+        B, H, S, D = keys.shape
+        if S != 1 or q.shape[2] != 1:
+            raise ValueError("decode_step appends one token and attends one query position per row")
+        n_after = self.size() + 1
+        (slot, _, _), = self.layout.append_spans(1)
+        fused = (slot == n_after - 1 and self.dk == 8 and self.dv == 4
+                 and api.vq_attend_path(self.B, q.shape[1], 1, self.D, self.dk, self.dv,
+                                        self.k_codebook.shape[0], self.H, self.S_cap, sliding_window,
+                                        code_bits=self.code_bits, transform=int(bool(self.transform))) == "stream")
+        if not fused:
+            self.update_and_fetch(keys, values)
+            return self.fused_sdpa(q, scale, causal=causal, sliding_window=sliding_window)
+        if (B, H, D) != (self.B, self.H, self.D) or tuple(values.shape) != tuple(keys.shape):
+            raise ValueError("keys/values do not match the cache's [B, H, *, D]")
+        if self._lens_val != n_after:
+            self._lens.fill_(n_after)
+            self._lens_val = n_after
+        out = api.vq_decode_step(q, keys.contiguous(), values.contiguous(), self.k_codes, self.k_codebook,
+                                 self.v_codes, self.v_codebook, scale=scale, kv_lens=self._lens,
+                                 smooth=self.smooth, transform=self.transform, causal=causal,
+                                 sliding_window=sliding_window, code_bits=self.code_bits)
+        self.layout.advance(1)
+        return out
+
     # -- byte accounting ------------------------------------------------------
     @property
     def compressed_key_bytes(self) -> int:
