@@ -30,7 +30,10 @@
 //                an LDS tile [dim][key] whose key axis is permuted to match
 //                those slots (a 4 x 4 byte transpose of the value codes
 //                across each lane quad, then a 4 x 4 half transpose of the
-//                gathered value rows).
+//                gathered value rows).  Two V^T buffers alternate between
+//                key tiles, so one barrier per tile (the tile's V^T is
+//                complete) suffices: the buffer a tile writes was last read
+//                two tiles before, ahead of the previous tile's barrier.
 //
 // Each workgroup writes (m, l, acc[128]) per query row and split; the split
 // merge kernel combines them.
@@ -51,11 +54,11 @@ constexpr int tKT = 64;       // keys per tile
 // replicas and lane l reads replica l mod 16, so gathers by any codes are
 // conflict-free.
 constexpr uint32_t tKTab = 0;       // key codebook hi [256][16 replicas][8 fp16] 64 KiB
-constexpr uint32_t tKLo = 65536;    // key codebook lo [256][16 replicas][8 fp16] 64 KiB
-constexpr uint32_t tVTab = 131072;  // value codebook  [256][4 replicas][4 fp16]   8 KiB
-constexpr uint32_t tVT = 139264;    // V^T tile        [128 dims][72 fp16]        18 KiB
+constexpr uint32_t tKLo = 65536;    // key codebook lo [256][8 replicas][8 fp16] 32 KiB
+constexpr uint32_t tVTab = 98304;   // value codebook  [256][4 replicas][4 fp16]   8 KiB
+constexpr uint32_t tVT = 106496;    // V^T tiles       [2][128 dims][72 fp16]     36 KiB
 constexpr uint32_t tRowB = 144;     // bytes per V^T row (64 fp16 + pad)
-constexpr uint32_t tAl = tVT + tD * tRowB;          // per-wave row rescale factors
+constexpr uint32_t tAl = tVT + 2 * tD * tRowB;      // per-wave row rescale factors
 constexpr uint32_t tLdsBytes = tAl + tW * 32 * 4;
 static_assert(tLdsBytes <= 160 * 1024, "LDS budget");
 constexpr float tLazyMargin = 8.f;
@@ -148,8 +151,7 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
     for (int r = 4 * half; r < 4 * half + 4; ++r) {
       lds_st<half8_t>(tKTab + code * 256 + r * 16, hi);
       lds_st<half8_t>(tKTab + code * 256 + (r + 8) * 16, hi);
-      lds_st<half8_t>(tKLo + code * 256 + r * 16, lo);
-      lds_st<half8_t>(tKLo + code * 256 + (r + 8) * 16, lo);
+      lds_st<half8_t>(tKLo + code * 128 + r * 16, lo);
     }
 #pragma unroll
     for (int r = 2 * half; r < 2 * half + 2; ++r) lds_st<u32x2_t>(tVTab + code * 32 + r * 8, hv);
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
 
   // ---- per-lane constants ---------------------------------------------------
   const uint32_t kbase = tKTab + (uint32_t)(lane & 15) * 16u;    // key hi replica (256 B per code)
-  const uint32_t kbase_lo = tKLo + (uint32_t)(lane & 15) * 16u;  // key lo replica (256 B per code)
+  const uint32_t kbase_lo = tKLo + (uint32_t)(lane & 7) * 16u;   // key lo replica (128 B per code)
   const uint32_t vtab = tVTab + (uint32_t)(lane & 3) * 8u;        // value replica
   // V^T decode task: lane quad (u = tid % 4) = keys 4 tq .. 4 tq + 3 x subs 4 sm .. 4 sm + 3,
   // quad tid / 4 = 16 sm + tq, so that the 32 lanes of each 8-byte V^T write
@@ -301,9 +303,10 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
 
   // one key tile; the next tile's codes are requested once this one's have
   // been consumed (after the scores), so they arrive during softmax and P V
-  auto tile = [&](int tb) {
+  auto tile = [&](int tb, uint32_t vtb) {
     // ---- V^T tile of this key tile, decoded by the whole workgroup --------
-    __syncthreads();  // every wave is done with the previous tile's V^T
+    // (two buffers: the one written here was last read two tiles ago, before
+    // the previous tile's barrier)
 #pragma unroll
     for (int j = 0; j < 1; ++j) {
       const int quad = tid >> 2;
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
       // the P V operand slots take the weights straight from the score
       // registers
       const uint32_t kpos = 32u * (uint32_t)(tq >> 3) + 8u * (uint32_t)(tq & 3) + 4u * (uint32_t)((tq >> 2) & 1);
-      const uint32_t base = tVT + dim0 * tRowB + 2 * kpos;
+      const uint32_t base = vtb + dim0 * tRowB + 2 * kpos;
       lds_st<u32x2_t>(base + 0 * tRowB, u32x2_t{__builtin_amdgcn_perm(R1.x, R0.x, 0x05040100u),
                                                  __builtin_amdgcn_perm(R3.x, R2.x, 0x05040100u)});
       lds_st<u32x2_t>(base + 1 * tRowB, u32x2_t{__builtin_amdgcn_perm(R1.x, R0.x, 0x07060302u),
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
       for (int c = 0; c < 4; ++c) {
         const uint32_t code = __builtin_amdgcn_ubfe(kw[c], 8u * kg, 8u);
         kv[c] = lds_ld<half8_t>((code << 8) | kbase);
-        kl[c] = lds_ld<half8_t>((code << 8) + kbase_lo);
+        kl[c] = lds_ld<half8_t>((code << 7) + kbase_lo);
       }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
       }
 #pragma unroll
       for (int nd = 0; nd < 8; ++nd) {
-        const half8_t vb = lds_ld<half8_t>(tVT + (16 * nd + n16) * tRowB + 2 * (32 * kc2 + 8 * kg));
+        const half8_t vb = lds_ld<half8_t>(vtb + (16 * nd + n16) * tRowB + 2 * (32 * kc2 + 8 * kg));
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
           oacc[mt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[mt], vb, oacc[mt][nd], 0, 0, 0);
@@ -452,9 +455,14 @@ __global__ __launch_bounds__(tThreads, 1) void attend_tile_kernel(
     }
   };
 
+  __syncthreads();  // the codebook tables are complete
   if (s_lo < s_hi) {
     load_codes(s_lo, kc, vc);
-    for (int tb = s_lo; tb < s_hi; tb += tKT) tile(tb);
+    uint32_t vtb = tVT;
+    for (int tb = s_lo; tb < s_hi; tb += tKT) {
+      tile(tb, vtb);
+      vtb ^= tVT ^ (tVT + tD * tRowB);
+    }
   }
 
   // ---- partials: (m, l, acc[128]) per row ------------------------------------
