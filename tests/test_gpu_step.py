@@ -140,3 +140,48 @@ def test_decode_step_unsupported_shape():
                        kv_lens=dev(c["kv_lens"]))
     torch.cuda.synchronize()
     assert np.array_equal(kc.cpu().numpy(), before)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_step_random_shapes(seed):
+    """Random shapes on the streaming kernel: batch size, kv heads, query
+    heads per kv head (1, 2: padded units; 8: two units per kv head), 8- or
+    4-bit codes, windows, causal or not, smoothing rows, ragged lengths with
+    empty and one-token rows.  Caches byte-equal to the two calls, outputs
+    within the attention bar of them and, on sampled rows, of the oracle."""
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(2, 7))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    bits = int(rng.choice([8, 4]))
+    n_c = 16 if bits == 4 else int(rng.choice([256, 97]))
+    U = B * Hkv * ((G + 3) // 4)
+    need = -(-(1 << 18) // U)          # keys per unit for the streaming kernel
+    S_cap = max(2048, 2 * need)
+    # odd seeds: a sliding window, long enough for the streaming kernel
+    window = int(rng.integers(need, S_cap)) if seed % 2 else 0
+    causal = bool(rng.integers(0, 2))
+    lens = rng.integers(0, S_cap + 1, size=B)
+    lens[0] = S_cap
+    lens[1] = int(rng.choice([0, 1]))
+    smooth_rows = int(rng.choice([0, 1, Hkv]))
+    transform = bool(rng.integers(0, 2))
+    c = step_case(6000 + seed, B, G * Hkv, Hkv, S_cap, lens.tolist(), bits, n_c, smooth_rows, transform)
+    print(f"[step] random {seed}: B={B} H_kv={Hkv} G={G} bits={bits} n_c={n_c} S_cap={S_cap} W={window} "
+          f"causal={causal} smooth_rows={smooth_rows} transform={transform} lens={lens.tolist()}")
+    assert vq_attend_path(B, G * Hkv, 1, 128, 8, 4, n_c, Hkv, S_cap, window, code_bits=bits,
+                          transform=int(transform)) == "stream"
+    kc, vc, out, kc2, vc2, out2 = run_step(c, causal, window)
+    assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2), "caches differ from vq_encode_kv's"
+    check_attn(out, out2.astype(np.float64), f"random {seed} against the two calls")
+    rows = [b for b, L in enumerate(lens) if L >= 1]
+    got_k = np.stack([unpacked(kc[b:b + 1, :, lens[b] - 1:lens[b]], bits)[0] for b in rows])
+    got_v = np.stack([unpacked(vc[b:b + 1, :, lens[b] - 1:lens[b]], bits)[0] for b in rows])
+    check_codes(c["k_new"][rows], c["k_codebook"], 8, c["smooth_full"], transform, got_k, f"random {seed} keys")
+    check_codes(c["v_new"][rows], c["v_codebook"], 4, None, False, got_v, f"random {seed} values")
+    sample = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 6), rng.integers(0, G * Hkv, 6))]
+    ref = O.attend(c["q"], unpacked(kc, bits), c["k_codebook"], unpacked(vc, bits), c["v_codebook"],
+                   scale=c["scale"], causal=causal, sliding_window=window, smooth=c["smooth_full"],
+                   transform=transform, kv_lens=c["kv_lens"], rows=sample)
+    for b, h in sample:
+        check_attn(out[b, h], ref[b, h], f"random {seed} row ({b}, {h})")
