@@ -185,3 +185,53 @@ def test_decode_step_random_shapes(seed):
                    transform=transform, kv_lens=c["kv_lens"], rows=sample)
     for b, h in sample:
         check_attn(out[b, h], ref[b, h], f"random {seed} row ({b}, {h})")
+
+
+def test_decode_step_graph_capture():
+    """vq_decode_step captured in a HIP graph (one launch of the streaming
+    kernel with the append, then the merge) and replayed with new inputs,
+    eager calls between the replays: each replay writes the eager codes and
+    matches the eager output (within the attention bar) and the oracle."""
+    from test_gpu_parity import oracle_attend, small_case
+    c = small_case(411, B=4, Hq=32, Hkv=8, Sq=1, D=128, dk=8, dv=4, S_cap=8192)
+    c["kv_lens"] = np.array([8192, 6000, 77, 8000], np.int32)
+    kc, vc = dev(c["k_codes"]), dev(c["v_codes"])
+    kb, vb, sm, kl = dev(c["k_codebook"]), dev(c["v_codebook"]), dev(c["smooth"]), dev(c["kv_lens"])
+    q = torch.empty((4, 32, 1, 128), dtype=torch.float16, device=DEV)
+    kn = torch.empty((4, 8, 1, 128), dtype=torch.float16, device=DEV)
+    vn = torch.empty_like(kn)
+    out = torch.empty_like(q)
+    ws = attend_workspace(q, kc, 0)
+
+    def new_inputs(seed):
+        r = np.random.default_rng(seed)
+        q.copy_(dev(synth.outlier_normal(r, (4, 32, 1, 128), 2)))
+        kn.copy_(dev(synth.outlier_normal(r, (4, 8, 1, 128), 2)))
+        vn.copy_(dev(synth.outlier_normal(r, (4, 8, 1, 128), 2)))
+
+    def step():
+        vq_decode_step(q, kn, vn, kc, kb, vc, vb, scale=c["scale"], smooth=sm, kv_lens=kl, causal=True,
+                       out=out, workspace=ws)
+
+    new_inputs(0)
+    step()                                   # eager warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        new_inputs(20 + rep)
+        g.replay()
+        torch.cuda.synchronize()
+        got, gk, gv = out.clone(), kc.clone(), vc.clone()
+        step()                               # eager, same inputs (rewrites the same slots)
+        torch.cuda.synchronize()
+        assert torch.equal(gk, kc) and torch.equal(gv, vc), f"replay {rep}: codes differ from eager"
+        check_attn(got.cpu().numpy(), out.cpu().numpy().astype(np.float64), f"step graph replay {rep} vs eager")
+        p = dict(c, q=q.cpu().numpy())
+        check_attn(got.cpu().numpy(), oracle_attend(p, kc.cpu().numpy(), vc.cpu().numpy()),
+                   f"step graph replay {rep}")
+        # the appended slots hold the oracle's codes of this replay's tokens
+        for b, L in enumerate(c["kv_lens"]):
+            check_codes(kn[b:b + 1].cpu().numpy(), c["k_codebook"], 8, c["smooth"], True,
+                        kc[b:b + 1, :, L - 1:L].cpu().numpy(), f"graph replay {rep} keys row {b}")
