@@ -86,8 +86,8 @@ constexpr int kMaxChunks = 4096;       // partial slots reserved for chunks (>= 
 constexpr int kSegCharge = 2048;
 // Keys charged, in the decode step, to the chunk holding a unit's last key
 // for the encode of the unit's new token (about 3 us of that workgroup's
-// setup).
-constexpr int kAppendCharge = 1024;
+// setup; 1536 measured best among 1024 .. 3072).
+constexpr int kAppendCharge = 1536;
 // int slots of the scan area: 0..3 the chunk plan, kW the block-claim
 // counter, kQExp and kQExp + 1 the exponents of the two query buffers
 constexpr int kQExp = kW + 4;
